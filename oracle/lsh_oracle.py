@@ -1,0 +1,278 @@
+"""Plain fp64 CPU oracle for the forward pass of multi-round LSH attention with
+shared query/key vectors (Reformer).
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import or run this module.  The HIP library and its Python
+binding never import it, and it imports nothing from them: it shares no code,
+table or constant with the GPU path.  Inputs arrive as NumPy arrays (the seeded
+generator's float32 values, upcast here exactly to float64).
+
+Sources (page title, section):
+  [ULT] Ultralytics glossary "Reformer" (Spanish and Arabic editions), section
+        "Atención LSH" / "الانتباه باستخدام LSH", with its hashing example and the
+        result printed after it.
+  [MOD] modulabs-hub notes on "Reformer: The Efficient Transformer", sections
+        "Locality sensitive hashing", "LSH attention", "Multi-round LSH attention".
+  [AIS] ai-scholar.tech article on Reformer, section "变形金刚有哪些问题？" (the
+        scaled dot-product attention formula) and section "什么是本地敏感散列（LSH）？"
+        (bucket, sort, equal chunks, attend to own and previous chunk).
+
+The steps, in the pages' order:
+  1. hash     bucket = first index of the maximum of [x R_r, -x R_r]      [ULT], [MOD]
+  2. sort     positions sorted by bucket (stable, so ties keep position order),
+              one sort per (batch row, head, round)                       [AIS], [ULT], [MOD]
+  3. attend   sorted sequence cut into equal chunks; each query attends to its
+              own chunk and the previous one, never to itself unless nothing
+              else is there, optionally only to earlier positions          [AIS], [ULT], [MOD]
+  4. combine  the rounds merged by logsumexp weights                      [ULT], [MOD]
+
+Readings taken where the pages leave a step open (each is argued in the design
+notes):
+  * scale is a parameter, default 1/sqrt(d_head) ([AIS] formula; [MOD] says the
+    LSH form drops it, so scale = 1 is also accepted);
+  * keys are the shared vectors themselves (no normalisation);
+  * inside a window there is no same-bucket mask: the attended set of a round
+    is the chunk window;
+  * chunk 0 has no previous chunk (no wrap-around) and look-back stays inside
+    a round; chunk must divide L;
+  * the self score carries a penalty of SELF_PENALTY score units in every
+    round, so "self only if nothing else" is decided over all rounds together;
+  * the score of key j for query i in a round is lowered by log N_ij, where
+    N_ij is the number of rounds whose window for i contains j (duplicate-count
+    correction); with it, the combined output equals attention over the union
+    of the rounds' windows;
+  * R has shape [n_rounds, d, n_buckets/2] and is shared by every batch row and
+    head, as in [ULT]'s example;
+  * ties in the argmax go to the first index, as in [ULT]'s example.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+SELF_PENALTY = 1.0e5      # subtracted from the self score, in score units (after scaling)
+NEAR_TIE_MARGIN = 1.0e-4  # a hash whose top-2 gap is at most this is a near-tie
+
+
+# --------------------------------------------------------------------------- 1. hash
+def project(x: np.ndarray, R_r: np.ndarray) -> np.ndarray:
+    """Random projection p = x · R_r in float64.  x [n, d], R_r [d, n_buckets/2].
+
+    [ULT]: multiply by a random matrix R (one per round).
+    """
+    return np.asarray(x, dtype=np.float64) @ np.asarray(R_r, dtype=np.float64)
+
+
+def bucket_from_projection(p: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """bucket = first index of the maximum of [p, -p]; margin = top-1 minus top-2.
+
+    [ULT], [MOD] "Locality sensitive hashing": half as many random columns as
+    buckets, concatenated with their negation; the bucket is the position of the
+    largest entry.  np.argmax returns the first index on exact ties, like the
+    argmax of [ULT]'s example.  The margin is the gap between the largest and
+    second-largest entries of [p, -p]; a zero vector has margin 0.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    a = np.concatenate([p, -p], axis=-1)
+    bucket = np.argmax(a, axis=-1)
+    rows = np.arange(a.shape[0])
+    top = a[rows, bucket]
+    rest = a.copy()
+    rest[rows, bucket] = -np.inf
+    margin = top - rest.max(axis=-1)
+    return bucket.astype(np.int32), margin
+
+
+def hash_buckets(qk: np.ndarray, R: np.ndarray, row_block: int = 16384):
+    """Buckets and margins for every (batch row, head, round, position).
+
+    qk [B, H, L, d], R [n_rounds, d, n_buckets/2]  ->
+    buckets int32 [B, H, n_rounds, L], margins float64 [B, H, n_rounds, L].
+    Rows are processed in blocks only to bound the size of the [p, -p] matrix.
+    """
+    B, H, L, _ = qk.shape
+    n_r = R.shape[0]
+    buckets = np.empty((B, H, n_r, L), dtype=np.int32)
+    margins = np.empty((B, H, n_r, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_r):
+                for s in range(0, L, row_block):
+                    e = min(s + row_block, L)
+                    bk, mg = bucket_from_projection(project(qk[b, h, s:e], R[r]))
+                    buckets[b, h, r, s:e] = bk
+                    margins[b, h, r, s:e] = mg
+    return buckets, margins
+
+
+def hash_one(qk_row: np.ndarray, R_r: np.ndarray) -> Tuple[int, float]:
+    """Bucket and margin of a single vector under one round's R (for sampled checks)."""
+    bk, mg = bucket_from_projection(project(np.asarray(qk_row)[None, :], R_r))
+    return int(bk[0]), float(mg[0])
+
+
+# --------------------------------------------------------------------------- 2. sort
+def stable_counting_sort(keys: np.ndarray, n_keys: int) -> np.ndarray:
+    """Positions sorted by key, equal keys kept in position order.
+
+    Counting sort: histogram of the keys, exclusive prefix sum of the histogram
+    (the first slot of each key), then every position, visited in increasing
+    order, is written to the next free slot of its key.  [AIS], [MOD]: sort the
+    tokens by bucket so that bucket-mates become neighbours.
+    """
+    keys = np.asarray(keys, dtype=np.int64)
+    counts = np.bincount(keys, minlength=n_keys)
+    first_slot = np.zeros(n_keys, dtype=np.int64)
+    first_slot[1:] = np.cumsum(counts)[:-1]
+    next_slot = first_slot.tolist()
+    perm = [0] * keys.size
+    for pos, k in enumerate(keys.tolist()):
+        perm[next_slot[k]] = pos
+        next_slot[k] += 1
+    return np.asarray(perm, dtype=np.int64)
+
+
+def sort_rounds(buckets: np.ndarray, n_buckets: int, chunk: int):
+    """Sorted order and chunk ids for every (batch row, head, round).
+
+    buckets [B, H, n_r, L] -> perm int32 [B, H, n_r, L] (perm[slot] = position)
+    and cid int16 [B, H, L, n_r] (cid[position, r] = slot // chunk in round r).
+    Sorting by (round, bucket, position) with one sort per round gives the same
+    order as one sort over all rounds with the round in the key.
+    """
+    B, H, n_r, L = buckets.shape
+    perm = np.empty((B, H, n_r, L), dtype=np.int32)
+    cid = np.empty((B, H, L, n_r), dtype=np.int16)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_r):
+                p = stable_counting_sort(buckets[b, h, r], n_buckets)
+                perm[b, h, r] = p
+                slot = np.empty(L, dtype=np.int64)
+                slot[p] = np.arange(L)
+                cid[b, h, :, r] = slot // chunk
+    return perm, cid
+
+
+# --------------------------------------------------------------------------- 3. attend
+def window_slots(k: int, chunk: int) -> np.ndarray:
+    """Sorted slots attended by chunk k: the previous chunk (if k >= 1) and chunk k.
+
+    [AIS], [ULT]: the sorted sequence is cut into equal chunks and each chunk
+    attends to itself and to the chunk before it.  Chunk 0 has no predecessor.
+    """
+    return np.arange(max(k - 1, 0) * chunk, (k + 1) * chunk)
+
+
+def duplicate_counts(cid_q: np.ndarray, cid_k: np.ndarray) -> np.ndarray:
+    """N[i, j] = number of rounds whose window for query i contains key j.
+
+    cid_q [nq, n_r], cid_k [nk, n_r] are chunk ids per round.  Key j lies in the
+    window of query i in round r exactly when its chunk is the query's chunk or
+    the one before it: cid_q[i, r] - cid_k[j, r] is 0 or 1.
+    """
+    diff = cid_q[:, None, :].astype(np.int64) - cid_k[None, :, :].astype(np.int64)
+    return ((diff == 0) | (diff == 1)).sum(axis=2)
+
+
+def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
+                    cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
+                    query_slots: Optional[np.ndarray] = None, dup_correct: bool = True):
+    """One round's attention for the queries of sorted chunk k.
+
+    qk_bh, v_bh [L, d] (one batch row and head), perm_r [L] (this round's sorted
+    order), cid_bh [L, n_r].  For query i and key j in the window of chunk k:
+        s_ij = scale * <qk_i, qk_j> - log N_ij - SELF_PENALTY * [j == i],
+    keys j > i are dropped when causal ([MOD] "LSH attention": only earlier
+    positions; the query itself is removed because shared QK makes it the most
+    similar key).  Returns (positions of the queries, o [nq, d], lse [nq]) with
+    lse = logsumexp_j s_ij and o = sum_j softmax(s)_ij v_j ([AIS] formula).
+    query_slots restricts the queries to some sorted slots of chunk k.
+    """
+    q_slots = np.arange(k * chunk, (k + 1) * chunk) if query_slots is None else np.asarray(query_slots)
+    k_slots = window_slots(k, chunk)
+    qi = perm_r[q_slots].astype(np.int64)
+    kj = perm_r[k_slots].astype(np.int64)
+    q = np.asarray(qk_bh[qi], dtype=np.float64)
+    kk = np.asarray(qk_bh[kj], dtype=np.float64)
+    s = scale * (q @ kk.T)
+    if dup_correct:
+        s = s - np.log(duplicate_counts(cid_bh[qi], cid_bh[kj]))
+    s = s - SELF_PENALTY * (qi[:, None] == kj[None, :])
+    if causal:
+        s = np.where(kj[None, :] > qi[:, None], -np.inf, s)
+    m = s.max(axis=1, keepdims=True)          # finite: the query itself is never dropped
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    lse = (m + np.log(z))[:, 0]
+    o = (e / z) @ np.asarray(v_bh[kj], dtype=np.float64)
+    return qi, o, lse
+
+
+def attention_rounds(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.ndarray,
+                     chunk: int, causal: bool, scale: float, dup_correct: bool = True):
+    """Every round's output in original position order.
+
+    -> o_r float64 [B, H, n_r, L, d], lse float64 [B, H, n_r, L].
+    """
+    B, H, L, d = qk.shape
+    n_r = perm.shape[2]
+    if L % chunk:
+        raise ValueError("chunk must divide the sequence length")
+    o_r = np.empty((B, H, n_r, L, d), dtype=np.float64)
+    lse = np.empty((B, H, n_r, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_r):
+                for k in range(L // chunk):
+                    qi, o, l = chunk_attention(qk[b, h], v[b, h], perm[b, h, r], cid[b, h],
+                                               k, chunk, causal, scale, dup_correct=dup_correct)
+                    o_r[b, h, r, qi] = o
+                    lse[b, h, r, qi] = l
+    return o_r, lse
+
+
+def attention_one(qk_bh, v_bh, perm_bh, cid_bh, r: int, pos: int, chunk: int,
+                  causal: bool, scale: float, dup_correct: bool = True):
+    """Round r's (o, lse) for the single query at position ``pos`` (sampled checks)."""
+    slot = int(cid_bh[pos, r]) * chunk
+    seg = perm_bh[r]
+    slot += int(np.nonzero(seg[slot:slot + chunk] == pos)[0][0])
+    _, o, l = chunk_attention(qk_bh, v_bh, seg, cid_bh, slot // chunk, chunk, causal, scale,
+                              query_slots=np.array([slot]), dup_correct=dup_correct)
+    return o[0], float(l[0])
+
+
+# --------------------------------------------------------------------------- 4. combine
+def combine_rounds(o_r: np.ndarray, lse: np.ndarray):
+    """Merge the rounds by logsumexp weights ([MOD] "Multi-round LSH attention").
+
+    LSE = logsumexp_r lse_r;  o = sum_r exp(lse_r - LSE) * o_r.
+    o_r [..., n_r, L, d], lse [..., n_r, L] -> (o [..., L, d], LSE [..., L]).
+    """
+    o_r = np.asarray(o_r, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(axis=-2, keepdims=True)
+    LSE = m + np.log(np.exp(lse - m).sum(axis=-2, keepdims=True))
+    w = np.exp(lse - LSE)
+    o = (w[..., None] * o_r).sum(axis=-3)
+    return o, LSE[..., 0, :]
+
+
+# --------------------------------------------------------------------------- forward
+def default_scale(d_head: int) -> float:
+    return 1.0 / np.sqrt(d_head)
+
+
+def forward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, n_buckets: int, chunk: int,
+            causal: bool, scale: Optional[float] = None, dup_correct: bool = True):
+    """All four steps.  Returns a dict with every intermediate (float64 / int)."""
+    if scale is None:
+        scale = default_scale(qk.shape[-1])
+    buckets, margins = hash_buckets(qk, R)
+    perm, cid = sort_rounds(buckets, n_buckets, chunk)
+    o_r, lse = attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct)
+    o, LSE = combine_rounds(o_r, lse)
+    return {"buckets": buckets, "margins": margins, "perm": perm, "cid": cid,
+            "o_rounds": o_r, "lse": lse, "o": o, "LSE": LSE}

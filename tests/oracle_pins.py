@@ -1,0 +1,279 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check is a plain function that raises AssertionError on failure, so that
+the mutation tests can plant a mistake in the oracle (on the CPU) and confirm
+that some check catches it.  The oracle is always reached through the module
+attribute ``O`` so that a monkeypatched function is the one that runs.
+
+What pins what:
+  hash   - the worked hashing example of the Ultralytics "Reformer" page
+           (section on LSH attention): printed cosines and same-bucket shares;
+         - bucket labels on axis-aligned inputs (x along column k of R lands in
+           bucket k, -x in bucket k + n_buckets/2; exact ties go to the first
+           index of [p, -p]);
+         - antipodal identity h(-x) = (h(x) + n_buckets/2) mod n_buckets;
+         - scale invariance h(2^k x) = h(x);
+         - with 2 buckets, the collision rate over random R is 1 - angle/pi
+           (Charikar's SimHash; textbook, not on the pages).
+  sort   - equals the library's stable sort (np.lexsort); chunk ids agree with
+           the permutation.
+  attend - one chunk spanning the sequence gives textbook full attention with
+  +combine the self-mask (any bucket count, any number of rounds);
+         - union brute force on L <= 64: the combined output equals plain
+           softmax attention over the union of the rounds' windows;
+         - constant values give constant outputs; one-hot values expose the
+           weights (non-negative, sum 1, zero outside the round's window, zero
+           on the query itself when it has company);
+         - causal: position 0 returns its own value exactly;
+         - combine: one round is the identity; equal lse gives the mean.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.lsh_oracle as O
+import reference_forms as RF
+from synthetic_inputs import Workload, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# A round whose window holds only the query has lse near -SELF_PENALTY (1e5);
+# the combine takes differences of such numbers, whose ulp is 1.5e-11, so the
+# combined output is exact only to ~1e-10 on those rows.  Every other row is
+# exact to ~1e-15.  A planted mistake moves outputs by far more than this.
+TOL_COMBINED = 1e-9
+
+
+def small_case(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=11, dtype="f32"):
+    w = Workload("pin", batch=1, heads=1, seq_len=L, d_head=d, dtype=dtype, n_buckets=nb,
+                 n_rounds=n_r, chunk=chunk, causal=causal, seed=seed)
+    x = make_inputs(w)
+    return w, x["qk"].astype(np.float64), x["v"].astype(np.float64), x["R"].astype(np.float64)
+
+
+# --------------------------------------------------------------------------- hash
+def check_hash_demo():
+    import torch  # only to reproduce the page's random draws (CPU generator)
+    with open(os.path.join(GOLDEN, "hash_demo.json")) as f:
+        g = json.load(f)
+    rc = g["recipe"]
+    dim, nb, rounds = rc["dim"], rc["n_buckets"], rc["rounds"]
+    gen_state = torch.random.get_rng_state()
+    try:
+        torch.manual_seed(0)
+        query = torch.randn(dim)
+        near = query + rc["near_noise"] * torch.randn(dim)
+        far = torch.randn(dim)
+        R = torch.randn(rounds, dim, nb // 2)
+    finally:
+        torch.random.set_rng_state(gen_state)
+    vecs = {"query": query.numpy(), "near": near.numpy(), "far": far.numpy()}
+    Rn = R.numpy().astype(np.float64)
+    bk = {}
+    for name, x in vecs.items():
+        bk[name] = np.array([O.hash_one(x, Rn[r])[0] for r in range(rounds)])
+    for name in ("near", "far"):
+        q = vecs["query"].astype(np.float64)
+        x = vecs[name].astype(np.float64)
+        cos = float(q @ x / (np.linalg.norm(q) * np.linalg.norm(x)))
+        # The page's example averages in single precision: 85/1000 is then
+        # 0.0850000009 and prints as 9%, where the double 0.085 would print 8%.
+        share = float(np.float32(np.count_nonzero(bk[name] == bk["query"])) / np.float32(rounds))
+        got = {"cosine": f"{cos:.2f}", "same_bucket_percent": f"{share:.0%}"}
+        assert got == g["printed"][name], (name, got, g["printed"][name])
+
+
+def check_hash_labels():
+    d, nb = 16, 12
+    half = nb // 2
+    R = np.zeros((d, half))
+    R[np.arange(half), np.arange(half)] = 1.0         # p = x[:half] exactly
+    for k in range(half):
+        e = np.zeros(d)
+        e[k] = 2.5
+        assert O.hash_one(e, R)[0] == k
+        assert O.hash_one(-e, R)[0] == k + half
+    x = np.zeros(d)
+    x[1], x[3] = 1.0, 1.0                              # exact tie between columns 1 and 3
+    assert O.hash_one(x, R)[0] == 1
+    x = np.zeros(d)
+    x[1], x[3] = -1.0, 1.0                             # [p,-p] ties at index 3 and half+1
+    assert O.hash_one(x, R)[0] == 3
+    assert O.hash_one(np.zeros(d), R) == (0, 0.0)      # zero vector: bucket 0, margin 0
+
+
+def check_hash_antipodal(seed=5):
+    rng = np.random.default_rng(seed)
+    for d, nb in ((64, 16), (128, 64), (8, 2), (16, 10)):
+        x = rng.standard_normal((500, d))
+        R = rng.standard_normal((d, nb // 2))
+        b1, m1 = O.bucket_from_projection(O.project(x, R))
+        b2, _ = O.bucket_from_projection(O.project(-x, R))
+        ok = m1 > 0
+        assert ok.mean() > 0.99
+        assert np.array_equal(b2[ok], (b1[ok] + nb // 2) % nb)
+
+
+def check_hash_scale_invariance(seed=6):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((400, 32))
+    R = rng.standard_normal((32, 24))
+    b0, _ = O.bucket_from_projection(O.project(x, R))
+    for k in (-3, 1, 7):
+        bk, _ = O.bucket_from_projection(O.project(x * 2.0 ** k, R))
+        assert np.array_equal(bk, b0)
+
+
+def check_simhash_rate(seed=7, rounds=20000):
+    """n_buckets = 2: P[h(x) = h(y)] = 1 - angle(x, y)/pi over random R."""
+    rng = np.random.default_rng(seed)
+    d = 16
+    R = rng.standard_normal((rounds, d, 1))
+    x = rng.standard_normal(d)
+    for target in (0.3, 1.2, 2.5):
+        u = rng.standard_normal(d)
+        u -= (u @ x) / (x @ x) * x
+        u *= np.linalg.norm(x) / np.linalg.norm(u)
+        y = math.cos(target) * x + math.sin(target) * u
+        theta = math.acos(float(x @ y / (np.linalg.norm(x) * np.linalg.norm(y))))
+        hx = np.array([O.hash_one(x, R[r])[0] for r in range(rounds)])
+        hy = np.array([O.hash_one(y, R[r])[0] for r in range(rounds)])
+        p = 1 - theta / math.pi
+        rate = float(np.mean(hx == hy))
+        sigma = math.sqrt(p * (1 - p) / rounds)
+        assert abs(rate - p) < 5 * sigma, (theta, rate, p)
+
+
+# --------------------------------------------------------------------------- sort
+def check_sort_matches_library(seed=8):
+    rng = np.random.default_rng(seed)
+    cases = [rng.integers(0, 7, 1000), rng.integers(0, 1024, 5000), np.zeros(300, int),
+             np.arange(200)[::-1].copy(), np.array([3]), rng.integers(0, 2, 64)]
+    for keys in cases:
+        nk = int(keys.max()) + 1
+        got = O.stable_counting_sort(keys, nk)
+        want = np.lexsort((np.arange(keys.size), keys))
+        assert np.array_equal(got, want)
+
+
+def check_sort_rounds_cid(seed=9):
+    rng = np.random.default_rng(seed)
+    B, H, n_r, L, nb, c = 2, 2, 3, 96, 10, 16
+    buckets = rng.integers(0, nb, (B, H, n_r, L)).astype(np.int32)
+    perm, cid = O.sort_rounds(buckets, nb, c)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_r):
+                want = np.lexsort((np.arange(L), buckets[b, h, r]))
+                assert np.array_equal(perm[b, h, r], want)
+                slots = np.arange(L)
+                assert np.array_equal(cid[b, h, perm[b, h, r], r], slots // c)
+
+
+# --------------------------------------------------------------------------- attention + combine
+def _forward(w, qk, v, R, scale=None, **kw):
+    out = O.forward(qk[None, None] if qk.ndim == 2 else qk, v[None, None] if v.ndim == 2 else v,
+                    R, w.n_buckets, w.chunk, w.causal, scale=scale, **kw)
+    return out
+
+
+def check_full_attention(L=40, d=8, nb=6, n_r=3, causal=False, scale=None, seed=12):
+    w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=L, causal=causal, seed=seed)
+    sc = (1.0 / math.sqrt(d)) if scale is None else scale
+    out = _forward(w, qk[0, 0], v[0, 0], R, scale=scale)
+    ref = RF.full_attention_self_masked(qk[0, 0], v[0, 0], causal, sc)
+    err = np.max(np.abs(out["o"][0, 0] - ref))
+    assert err < TOL_COMBINED, err
+
+
+def check_union(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13, dup_correct=True):
+    w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
+    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=dup_correct)
+    ref = RF.union_attention(qk[0, 0], v[0, 0], out["buckets"][0, 0], chunk, causal, 1.0 / math.sqrt(d))
+    err = np.max(np.abs(out["o"][0, 0] - ref))
+    assert err < TOL_COMBINED, err
+
+
+def union_has_duplicates(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13) -> bool:
+    """True if some query sees some other key in two or more rounds."""
+    w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
+    buckets, _ = O.hash_buckets(qk, R)
+    W = RF.brute_windows(buckets[0, 0], chunk, causal)
+    for i in range(L):
+        for j in range(L):
+            if j != i and sum(j in Wr[i] for Wr in W) > 1:
+                return True
+    return False
+
+
+def check_constant_values(seed=14):
+    w, qk, v, R = small_case(L=64, d=8, nb=8, n_r=2, chunk=16, causal=True, seed=seed)
+    ones = np.ones_like(v)
+    out = _forward(w, qk, ones, R)
+    assert np.max(np.abs(out["o_rounds"] - 1.0)) < 1e-12
+    # rounds whose window holds only the query have lse near -SELF_PENALTY, whose
+    # rounding (ulp 1.5e-11) bounds how exactly the combine weights sum to one
+    assert np.max(np.abs(out["o"] - 1.0)) < TOL_COMBINED
+
+
+def check_onehot_values(causal=True, seed=15):
+    L, d = 32, 32
+    w, qk, _, R = small_case(L=L, d=d, nb=6, n_r=2, chunk=8, causal=causal, seed=seed)
+    v = np.eye(L, d)[None, None]
+    out = _forward(w, qk, v, R)
+    W = RF.brute_windows(out["buckets"][0, 0], w.chunk, causal)
+    for r in range(w.n_rounds):
+        wts = out["o_rounds"][0, 0, r]                 # row i = weights of query i over positions
+        assert np.all(wts > -1e-15)
+        assert np.max(np.abs(wts.sum(axis=1) - 1.0)) < 1e-12
+        for i in range(L):
+            outside = [j for j in range(L) if j not in W[r][i]]
+            assert np.max(np.abs(wts[i, outside]), initial=0.0) < 1e-300
+            if len(W[r][i]) > 1:
+                assert wts[i, i] == 0.0
+
+
+def check_causal_first_position(seed=16):
+    w, qk, v, R = small_case(L=64, d=8, nb=8, n_r=3, chunk=16, causal=True, seed=seed)
+    out = _forward(w, qk, v, R)
+    assert np.array_equal(out["o_rounds"][0, 0, :, 0], np.repeat(v[0, 0, :1], 3, axis=0))
+    # Every round's lse is about -SELF_PENALTY here, so lse - LSE carries the
+    # rounding of numbers near 1e5 (ulp 1.5e-11): the combine is exact to ~1e-10.
+    assert np.max(np.abs(out["o"][0, 0, 0] - v[0, 0, 0])) < TOL_COMBINED
+
+
+def check_combine(seed=17):
+    rng = np.random.default_rng(seed)
+    o_r = rng.standard_normal((2, 1, 20, 4))
+    lse = rng.standard_normal((2, 1, 20))
+    o, LSE = O.combine_rounds(o_r, lse)
+    assert np.array_equal(o, o_r[:, 0])
+    assert np.array_equal(LSE, lse[:, 0])
+    o_r = rng.standard_normal((3, 5, 20, 4))
+    lse = np.full((3, 5, 20), 0.7)
+    o, LSE = O.combine_rounds(o_r, lse)
+    assert np.max(np.abs(o - o_r.mean(axis=1))) < 1e-14
+    assert np.max(np.abs(LSE - (0.7 + math.log(5)))) < 1e-14
+
+
+ALL_CHECKS = {
+    "hash_demo": check_hash_demo,
+    "hash_labels": check_hash_labels,
+    "hash_antipodal": check_hash_antipodal,
+    "hash_scale": check_hash_scale_invariance,
+    "simhash": check_simhash_rate,
+    "sort_library": check_sort_matches_library,
+    "sort_cid": check_sort_rounds_cid,
+    "full_attention": check_full_attention,
+    "full_attention_causal": lambda: check_full_attention(causal=True, n_r=2, nb=2),
+    "union": check_union,
+    "union_causal": lambda: check_union(causal=True, n_r=4, nb=4, chunk=4, L=32),
+    "constant_values": check_constant_values,
+    "onehot_values": check_onehot_values,
+    "causal_first": check_causal_first_position,
+    "combine": check_combine,
+}

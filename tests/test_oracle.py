@@ -1,0 +1,148 @@
+"""CPU tests of the oracle against its pins, and mutation tests showing that a
+plausible mistake planted in the oracle (on the CPU) fails at least one pin."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle.lsh_oracle as O
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("name", sorted(P.ALL_CHECKS))
+def test_pin(name):
+    P.ALL_CHECKS[name]()
+
+
+@pytest.mark.parametrize("nb,n_r,causal,scale", [(2, 1, False, None), (2, 3, True, None),
+                                                 (10, 4, False, 1.0), (16, 2, True, 0.3)])
+def test_full_attention_any_buckets_and_rounds(nb, n_r, causal, scale):
+    P.check_full_attention(L=32, d=8, nb=nb, n_r=n_r, causal=causal, scale=scale, seed=nb + n_r)
+
+
+@settings(max_examples=40, deadline=None)
+@given(L_chunks=st.integers(1, 8), chunk=st.sampled_from([1, 2, 4, 8]),
+       nb_half=st.integers(1, 8), n_r=st.integers(1, 4), causal=st.booleans(),
+       seed=st.integers(0, 10_000))
+def test_union_bruteforce(L_chunks, chunk, nb_half, n_r, causal, seed):
+    L = L_chunks * chunk
+    if L > 64:
+        return
+    P.check_union(L=L, d=4, nb=2 * nb_half, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
+
+
+def test_union_negative_control():
+    """Without the duplicate-count correction the union identity must fail."""
+    kw = dict(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13)
+    assert P.union_has_duplicates(**kw)
+    P.check_union(**kw)
+    with pytest.raises(AssertionError):
+        P.check_union(dup_correct=False, **kw)
+
+
+def test_oracle_shapes_and_dtypes():
+    w, qk, v, R = P.small_case(L=64, d=8, nb=8, n_r=2, chunk=16, causal=True)
+    out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
+    assert out["buckets"].shape == (1, 1, 2, 64) and out["buckets"].dtype == np.int32
+    assert out["perm"].shape == (1, 1, 2, 64) and out["perm"].dtype == np.int32
+    assert out["cid"].shape == (1, 1, 64, 2) and out["cid"].dtype == np.int16
+    assert out["o_rounds"].shape == (1, 1, 2, 64, 8)
+    assert out["lse"].shape == (1, 1, 2, 64)
+    assert out["o"].shape == (1, 1, 64, 8)
+
+
+def test_attention_one_matches_rounds():
+    w, qk, v, R = P.small_case(L=64, d=8, nb=8, n_r=3, chunk=16, causal=True, seed=21)
+    out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
+    sc = O.default_scale(8)
+    for r in range(3):
+        for pos in (0, 5, 17, 63):
+            o, l = O.attention_one(qk[0, 0], v[0, 0], out["perm"][0, 0], out["cid"][0, 0], r, pos,
+                                   w.chunk, w.causal, sc)
+            assert np.max(np.abs(o - out["o_rounds"][0, 0, r, pos])) < 1e-14
+            assert abs(l - out["lse"][0, 0, r, pos]) < 1e-12
+
+
+# --------------------------------------------------------------------------- mutations
+def _argmax_positive_half_only(p):
+    p = np.asarray(p, dtype=np.float64)
+    b = np.argmax(p, axis=-1).astype(np.int32)
+    s = np.sort(p, axis=-1)
+    m = s[:, -1] - (s[:, -2] if p.shape[1] > 1 else -np.inf)
+    return b, m
+
+
+def _argmin_labels(p):
+    a = np.concatenate([p, -p], axis=-1)
+    b = np.argmin(a, axis=-1).astype(np.int32)
+    return b, np.ones(a.shape[0])
+
+
+def _unstable_sort(keys, n_keys):
+    keys = np.asarray(keys)
+    return np.lexsort((-np.arange(keys.size), keys))
+
+
+def _own_chunk_only(k, chunk):
+    return np.arange(k * chunk, (k + 1) * chunk)
+
+
+def _two_back(k, chunk):
+    own = np.arange(k * chunk, (k + 1) * chunk)
+    return own if k < 2 else np.concatenate([np.arange((k - 2) * chunk, (k - 1) * chunk), own])
+
+
+def _mean_combine(o_r, lse):
+    return np.asarray(o_r).mean(axis=-3), np.asarray(lse).max(axis=-2)
+
+
+_DUP_ORIG = O.duplicate_counts
+
+
+def _wrap(fn, transform):
+    def inner(*a, **k):
+        a, k = transform(list(a), dict(k))
+        return fn(*a, **k)
+    return inner
+
+
+def _ignore_causal(a, k):
+    a[6] = False
+    return a, k
+
+
+def _values_are_keys(a, k):
+    a[1] = a[0]
+    return a, k
+
+
+MUTATIONS = {
+    "hash drops the negated half": ("bucket_from_projection", _argmax_positive_half_only, "hash_antipodal"),
+    "hash takes argmin": ("bucket_from_projection", _argmin_labels, "hash_labels"),
+    "sort not stable": ("stable_counting_sort", _unstable_sort, "sort_library"),
+    "no look-back chunk": ("window_slots", _own_chunk_only, "union"),
+    "look-back two chunks": ("window_slots", _two_back, "union"),
+    "duplicate counts dropped": ("duplicate_counts", lambda q, k: np.ones((len(q), len(k))), "union"),
+    "log of duplicate count dropped": ("duplicate_counts",
+                                       lambda q, k: np.exp(_DUP_ORIG(q, k)),
+                                       "union"),
+    "no self penalty": ("SELF_PENALTY", 0.0, "full_attention"),
+    "causal flag ignored": ("chunk_attention", "ignore_causal", "full_attention_causal"),
+    "keys used as values": ("chunk_attention", "values_are_keys", "full_attention"),
+    "scale dropped": ("default_scale", lambda d: 1.0, "full_attention"),
+    "rounds averaged": ("combine_rounds", _mean_combine, "union"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, repl, check = MUTATIONS[name]
+    orig = getattr(O, attr)
+    if repl == "ignore_causal":
+        repl = _wrap(orig, _ignore_causal)
+    elif repl == "values_are_keys":
+        repl = _wrap(orig, _values_are_keys)
+    monkeypatch.setattr(O, attr, repl)
+    with pytest.raises((AssertionError, IndexError, ValueError)):
+        P.ALL_CHECKS[check]()
