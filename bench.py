@@ -1,0 +1,250 @@
+"""Benchmark of the MI355X LSH-attention forward (hash, sort, chunk attention, combine).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload paper_64k]
+
+One step = the four calls over one batch of synthetic input already resident in
+HBM.  Prints one JSON line.  Per-call times come from HIP events recorded on the
+stream the calls are launched on.  `roofline` describes the call with the
+largest time: achieved = algorithmic bytes (or FLOPs) per launch / its average
+duration.  `traffic` is the HBM traffic per launch of that kernel measured with
+rocprofv3 counters (profiles/pmc_traffic.json), or null when those counters were
+taken on a different kernel source.  `cpu_baseline` is the CPU oracle timed on
+one (batch row, head) of the same workload on this host, scaled to the whole
+workload.
+
+Other modes:
+    --copy-calibration   run only a plain 1 GiB device copy (for scaling the
+                         FETCH_SIZE / WRITE_SIZE counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+METRIC = "LSH-attn fwd tokens/s at L=64K, 8 heads, 8 rounds; % MFMA/HBM peak"
+KERNEL_SOURCES = {"lsh_hash": "lsh_hash.hip", "lsh_sort": "lsh_sort.hip",
+                  "lsh_chunk_attn": "lsh_chunk_attn.hip", "lsh_combine_rounds": "lsh_combine.hip"}
+KERNEL_SYMBOLS = {"lsh_hash": "k_hash", "lsh_sort": "k_sort_*", "lsh_chunk_attn": "k_chunk_attn",
+                  "lsh_combine_rounds": "k_combine"}
+
+
+def algorithmic_work(w):
+    """Algorithmic FLOPs and HBM bytes per launch of each call.
+
+    TR = token-head-rounds, T = token-heads, e = bytes per element.
+      hash     2*d*(nb/2) FLOP per TR; reads qk once (T*d*e) and R, writes 4 B per TR
+      sort     reads the bucket (4 B), writes perm (4 B) and cid (2 B): 10 B per TR
+      attn     8*c*d FLOP per TR (QK^T and PV over a 2c-key window); gathers the qk
+               and v rows once and writes the o_rounds row (3*d*e), reads perm (4),
+               writes lse (4), reads the cid row (2*n_r) per TR
+      combine  reads n_r rows and lse values, writes one row: n_r*(d*e+4) + d*e per T
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    T = w.batch * w.heads * w.seq_len
+    TR = T * w.n_rounds
+    d, nb = w.d_head, w.n_buckets
+    return {
+        "lsh_hash": {"flops": 2.0 * d * (nb // 2) * TR,
+                     "bytes": T * d * e + w.n_rounds * d * (nb // 2) * e + 4.0 * TR},
+        "lsh_sort": {"flops": 0.0, "bytes": 10.0 * TR},
+        "lsh_chunk_attn": {"flops": 8.0 * w.chunk * d * TR,
+                           "bytes": TR * (3.0 * d * e + 8 + 2 * w.n_rounds)},
+        "lsh_combine_rounds": {"flops": 0.0,
+                               "bytes": T * (w.n_rounds * (d * e + 4.0) + d * e)},
+    }
+
+
+def bound_of(name, w):
+    """Binding roofline of each call at the benchmark sizes: the hash is a dense
+    contraction (thousands of FLOP per byte), the other three stream memory."""
+    return "mfma" if name == "lsh_hash" else "hbm"
+
+
+def roofline_entry(name, w, ms):
+    work = algorithmic_work(w)[name]
+    if bound_of(name, w) == "mfma":
+        ach = work["flops"] / (ms * 1e-3) / 1e12
+        peak = PEAK_MFMA_TFLOPS[w.dtype]
+        unit = "TFLOP/s"
+    else:
+        ach = work["bytes"] / (ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+        unit = "GB/s"
+    return {"bound": bound_of(name, w), "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4)}
+
+
+def source_sha(name):
+    path = os.path.join(ROOT, "lsh_attention_02_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(name, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("kernels", {}).get(name)
+    if not ent or ent.get("workload") != workload or ent.get("source_sha256") != source_sha(name):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x):
+    """The oracle on one (batch row, head) of the workload, scaled to all heads."""
+    import numpy as np
+    import oracle.lsh_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    qk = x["qk"][:1, :1].astype(np.float64)
+    v = x["v"][:1, :1].astype(np.float64)
+    R = x["R"].astype(np.float64)
+    t0 = time.perf_counter()
+    out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["o"]).all()
+    heads = w.batch * w.heads
+    tokens_per_s = w.batch * w.seq_len / (dt * heads)
+    return {"value": round(tokens_per_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch row 0, head 0 of {heads} (all {w.n_rounds} rounds, all "
+                      f"{w.seq_len} positions) in {dt:.1f} s; value = B*L / (time * B*H)"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="paper_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the forward pass shards over batch rows and heads "
+              "with no exchange, so a multi-GPU figure is not produced (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import lsh_attention_02_amd as lsh
+    from synthetic_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    cfg = lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
+                        w.causal, dtype=w.dtype)
+    tdt = cfg.torch_dtype
+    qk = torch.from_numpy(x["qk"]).to(dev).to(tdt)
+    v = torch.from_numpy(x["v"]).to(dev).to(tdt)
+    R = torch.from_numpy(x["R"]).to(dev).to(tdt)
+    B, H, L, d, nr = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
+    buckets = torch.empty((B, H, nr, L), dtype=torch.int32, device=dev)
+    perm = torch.empty((B, H, nr, L), dtype=torch.int32, device=dev)
+    cid = torch.empty((B, H, L, nr), dtype=torch.int16, device=dev)
+    o_r = torch.empty((B, H, nr, L, d), dtype=tdt, device=dev)
+    lse = torch.empty((B, H, nr, L), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, L, d), dtype=tdt, device=dev)
+    ws = lsh.sort_workspace(cfg, dev)
+    stream = torch.cuda.Stream(device=dev)
+    names = ["lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds"]
+    calls = [
+        lambda: lsh.lsh_hash(cfg, qk, R, buckets, stream=stream),
+        lambda: lsh.lsh_sort(cfg, buckets, perm, cid, ws, stream=stream),
+        lambda: lsh.lsh_chunk_attn(cfg, qk, v, perm, cid, o_r, lse, stream=stream),
+        lambda: lsh.lsh_combine_rounds(cfg, o_r, lse, o, stream=stream),
+    ]
+
+    def step(evs=None):
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record(stream)
+            c()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+              for _ in range(args.steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.steps):
+            step(ev[k])
+        end.record(stream)
+        torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per_call = {n: float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
+                for i, n in enumerate(names)}
+    assert torch.isfinite(o.float()).all().item(), "non-finite output"
+
+    tokens = B * L
+    value = tokens / (ms_per_step * 1e-3)
+    dominant = max(per_call, key=per_call.get)
+    roof = roofline_entry(dominant, w, per_call[dominant])
+    work = algorithmic_work(w)[dominant]
+    roof["traffic"] = traffic_for(dominant, w.name)
+    roof["kernel"] = KERNEL_SYMBOLS[dominant]
+    roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
+    kernels = {}
+    for n in names:
+        e = roofline_entry(n, w, per_call[n])
+        e["ms"] = round(per_call[n], 4)
+        kernels[n] = e
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": d,
+                   "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
+                   "causal": w.causal},
+        "roofline": roof, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

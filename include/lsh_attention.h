@@ -1,0 +1,153 @@
+/*
+ * lsh_attention.h — C ABI of the MI355X (gfx950) multi-round LSH-attention forward.
+ *
+ * The forward pass of Reformer's LSH attention with shared query/key vectors,
+ * split into its four steps.  Each step is one call; the calls run their HIP
+ * kernels asynchronously on the caller's stream and never synchronise it.
+ *
+ * Passages followed (page title, section):
+ *   [ULT] Ultralytics glossary "Reformer" (Spanish / Arabic editions), section on
+ *         LSH attention: angular hashing by the position of the largest entry of
+ *         [xR, -xR] for a random R; tokens sorted by bucket; the sorted sequence
+ *         cut into equal chunks; each token attends to its own chunk and the one
+ *         before it; several hash rounds.
+ *   [MOD] modulabs-hub notes on "Reformer: The Efficient Transformer", sections
+ *         "Locality sensitive hashing" (n_buckets/2 random columns, concatenated
+ *         with their negation), "LSH attention" (the query itself removed because
+ *         shared QK makes it its own best match; causal attention to earlier
+ *         positions only; sorting and equal chunks), "Multi-round LSH attention".
+ *   [AIS] ai-scholar.tech article on Reformer: the scaled dot-product attention
+ *         formula; section on LSH attention (sort by bucket, equal chunks, attend
+ *         to each chunk and the previous one).
+ *
+ * Conventions shared by every call
+ *   B = batch, H = heads, L = seq_len, d = d_head, nb = n_buckets, n_r = n_rounds,
+ *   c = chunk.  Tensors are dense, row-major, last index fastest, and live in
+ *   device memory (pointers from hipMalloc or a framework allocator on the
+ *   current device).  The caller allocates and owns every buffer; the library
+ *   allocates nothing, draws no random numbers and keeps no mutable global state,
+ *   so calls on different streams may run concurrently.
+ *   `stream` is a hipStream_t (NULL = the default stream).
+ *   dtype LSH_BF16: qk, v, R, o_rounds and o hold bfloat16; products are exact and
+ *   accumulate in fp32; outputs are rounded to nearest even.  dtype LSH_F32: all
+ *   float32.
+ *
+ * Errors
+ *   Every call checks its arguments on the host before any HIP call and returns
+ *   a status; nothing is launched unless it returns LSH_OK.
+ *   LSH_ERR_INVALID_ARG  null or non-16-byte-aligned pointer; a size <= 0;
+ *                        n_buckets odd; L % chunk != 0; L / chunk > 32767;
+ *                        L > 2^30; scale not finite; causal not 0/1; a buffer
+ *                        larger than 2^62 bytes.
+ *   LSH_ERR_UNSUPPORTED  d_head not 64 or 128; dtype not LSH_F32/LSH_BF16;
+ *                        n_buckets > 32768; n_rounds > 16; chunk not 32, 64 or
+ *                        128 (attention only); flags != 0.
+ *   LSH_ERR_WORKSPACE    workspace smaller than lsh_sort_workspace_bytes().
+ *   LSH_ERR_HIP          a kernel launch failed (hipGetLastError).
+ *   Faults inside a kernel surface asynchronously at the caller's next
+ *   synchronisation of `stream`.  lsh_last_error() names the failed check
+ *   (per thread).
+ */
+#ifndef LSH_ATTENTION_H
+#define LSH_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lsh_status {
+    LSH_OK = 0,
+    LSH_ERR_INVALID_ARG = 1,
+    LSH_ERR_UNSUPPORTED = 2,
+    LSH_ERR_WORKSPACE = 3,
+    LSH_ERR_HIP = 4
+} lsh_status;
+
+enum { LSH_F32 = 0, LSH_BF16 = 1 };
+
+typedef struct lsh_config {
+    int32_t batch;      /* B >= 1 */
+    int32_t heads;      /* H >= 1 */
+    int32_t seq_len;    /* L >= 1, L % chunk == 0 */
+    int32_t d_head;     /* 64 or 128 */
+    int32_t n_buckets;  /* even, 2 .. 32768 */
+    int32_t n_rounds;   /* 1 .. 16 hash rounds, each with its own R */
+    int32_t chunk;      /* c >= 1; attention supports 32, 64, 128 */
+    int32_t causal;     /* 1: a query never attends to a later position */
+    float scale;        /* score = scale * <qk_i, qk_j>; usually 1/sqrt(d_head) */
+    int32_t dtype;      /* LSH_F32 or LSH_BF16 */
+    int32_t flags;      /* reserved, must be 0 */
+} lsh_config;
+
+/*
+ * Step 1 — angular LSH hash.  [ULT]; [MOD] "Locality sensitive hashing".
+ *   buckets[b,h,r,i] = index of the largest entry of [p, -p], p = qk[b,h,i,:] · R[r]
+ *   (p has nb/2 entries; an index k >= nb/2 means entry k - nb/2 of -p).
+ *   Exact ties of |p| go to the lowest column; a zero vector gets bucket 0.
+ *   qk       [B, H, L, d]        dtype
+ *   R        [n_r, d, nb/2]      dtype; one random matrix per round, shared by
+ *                                every batch row and head
+ *   buckets  [B, H, n_r, L]      int32 out, values in [0, nb)
+ */
+lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R,
+                    int32_t* buckets, void* stream);
+
+/* Bytes of device workspace lsh_sort needs for `cfg` (0 if cfg is invalid). */
+size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
+
+/*
+ * Step 2 — sort by bucket.  [AIS] LSH section; [ULT]; [MOD] "LSH attention".
+ *   For every (b, h, r): a stable sort of positions 0..L-1 by bucket, i.e. the
+ *   lexicographic order of (round, bucket, position).
+ *   buckets    [B, H, n_r, L]   int32 in, values in [0, nb) (not checked)
+ *   perm       [B, H, n_r, L]   int32 out: perm[b,h,r,slot] = position
+ *   cid        [B, H, L, n_r]   int16 out: cid[b,h,pos,r] = slot(pos) / chunk
+ *   workspace  device scratch of at least lsh_sort_workspace_bytes(cfg) bytes;
+ *              its contents on entry do not matter.
+ */
+lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm,
+                    int16_t* cid, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Step 3 — chunked attention, one output per round.  [AIS] formula and LSH
+ * section; [ULT]; [MOD] "LSH attention".
+ *   In round r, the query at sorted slot s (chunk k = s / c) attends to the keys
+ *   in chunks k-1 and k of that round's sorted order (chunk 0: only itself).  For
+ *   query i and key j:
+ *       s_ij = scale * <qk_i, qk_j> - log N_ij - 1e5 * [j == i]
+ *   where N_ij = number of rounds r' with cid[i,r'] - cid[j,r'] in {0, 1} (the
+ *   rounds whose window for i holds j); keys j > i are dropped when causal.
+ *       lse_i = logsumexp_j s_ij,   o_i = sum_j exp(s_ij - lse_i) v_j.
+ *   qk, v     [B, H, L, d]          dtype
+ *   perm      [B, H, n_r, L]        int32, from lsh_sort
+ *   cid       [B, H, L, n_r]        int16, from lsh_sort
+ *   o_rounds  [B, H, n_r, L, d]     dtype out, rows in original position order
+ *   lse       [B, H, n_r, L]        float32 out, original position order
+ */
+lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v,
+                          const int32_t* perm, const int16_t* cid, void* o_rounds,
+                          float* lse, void* stream);
+
+/*
+ * Step 4 — combine the rounds.  [MOD] "Multi-round LSH attention"; [ULT].
+ *   LSE_i = logsumexp_r lse[r,i];  o_i = sum_r exp(lse[r,i] - LSE_i) o_rounds[r,i].
+ *   o_rounds [B, H, n_r, L, d] dtype;  lse [B, H, n_r, L] float32;
+ *   o        [B, H, L, d]      dtype out.
+ */
+lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
+                              const float* lse, void* o, void* stream);
+
+/* Static description of a status code. */
+const char* lsh_status_string(lsh_status status);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char* lsh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_ATTENTION_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) forward pass of multi-round LSH attention with shared QK.
+
+The four steps (hash, sort, chunk attention, round combine) run in the HIP
+kernels of liblsh_attention.so behind a C ABI (include/lsh_attention.h); this
+package is its Python binding.  Build the library with
+``python -m lsh_attention_02_amd.build``.
+"""
+from ._binding import (EXPORTED, LIB_PATH, LSH_BF16, LSH_ERR_HIP, LSH_ERR_INVALID_ARG,  # noqa: F401
+                       LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_F32, LSH_OK, CConfig,
+                       LSHConfig, LSHError, forward, load_library, lsh_chunk_attn,
+                       lsh_combine_rounds, lsh_hash, lsh_sort, lsh_sort_workspace_bytes,
+                       sort_workspace)

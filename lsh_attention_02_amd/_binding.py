@@ -1,0 +1,242 @@
+"""ctypes binding of liblsh_attention.so (declared in include/lsh_attention.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI.  torch provides device memory and streams.  The
+wrappers check shapes, dtypes, devices and contiguity of the tensors on the
+host, because the C ABI receives bare pointers and cannot.
+
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblsh_attention.so")
+
+LSH_OK, LSH_ERR_INVALID_ARG, LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_ERR_HIP = range(5)
+LSH_F32, LSH_BF16 = 0, 1
+
+EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
+            "lsh_combine_rounds", "lsh_status_string", "lsh_last_error")
+
+
+class LSHError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message} (status {status})")
+        self.status = status
+
+
+class CConfig(ctypes.Structure):
+    """Mirror of struct lsh_config."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("n_buckets", ctypes.c_int32), ("n_rounds", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
+
+
+@dataclasses.dataclass(frozen=True)
+class LSHConfig:
+    batch: int
+    heads: int
+    seq_len: int
+    d_head: int
+    n_buckets: int
+    n_rounds: int
+    chunk: int
+    causal: bool
+    dtype: str = "bf16"            # "bf16" or "f32"
+    scale: Optional[float] = None  # None: 1/sqrt(d_head)
+    flags: int = 0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+
+    @property
+    def score_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_head) if self.scale is None else float(self.scale)
+
+    def to_c(self) -> CConfig:
+        return CConfig(self.batch, self.heads, self.seq_len, self.d_head, self.n_buckets,
+                       self.n_rounds, self.chunk, int(bool(self.causal)), self.score_scale,
+                       {"bf16": LSH_BF16, "f32": LSH_F32}[self.dtype], self.flags)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m lsh_attention_02_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, CP, I32 = ctypes.c_void_p, ctypes.POINTER(CConfig), ctypes.c_int
+    lib.lsh_hash.argtypes = [CP, P, P, P, P]
+    lib.lsh_sort_workspace_bytes.argtypes = [CP]
+    lib.lsh_sort_workspace_bytes.restype = ctypes.c_size_t
+    lib.lsh_sort.argtypes = [CP, P, P, P, P, ctypes.c_size_t, P]
+    lib.lsh_chunk_attn.argtypes = [CP, P, P, P, P, P, P, P]
+    lib.lsh_combine_rounds.argtypes = [CP, P, P, P, P]
+    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds"):
+        getattr(lib, f).restype = I32
+    lib.lsh_status_string.argtypes = [I32]
+    lib.lsh_status_string.restype = ctypes.c_char_p
+    lib.lsh_last_error.argtypes = []
+    lib.lsh_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != LSH_OK:
+        lib = load_library()
+        raise LSHError(status, where, lib.lsh_last_error().decode())
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(cfg: LSHConfig):
+    B, H, L, d, nr = cfg.batch, cfg.heads, cfg.seq_len, cfg.d_head, cfg.n_rounds
+    return {"qk": (B, H, L, d), "v": (B, H, L, d), "R": (nr, d, cfg.n_buckets // 2),
+            "buckets": (B, H, nr, L), "perm": (B, H, nr, L), "cid": (B, H, L, nr),
+            "o_rounds": (B, H, nr, L, d), "lse": (B, H, nr, L), "o": (B, H, L, d)}
+
+
+def lsh_hash(cfg: LSHConfig, qk: torch.Tensor, R: torch.Tensor,
+             buckets: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Step 1: buckets [B, H, n_rounds, L] int32 (see lsh_hash in the header)."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(qk, "qk", sh["qk"], cfg.torch_dtype)
+    _expect(R, "R", sh["R"], cfg.torch_dtype, qk.device)
+    if buckets is None:
+        buckets = torch.empty(sh["buckets"], dtype=torch.int32, device=qk.device)
+    _expect(buckets, "buckets", sh["buckets"], torch.int32, qk.device)
+    c = cfg.to_c()
+    _check(lib.lsh_hash(ctypes.byref(c), _ptr(qk), _ptr(R), _ptr(buckets),
+                        _stream(qk.device, stream)), "lsh_hash")
+    return buckets
+
+
+def lsh_sort_workspace_bytes(cfg: LSHConfig) -> int:
+    c = cfg.to_c()
+    return int(load_library().lsh_sort_workspace_bytes(ctypes.byref(c)))
+
+
+def sort_workspace(cfg: LSHConfig, device) -> torch.Tensor:
+    """A device buffer large enough for lsh_sort (at least 16 bytes)."""
+    n = max(16, lsh_sort_workspace_bytes(cfg))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lsh_sort(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor] = None,
+             cid: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None):
+    """Step 2: (perm [B, H, n_rounds, L] int32, cid [B, H, L, n_rounds] int16)."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(buckets, "buckets", sh["buckets"], torch.int32)
+    dev = buckets.device
+    if perm is None:
+        perm = torch.empty(sh["perm"], dtype=torch.int32, device=dev)
+    if cid is None:
+        cid = torch.empty(sh["cid"], dtype=torch.int16, device=dev)
+    if workspace is None:
+        workspace = sort_workspace(cfg, dev)
+    _expect(perm, "perm", sh["perm"], torch.int32, dev)
+    _expect(cid, "cid", sh["cid"], torch.int16, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same device")
+    nbytes = workspace.numel() * workspace.element_size()
+    c = cfg.to_c()
+    _check(lib.lsh_sort(ctypes.byref(c), _ptr(buckets), _ptr(perm), _ptr(cid), _ptr(workspace),
+                        ctypes.c_size_t(nbytes), _stream(dev, stream)), "lsh_sort")
+    return perm, cid
+
+
+def lsh_chunk_attn(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor,
+                   cid: torch.Tensor, o_rounds: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None):
+    """Step 3: (o_rounds [B, H, n_rounds, L, d], lse [B, H, n_rounds, L] float32)."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(qk, "qk", sh["qk"], cfg.torch_dtype)
+    dev = qk.device
+    _expect(v, "v", sh["v"], cfg.torch_dtype, dev)
+    _expect(perm, "perm", sh["perm"], torch.int32, dev)
+    _expect(cid, "cid", sh["cid"], torch.int16, dev)
+    if o_rounds is None:
+        o_rounds = torch.empty(sh["o_rounds"], dtype=cfg.torch_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(sh["lse"], dtype=torch.float32, device=dev)
+    _expect(o_rounds, "o_rounds", sh["o_rounds"], cfg.torch_dtype, dev)
+    _expect(lse, "lse", sh["lse"], torch.float32, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_chunk_attn(ctypes.byref(c), _ptr(qk), _ptr(v), _ptr(perm), _ptr(cid),
+                              _ptr(o_rounds), _ptr(lse), _stream(dev, stream)), "lsh_chunk_attn")
+    return o_rounds, lse
+
+
+def lsh_combine_rounds(cfg: LSHConfig, o_rounds: torch.Tensor, lse: torch.Tensor,
+                       o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Step 4: o [B, H, L, d]."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(o_rounds, "o_rounds", sh["o_rounds"], cfg.torch_dtype)
+    dev = o_rounds.device
+    _expect(lse, "lse", sh["lse"], torch.float32, dev)
+    if o is None:
+        o = torch.empty(sh["o"], dtype=cfg.torch_dtype, device=dev)
+    _expect(o, "o", sh["o"], cfg.torch_dtype, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_combine_rounds(ctypes.byref(c), _ptr(o_rounds), _ptr(lse), _ptr(o),
+                                  _stream(dev, stream)), "lsh_combine_rounds")
+    return o
+
+
+def forward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, R: torch.Tensor,
+            workspace: Optional[torch.Tensor] = None, stream=None, return_all: bool = False):
+    """All four steps on one stream; returns o (or a dict of every intermediate)."""
+    buckets = lsh_hash(cfg, qk, R, stream=stream)
+    perm, cid = lsh_sort(cfg, buckets, workspace=workspace, stream=stream)
+    o_rounds, lse = lsh_chunk_attn(cfg, qk, v, perm, cid, stream=stream)
+    o = lsh_combine_rounds(cfg, o_rounds, lse, stream=stream)
+    if return_all:
+        return {"buckets": buckets, "perm": perm, "cid": cid, "o_rounds": o_rounds,
+                "lse": lse, "o": o}
+    return o

@@ -1,0 +1,72 @@
+"""Build the HIP library of the LSH-attention forward for gfx950 (MI355X).
+
+    python -m lsh_attention_02_amd.build        # or: from lsh_attention_02_amd.build import build
+
+Compiles every csrc/*.hip with hipcc (in parallel) and links
+lsh_attention_02_amd/liblsh_attention.so in-tree.  Always recompiles.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB_NAME = "liblsh_attention.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+CXXFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # Packed FP32 instructions are disabled for all device code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the LSH-attention library)")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = [l for l in p.stdout.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l]
+    return p.returncode, "\n".join(lines)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link the library; returns its path.  Raises on failure."""
+    cc = hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    objs = [os.path.join(BUILD_DIR, s[:-4] + ".o") for s in sources]
+    jobs = [[cc, *CXXFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(_run, jobs))
+    for src, (rc, out) in zip(sources, results):
+        if verbose or rc:
+            print(f"[build] {src}\n{out}", file=sys.stderr)
+        if rc:
+            raise RuntimeError(f"hipcc failed on {src}")
+    tmp = LIB_PATH + ".tmp"
+    rc, out = _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
+    if rc:
+        print(out, file=sys.stderr)
+        raise RuntimeError("linking the LSH-attention library failed")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,181 @@
+// C ABI of the LSH-attention forward (declared in include/lsh_attention.h).
+// Every entry point validates its arguments on the host before any HIP call
+// and launches its kernels on the caller's stream without synchronising it.
+#include "lsh_attention.h"
+#include "lsh_internal.h"
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+lsh_status fail(lsh_status s, const char* what)
+{
+    g_last_error = what;
+    return s;
+}
+
+constexpr long long kMaxBytes = 1LL << 62;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lsh_status check_ptr(const void* p, const char* name)
+{
+    if (p == nullptr) {
+        g_last_error = std::string(name) + " is null";
+        return LSH_ERR_INVALID_ARG;
+    }
+    if (!aligned16(p)) {
+        g_last_error = std::string(name) + " is not 16-byte aligned";
+        return LSH_ERR_INVALID_ARG;
+    }
+    return LSH_OK;
+}
+
+// Product of positive factors, or -1 if it exceeds kMaxBytes.
+long long checked_product(std::initializer_list<long long> f)
+{
+    long long x = 1;
+    for (long long v : f) {
+        if (v <= 0) return -1;
+        if (x > kMaxBytes / v) return -1;
+        x *= v;
+    }
+    return x;
+}
+
+lsh_status check_config(const lsh_config* c)
+{
+    if (c == nullptr) return fail(LSH_ERR_INVALID_ARG, "config is null");
+    if (c->batch <= 0 || c->heads <= 0 || c->seq_len <= 0 || c->d_head <= 0 ||
+        c->n_buckets <= 0 || c->n_rounds <= 0 || c->chunk <= 0)
+        return fail(LSH_ERR_INVALID_ARG, "every size must be positive");
+    if (c->n_buckets % 2) return fail(LSH_ERR_INVALID_ARG, "n_buckets must be even");
+    if (c->seq_len % c->chunk) return fail(LSH_ERR_INVALID_ARG, "chunk must divide seq_len");
+    if (c->seq_len / c->chunk > 32767)
+        return fail(LSH_ERR_INVALID_ARG, "seq_len / chunk must be at most 32767 (int16 chunk ids)");
+    if (c->seq_len > (1 << 30)) return fail(LSH_ERR_INVALID_ARG, "seq_len must be at most 2^30");
+    if (!std::isfinite(c->scale)) return fail(LSH_ERR_INVALID_ARG, "scale must be finite");
+    if (c->causal != 0 && c->causal != 1) return fail(LSH_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (c->d_head != 64 && c->d_head != 128)
+        return fail(LSH_ERR_UNSUPPORTED, "d_head must be 64 or 128");
+    if (c->dtype != LSH_F32 && c->dtype != LSH_BF16)
+        return fail(LSH_ERR_UNSUPPORTED, "dtype must be LSH_F32 or LSH_BF16");
+    if (c->n_buckets > 32768) return fail(LSH_ERR_UNSUPPORTED, "n_buckets must be at most 32768");
+    if (c->n_rounds > 16) return fail(LSH_ERR_UNSUPPORTED, "n_rounds must be at most 16");
+    if (c->flags != 0) return fail(LSH_ERR_UNSUPPORTED, "flags must be 0");
+    const long long elem = c->dtype == LSH_BF16 ? 2 : 4;
+    // the largest buffer is o_rounds [B, H, n_r, L, d]
+    if (checked_product({c->batch, c->heads, c->n_rounds, c->seq_len, c->d_head, elem}) < 0)
+        return fail(LSH_ERR_INVALID_ARG, "a buffer would exceed 2^62 bytes");
+    return LSH_OK;
+}
+
+long bh_of(const lsh_config* c) { return (long)c->batch * c->heads; }
+
+lsh_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return LSH_OK;
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return LSH_ERR_HIP;
+}
+
+#define LSH_TRY(expr)                          \
+    do {                                       \
+        const lsh_status _s = (expr);          \
+        if (_s != LSH_OK) return _s;           \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lsh_status_string(lsh_status s)
+{
+    switch (s) {
+        case LSH_OK: return "LSH_OK";
+        case LSH_ERR_INVALID_ARG: return "LSH_ERR_INVALID_ARG: invalid argument";
+        case LSH_ERR_UNSUPPORTED: return "LSH_ERR_UNSUPPORTED: unsupported configuration";
+        case LSH_ERR_WORKSPACE: return "LSH_ERR_WORKSPACE: workspace too small";
+        case LSH_ERR_HIP: return "LSH_ERR_HIP: HIP launch failed";
+    }
+    return "unknown lsh_status";
+}
+
+const char* lsh_last_error(void) { return g_last_error.c_str(); }
+
+lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_t* buckets,
+                    void* stream)
+{
+    LSH_TRY(check_config(cfg));
+    LSH_TRY(check_ptr(qk, "qk"));
+    LSH_TRY(check_ptr(R, "R"));
+    LSH_TRY(check_ptr(buckets, "buckets"));
+    return hip_status(lshk::launch_hash(cfg->dtype, cfg->d_head, qk, R, buckets, bh_of(cfg),
+                                        cfg->seq_len, cfg->n_rounds, cfg->n_buckets / 2,
+                                        static_cast<hipStream_t>(stream)),
+                      "lsh_hash");
+}
+
+size_t lsh_sort_workspace_bytes(const lsh_config* cfg)
+{
+    if (check_config(cfg) != LSH_OK) return 0;
+    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
+    return p.counters * sizeof(int32_t);
+}
+
+lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm, int16_t* cid,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    LSH_TRY(check_config(cfg));
+    LSH_TRY(check_ptr(buckets, "buckets"));
+    LSH_TRY(check_ptr(perm, "perm"));
+    LSH_TRY(check_ptr(cid, "cid"));
+    LSH_TRY(check_ptr(workspace, "workspace"));
+    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
+    if (workspace_bytes < p.counters * sizeof(int32_t))
+        return fail(LSH_ERR_WORKSPACE, "workspace smaller than lsh_sort_workspace_bytes()");
+    return hip_status(lshk::launch_sort(buckets, perm, cid, static_cast<int32_t*>(workspace), p,
+                                        bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets,
+                                        cfg->chunk, static_cast<hipStream_t>(stream)),
+                      "lsh_sort");
+}
+
+lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v, const int32_t* perm,
+                          const int16_t* cid, void* o_rounds, float* lse, void* stream)
+{
+    LSH_TRY(check_config(cfg));
+    if (cfg->chunk != 32 && cfg->chunk != 64 && cfg->chunk != 128)
+        return fail(LSH_ERR_UNSUPPORTED, "chunk attention supports chunk 32, 64 or 128");
+    if (cfg->dtype == LSH_F32 && cfg->d_head == 128 && cfg->chunk == 128)
+        return fail(LSH_ERR_UNSUPPORTED, "float32 with d_head 128 supports chunk 32 or 64");
+    LSH_TRY(check_ptr(qk, "qk"));
+    LSH_TRY(check_ptr(v, "v"));
+    LSH_TRY(check_ptr(perm, "perm"));
+    LSH_TRY(check_ptr(cid, "cid"));
+    LSH_TRY(check_ptr(o_rounds, "o_rounds"));
+    LSH_TRY(check_ptr(lse, "lse"));
+    return hip_status(lshk::launch_chunk_attn(cfg->dtype, cfg->d_head, cfg->chunk, qk, v, perm, cid,
+                                              o_rounds, lse, bh_of(cfg), cfg->seq_len,
+                                              cfg->n_rounds, cfg->causal, cfg->scale,
+                                              static_cast<hipStream_t>(stream)),
+                      "lsh_chunk_attn");
+}
+
+lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds, const float* lse,
+                              void* o, void* stream)
+{
+    LSH_TRY(check_config(cfg));
+    LSH_TRY(check_ptr(o_rounds, "o_rounds"));
+    LSH_TRY(check_ptr(lse, "lse"));
+    LSH_TRY(check_ptr(o, "o"));
+    return hip_status(lshk::launch_combine(cfg->dtype, cfg->d_head, o_rounds, lse, o, bh_of(cfg),
+                                           cfg->seq_len, cfg->n_rounds,
+                                           static_cast<hipStream_t>(stream)),
+                      "lsh_combine_rounds");
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Round combine on gfx950 (modulabs-hub Reformer notes, "Multi-round LSH
+// attention": the hash rounds are run several times and merged):
+//   LSE_i = logsumexp_r lse[r, i],   o_i = sum_r exp(lse[r, i] - LSE_i) o_rounds[r, i].
+// Streaming and bandwidth-bound: each thread owns 16 bytes of one output row
+// and reads the same 16 bytes of that row in every round (coalesced rows).
+#include "lsh_device.h"
+#include "lsh_internal.h"
+
+namespace lshk {
+namespace {
+
+constexpr int COMB_THREADS = 256;
+constexpr int MAX_ROUNDS = 16;
+
+template <typename T, int D>
+__global__ __launch_bounds__(COMB_THREADS)
+void k_combine(const T* __restrict__ o_rounds, const float* __restrict__ lse, T* __restrict__ o,
+               long rows, int L, int n_r)
+{
+    constexpr int VE = 16 / (int)sizeof(T);        // elements per thread
+    constexpr int TPR = D / VE;                    // threads per row
+    constexpr int RPB = COMB_THREADS / TPR;        // rows per block
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    if (row >= rows) return;
+    const long bh = row / L;
+    const int i = (int)(row % L);
+
+    float l[MAX_ROUNDS];
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < MAX_ROUNDS; ++r) {
+        if (r < n_r) {
+            l[r] = lse[(bh * n_r + r) * (long)L + i];
+            m = fmaxf(m, l[r]);
+        }
+    }
+    float acc[VE];
+#pragma unroll
+    for (int x = 0; x < VE; ++x) acc[x] = 0.f;
+    float wsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < MAX_ROUNDS; ++r) {
+        if (r < n_r) {
+            const float w = __expf(l[r] - m);
+            wsum += w;
+            const uint4 raw = *reinterpret_cast<const uint4*>(
+                o_rounds + ((bh * n_r + r) * (long)L + i) * D + part * VE);
+            const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+            for (int x = 0; x < VE; ++x) acc[x] += w * to_f32(e[x]);
+        }
+    }
+    const float inv = 1.f / wsum;
+    uint4 out;
+    T* oe = reinterpret_cast<T*>(&out);
+#pragma unroll
+    for (int x = 0; x < VE; ++x) oe[x] = from_f32<T>(acc[x] * inv);
+    *reinterpret_cast<uint4*>(o + row * D + part * VE) = out;
+}
+
+template <typename T, int D>
+hipError_t launch(const void* o_rounds, const float* lse, void* o, long bh, int L, int n_r,
+                  hipStream_t s)
+{
+    constexpr int RPB = COMB_THREADS / (D / (16 / (int)sizeof(T)));
+    const long rows = bh * L;
+    const long blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((k_combine<T, D>), dim3((unsigned)blocks), dim3(COMB_THREADS), 0, s,
+                       static_cast<const T*>(o_rounds), lse, static_cast<T*>(o), rows, L, n_r);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
+                          long bh, int L, int n_rounds, hipStream_t stream)
+{
+    if (dtype == 1)
+        return d_head == 64 ? launch<bf16_t, 64>(o_rounds, lse, o, bh, L, n_rounds, stream)
+                            : launch<bf16_t, 128>(o_rounds, lse, o, bh, L, n_rounds, stream);
+    return d_head == 64 ? launch<float, 64>(o_rounds, lse, o, bh, L, n_rounds, stream)
+                        : launch<float, 128>(o_rounds, lse, o, bh, L, n_rounds, stream);
+}
+
+}  // namespace lshk

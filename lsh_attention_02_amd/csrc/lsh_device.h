@@ -1,0 +1,74 @@
+// Device-side helpers shared by the gfx950 kernels of the LSH-attention forward.
+//
+// MFMA conventions (CDNA3/CDNA4 32x32 tiles, wave64):
+//   D[32x32] += A[32xK] * B[Kx32], K = 2*KPL per instruction.
+//   lane l:  A operand = row  (l % 32), k = KPL*(l / 32) + [0, KPL)
+//            B operand = col  (l % 32), k = KPL*(l / 32) + [0, KPL)
+//            D element j (0..15) = row 8*(j/4) + 4*(l/32) + (j%4), col (l % 32)
+// bf16 uses v_mfma_f32_32x32x16_bf16 (KPL = 8), f32 uses v_mfma_f32_32x32x2_f32
+// (KPL = 1).  The contraction only needs A and B to agree on which k each
+// (lane, slot) holds, so any consistent permutation of k is allowed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lshk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Storage type of bfloat16 tensors in memory.
+struct bf16_t { uint16_t bits; };
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16_t> {
+    static constexpr int KPL = 8;          // elements per lane per instruction
+    static constexpr int KSTEP = 16;       // k per instruction
+    typedef bf16x8 Frag;
+    static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    // 8 consecutive elements from 16-byte-aligned memory (global or LDS).
+    static __device__ __forceinline__ Frag load(const bf16_t* p) {
+        return *reinterpret_cast<const Frag*>(p);
+    }
+    static __device__ __forceinline__ Frag zero() { return Frag{}; }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int KPL = 1;
+    static constexpr int KSTEP = 2;
+    typedef float Frag;
+    static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ Frag load(const float* p) { return *p; }
+    static __device__ __forceinline__ Frag zero() { return 0.f; }
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return bf16_t{f32_to_bf16_rne(f)}; }
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace lshk

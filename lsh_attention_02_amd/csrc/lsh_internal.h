@@ -1,0 +1,37 @@
+// Internal launchers between the C ABI (lsh_api.hip) and the kernel files.
+// Arguments are already validated by the caller; every launcher returns the
+// hipGetLastError() status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lshk {
+
+hipError_t launch_hash(int dtype, int d_head, const void* qk, const void* R, int32_t* buckets,
+                       long bh, int L, int n_rounds, int ncol, hipStream_t stream);
+
+// Sort geometry: positions of one (b, h, r) segment are split into tiles of
+// `tile` positions; the workspace holds one int32 counter per (segment, tile, bucket).
+struct SortPlan {
+    int tile;
+    int ntiles;
+    long nseg;
+    size_t counters;   // nseg * ntiles * n_buckets
+};
+SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets);
+
+hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
+                       const SortPlan& plan, long bh, int L, int n_rounds, int n_buckets,
+                       int chunk, hipStream_t stream);
+
+hipError_t launch_chunk_attn(int dtype, int d_head, int chunk, const void* qk, const void* v,
+                             const int32_t* perm, const int16_t* cid, void* o_rounds, float* lse,
+                             long bh, int L, int n_rounds, int causal, float scale,
+                             hipStream_t stream);
+
+hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
+                          long bh, int L, int n_rounds, hipStream_t stream);
+
+}  // namespace lshk

@@ -1,0 +1,201 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Layered checks, so that one near-tie hash flip cannot fail the later steps:
+  hash     GPU buckets equal the oracle's wherever the oracle's fp64 top-2
+           margin exceeds 1e-4; every mismatch is a near-tie (counted).
+  sort     GPU perm/cid equal the oracle's stable counting sort of the GPU's
+           own buckets (bit-exact).  At full size: the properties that define
+           that sort uniquely (permutation, keys non-decreasing, equal keys in
+           position order, cid = slot // chunk).
+  attend   GPU o_rounds/lse against the oracle's attention fed the GPU's
+           perm/cid.
+  combine  GPU o against the oracle's combine fed the GPU's o_rounds/lse.
+  forward  GPU o against the oracle's forward from scratch (whole heads whose
+           buckets all agree).
+Error metric for float outputs: max|gpu - ref| / max|ref| over the tensor
+(or over the sampled rows).  Gates: 1e-5 for float32, 2e-2 for bfloat16.
+lse gate: |gpu - ref| <= LSE_ATOL + 1e-6 |ref|; 1e-6 relative covers the fp32
+rounding of the self-penalised scores, which sit near -1e5 (ulp 2^-7).
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+from typing import Dict
+
+import numpy as np
+import torch
+
+import lsh_attention_02_amd as lsh
+import oracle.lsh_oracle as O
+from synthetic_inputs import Workload, make_inputs
+
+GATE = {"f32": 1e-5, "bf16": 2e-2}
+LSE_ATOL = {"f32": 2e-5, "bf16": 1e-3}
+LSE_RTOL = 1e-6
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def cfg_of(w: Workload, scale=None) -> lsh.LSHConfig:
+    return lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
+                         w.causal, dtype=w.dtype, scale=scale)
+
+
+def upload(w: Workload, x: Dict[str, np.ndarray], device="cuda:0"):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    # the arrays hold values exactly representable in dt, so the conversion is exact
+    return {k: torch.from_numpy(x[k]).to(device).to(dt).contiguous() for k in ("qk", "v", "R")}
+
+
+def run_gpu(w: Workload, x, scale=None, device="cuda:0"):
+    cfg = cfg_of(w, scale)
+    t = upload(w, x, device)
+    out = lsh.forward(cfg, t["qk"], t["v"], t["R"], return_all=True)
+    torch.cuda.synchronize()
+    return cfg, t, out
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(got.astype(np.float64) - ref))) / max(den, 1e-300)
+
+
+def check_lse(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> float:
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = LSE_ATOL[dtype] + LSE_RTOL * np.abs(ref)
+    worst = float(np.max(err - bound))
+    assert worst <= 0, f"{what}: lse off by up to {float(np.max(err)):.3g} (excess {worst:.3g})"
+    return float(np.max(err))
+
+
+def check_hash(gpu_b: np.ndarray, ref_b: np.ndarray, margins: np.ndarray, what: str) -> dict:
+    mism = gpu_b != ref_b
+    near = margins <= O.NEAR_TIE_MARGIN
+    bad = mism & ~near
+    assert not bad.any(), f"{what}: {int(bad.sum())} bucket mismatches with margin > 1e-4"
+    assert np.all((gpu_b >= 0)), what
+    return {"near_ties": int(near.sum()), "near_tie_mismatches": int(mism.sum()), "hashes": int(mism.size)}
+
+
+def full_parity(w: Workload, scale=None, x=None) -> dict:
+    """Every output of every step against the oracle (small workloads)."""
+    t0 = time.time()
+    x = make_inputs(w) if x is None else x
+    cfg, _, g = run_gpu(w, x, scale)
+    sc = cfg.score_scale
+    qk = x["qk"].astype(np.float64)
+    v = x["v"].astype(np.float64)
+    R = x["R"].astype(np.float64)
+    gb = to_np(g["buckets"])
+    rep = {"workload": w.name}
+    # hash
+    ob, om = O.hash_buckets(qk, R)
+    rep.update(check_hash(gb, ob, om, w.name))
+    # sort of the GPU's own buckets
+    sp, sc_id = O.sort_rounds(gb, w.n_buckets, w.chunk)
+    assert np.array_equal(to_np(g["perm"]), sp), f"{w.name}: perm differs from the stable sort"
+    assert np.array_equal(to_np(g["cid"]), sc_id), f"{w.name}: cid differs"
+    # attention fed the GPU's perm/cid
+    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc)
+    rep["o_rounds_err"] = rel_err(to_np(g["o_rounds"]), o_r)
+    assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
+    rep["lse_abs_err"] = check_lse(to_np(g["lse"]), lse, w.dtype, w.name)
+    # combine fed the GPU's o_rounds/lse
+    oc, _ = O.combine_rounds(to_np(g["o_rounds"]).astype(np.float64), to_np(g["lse"]).astype(np.float64))
+    rep["combine_err"] = rel_err(to_np(g["o"]), oc)
+    assert rep["combine_err"] <= GATE[w.dtype], (w.name, "combine", rep["combine_err"])
+    # forward from scratch, on the heads whose buckets agree everywhere
+    same = np.all(gb == ob, axis=(2, 3))
+    rep["heads_bucket_exact"] = f"{int(same.sum())}/{same.size}"
+    if same.any():
+        pf, cf = O.sort_rounds(ob, w.n_buckets, w.chunk)
+        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc)
+        of, _ = O.combine_rounds(of_r, lf)
+        go = to_np(g["o"])
+        rep["forward_err"] = rel_err(go[same], of[same])
+        assert rep["forward_err"] <= GATE[w.dtype], (w.name, "forward", rep["forward_err"])
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[parity] {rep}")
+    return rep
+
+
+# --------------------------------------------------------------------------- full-size, sampled
+def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, what: str) -> None:
+    """The properties that determine the stable sort uniquely, checked on every segment."""
+    B, H, n_r, L = gb.shape
+    b2 = gb.reshape(-1, L).astype(np.int64)
+    p2 = gp.reshape(-1, L).astype(np.int64)
+    assert np.array_equal(np.sort(p2, axis=1), np.broadcast_to(np.arange(L), p2.shape)), \
+        f"{what}: perm is not a permutation"
+    keys = np.take_along_axis(b2, p2, axis=1)
+    dk = np.diff(keys, axis=1)
+    assert np.all(dk >= 0), f"{what}: buckets not sorted"
+    assert np.all((dk > 0) | (np.diff(p2, axis=1) > 0)), f"{what}: equal buckets out of position order"
+    slot = np.empty_like(p2)
+    np.put_along_axis(slot, p2, np.broadcast_to(np.arange(L), p2.shape), axis=1)
+    want = (slot // chunk).reshape(B, H, n_r, L).transpose(0, 1, 3, 2)
+    assert np.array_equal(gc.astype(np.int64), want), f"{what}: cid differs from slot // chunk"
+
+
+def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0) -> dict:
+    """Full-size workload: every sort output, sampled hashes, rows and tokens."""
+    t0 = time.time()
+    log(f"[sampled] {w.name}: generating inputs")
+    x = make_inputs(w)
+    log(f"[sampled] {w.name}: running the GPU path ({time.time() - t0:.1f}s)")
+    cfg, t, g = run_gpu(w, x)
+    sc = cfg.score_scale
+    B, H, L, d, n_r = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
+    rng = np.random.default_rng(seed)
+    rep = {"workload": w.name}
+    gb = to_np(g["buckets"])
+    gp = to_np(g["perm"])
+    gc = to_np(g["cid"])
+    log(f"[sampled] {w.name}: sort properties ({time.time() - t0:.1f}s)")
+    sort_properties(gb, gp, gc, w.chunk, w.name)
+    # sampled hashes
+    sb, sh, sr, si = (rng.integers(0, B, n_samples), rng.integers(0, H, n_samples),
+                      rng.integers(0, n_r, n_samples), rng.integers(0, L, n_samples))
+    ob = np.empty(n_samples, np.int64)
+    om = np.empty(n_samples)
+    for s in range(n_samples):
+        ob[s], om[s] = O.hash_one(x["qk"][sb[s], sh[s], si[s]].astype(np.float64),
+                                  x["R"][sr[s]].astype(np.float64))
+    rep.update(check_hash(gb[sb, sh, sr, si], ob, om, w.name))
+    # sampled attention rows, fed the GPU's perm/cid
+    log(f"[sampled] {w.name}: attention rows ({time.time() - t0:.1f}s)")
+    idx = torch.from_numpy(np.stack([sb, sh, sr, si])).to(t["qk"].device)
+    g_or = to_np(g["o_rounds"][idx[0], idx[1], idx[2], idx[3]])
+    g_lse = to_np(g["lse"][idx[0], idx[1], idx[2], idx[3]])
+    ref_o = np.empty((n_samples, d))
+    ref_l = np.empty(n_samples)
+    for s in range(n_samples):
+        b, h = sb[s], sh[s]
+        ref_o[s], ref_l[s] = O.attention_one(x["qk"][b, h], x["v"][b, h], gp[b, h], gc[b, h],
+                                             int(sr[s]), int(si[s]), w.chunk, w.causal, sc)
+    rep["o_rounds_err"] = rel_err(g_or, ref_o)
+    assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
+    rep["lse_abs_err"] = check_lse(g_lse, ref_l, w.dtype, w.name)
+    # sampled combine, fed the GPU's o_rounds/lse
+    tok = torch.from_numpy(np.stack([sb, sh, si])).to(t["qk"].device)
+    g_o = to_np(g["o"][tok[0], tok[1], tok[2]])
+    g_orall = to_np(g["o_rounds"][tok[0], tok[1], :, tok[2]])      # [S, n_r, d]
+    g_lall = to_np(g["lse"][tok[0], tok[1], :, tok[2]])            # [S, n_r]
+    oc, _ = O.combine_rounds(g_orall[:, :, None, :].astype(np.float64),
+                             g_lall[:, :, None].astype(np.float64))
+    rep["combine_err"] = rel_err(g_o, oc[:, 0])
+    assert rep["combine_err"] <= GATE[w.dtype], (w.name, "combine", rep["combine_err"])
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[sampled] {rep}")
+    return rep

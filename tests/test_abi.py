@@ -1,0 +1,175 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and every argument check returns its status before any HIP call.  Nothing here
+launches a kernel: every call fails validation first (fake pointers are only
+used where an earlier check is certain to fail)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import lsh_attention_02_amd as lsh
+from lsh_attention_02_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsh_attention.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    if torch.cuda.is_available():
+        # These tests pass fake device pointers that validation must reject; a
+        # mistake in a test would then reach a real GPU.  They run without one.
+        pytest.skip("ABI validation tests run on hosts without a GPU")
+    if not os.path.exists(B.LIB_PATH):
+        from lsh_attention_02_amd.build import build
+        build()
+    return lsh.load_library()
+
+
+def cfg(**kw):
+    base = dict(batch=1, heads=8, seq_len=4096, d_head=64, n_buckets=64, n_rounds=2, chunk=64,
+                causal=True, dtype="bf16")
+    base.update(kw)
+    return lsh.LSHConfig(**base).to_c()
+
+
+def raw(c):
+    return ctypes.byref(c)
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced (validation fails first)
+NULL = ctypes.c_void_p(0)
+MISALIGNED = ctypes.c_void_p((1 << 20) + 8)
+
+
+def test_exports_match_header(lib):
+    with open(HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(lsh_\w+)\s*\(", text, flags=re.M))
+    assert declared == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(B.CConfig) == 11 * 4
+    assert [f[0] for f in B.CConfig._fields_] == ["batch", "heads", "seq_len", "d_head", "n_buckets",
+                                                  "n_rounds", "chunk", "causal", "scale", "dtype",
+                                                  "flags"]
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.lsh_status_string(s).decode().startswith(
+            ["LSH_OK", "LSH_ERR_INVALID_ARG", "LSH_ERR_UNSUPPORTED", "LSH_ERR_WORKSPACE", "LSH_ERR_HIP"][s])
+    assert b"unknown" in lib.lsh_status_string(99)
+
+
+BAD_CONFIGS = [
+    (dict(batch=0), B.LSH_ERR_INVALID_ARG, "positive"),
+    (dict(heads=-1), B.LSH_ERR_INVALID_ARG, "positive"),
+    (dict(n_buckets=63), B.LSH_ERR_INVALID_ARG, "even"),
+    (dict(n_buckets=0), B.LSH_ERR_INVALID_ARG, "positive"),
+    (dict(seq_len=4000), B.LSH_ERR_INVALID_ARG, "divide"),
+    (dict(seq_len=32768 * 32, chunk=32), B.LSH_ERR_INVALID_ARG, "32767"),
+    (dict(seq_len=(1 << 30) + (1 << 16), chunk=1 << 16), B.LSH_ERR_INVALID_ARG, "2^30"),
+    (dict(scale=float("nan")), B.LSH_ERR_INVALID_ARG, "finite"),
+    (dict(scale=float("inf")), B.LSH_ERR_INVALID_ARG, "finite"),
+    (dict(d_head=96), B.LSH_ERR_UNSUPPORTED, "d_head"),
+    (dict(n_buckets=65536), B.LSH_ERR_UNSUPPORTED, "32768"),
+    (dict(n_rounds=17), B.LSH_ERR_UNSUPPORTED, "16"),
+    (dict(flags=1), B.LSH_ERR_UNSUPPORTED, "flags"),
+    # o_rounds = 2^20 * 2^10 * 16 * 2^20 * 128 float32 = 2^63 bytes
+    (dict(batch=1 << 20, heads=1 << 10, seq_len=1 << 20, chunk=1024, n_rounds=16, d_head=128,
+          dtype="f32"), B.LSH_ERR_INVALID_ARG, "2^62"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_CONFIGS)
+def test_bad_config_every_call(lib, kw, status, msg):
+    c = cfg(**kw)
+    calls = [
+        lambda: lib.lsh_hash(raw(c), FAKE, FAKE, FAKE, NULL),
+        lambda: lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL),
+        lambda: lib.lsh_chunk_attn(raw(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL),
+        lambda: lib.lsh_combine_rounds(raw(c), FAKE, FAKE, FAKE, NULL),
+    ]
+    for call in calls:
+        assert call() == status
+        assert msg in lib.lsh_last_error().decode()
+    assert lib.lsh_sort_workspace_bytes(raw(c)) == 0
+
+
+def test_bad_dtype_and_causal(lib):
+    c = cfg()
+    c.dtype = 7
+    assert lib.lsh_hash(raw(c), FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_UNSUPPORTED
+    c = cfg()
+    c.causal = 2
+    assert lib.lsh_hash(raw(c), FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
+
+
+def test_null_config(lib):
+    assert lib.lsh_hash(None, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
+    assert b"config" in lib.lsh_last_error()
+
+
+@pytest.mark.parametrize("which", range(3))
+def test_hash_pointer_checks(lib, which):
+    c = cfg()
+    for bad, word in ((NULL, "null"), (MISALIGNED, "aligned")):
+        args = [FAKE, FAKE, FAKE]
+        args[which] = bad
+        assert lib.lsh_hash(raw(c), *args, NULL) == B.LSH_ERR_INVALID_ARG
+        assert word in lib.lsh_last_error().decode()
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_attn_pointer_checks(lib, which):
+    c = cfg()
+    args = [FAKE] * 6
+    args[which] = NULL
+    assert lib.lsh_chunk_attn(raw(c), *args, NULL) == B.LSH_ERR_INVALID_ARG
+
+
+def test_attn_chunk_support(lib):
+    for chunk in (16, 256):
+        c = cfg(chunk=chunk, seq_len=4096)
+        assert lib.lsh_chunk_attn(raw(c), NULL, NULL, NULL, NULL, NULL, NULL, NULL) == B.LSH_ERR_UNSUPPORTED
+    c = cfg(dtype="f32", d_head=128, chunk=128)
+    assert lib.lsh_chunk_attn(raw(c), NULL, NULL, NULL, NULL, NULL, NULL, NULL) == B.LSH_ERR_UNSUPPORTED
+
+
+def test_sort_workspace(lib):
+    # tile = smallest power of two >= max(2048, 4 * n_buckets), at most 65536, at most L;
+    # one int32 counter per (segment, tile, bucket)
+    cases = [(dict(), 1 * 8 * 2 * 2 * 64),
+             (dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8), 8 * 8 * 16 * 1024),
+             (dict(seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128), 8 * 4 * 16 * 16384),
+             (dict(seq_len=1024, n_buckets=32, n_rounds=1, heads=1), 1 * 1 * 1 * 32)]
+    for kw, counters in cases:
+        c = cfg(**kw)
+        assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * counters, kw
+    c = cfg()
+    need = lib.lsh_sort_workspace_bytes(raw(c))
+    assert lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == B.LSH_ERR_WORKSPACE
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    c = lsh.LSHConfig(1, 1, 128, 64, 8, 1, 64, False, dtype="f32")
+    qk = torch.zeros(1, 1, 128, 64)
+    R = torch.zeros(1, 64, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        lsh.lsh_hash(c, qk, R)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/liblsh_attention.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load_library()
