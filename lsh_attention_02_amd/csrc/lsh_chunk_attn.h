@@ -1,0 +1,366 @@
+// Chunked LSH attention on gfx950, one output per hash round (kernel template;
+// instantiated by the lsh_chunk_attn_*.hip files).
+//
+// For round r of (batch row, head) the positions are in sorted order perm; the
+// sorted sequence is cut into chunks of C; the queries of chunk k attend to the
+// keys of chunks k-1 and k (ai-scholar Reformer article and Ultralytics
+// "Reformer" glossary, sections on LSH attention).  Scores follow the scaled
+// dot-product form of the ai-scholar article; the query itself is penalised
+// and later positions are dropped when causal (modulabs-hub notes, "LSH
+// attention"); the duplicate-count term -log N_ij (N_ij = rounds whose window
+// for i holds j) makes the round combine equal to attention over the union of
+// the rounds' windows.
+//
+// Workgroup = C/32 waves; it walks a run of consecutive chunks of one
+// (b, h, r).  Each chunk's qk rows (row-major) and v rows (transposed) are
+// gathered once into LDS and kept for the next chunk, whose look-back window
+// they form.  The rows of chunk k+1 are loaded into registers while chunk k is
+// computed (positions two chunks ahead), so the gathers overlap the math.
+// Wave w takes the 32 queries in rows 32w.. of the chunk:
+//   S^T[key, q] = K[key, :] · Q[q, :]     (A = key rows, B = query rows)
+// so each lane holds one query's scores as registers (keys 8(j/4)+4h+(j%4) of
+// each 32-key tile), the softmax is in-register plus one exchange between the
+// two half-waves, and the probabilities feed the PV product directly as the B
+// operand:
+//   O^T[d, q] = V^T[d, key] · P^T[key, q]
+// with V^T read from LDS in the same key order.  Rows of o_rounds and lse go
+// back to original position order.  Scores are kept in base 2 (exp2/log2).
+//
+// Duplicate counts: chunk ids of all rounds are packed two per 32-bit word
+// (NDW words per token, padded with equal values on both sides, which always
+// compare as inside).  For key chunk k and query chunk q of a round, the key is
+// inside the query's window when u = k - (q - 1) (mod 2^16) is 0 or 1; per word
+// that is one packed subtract, shift, min and a dot2 that adds both halves.
+#pragma once
+
+#include "lsh_device.h"
+#include "lsh_internal.h"
+
+namespace lshk {
+namespace attn {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float SELF_PENALTY = 1.0e5f;               // score units
+constexpr int RUN = 16;                              // chunks per workgroup
+
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_pk_sub_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
+// Per 16-bit half: 1 if the half is >= 2, else 0.
+__device__ __forceinline__ uint32_t pk_ge2(uint32_t u, uint32_t ones)
+{
+    uint32_t d;
+    asm("v_pk_lshrrev_b16 %0, %2, %1\n\tv_pk_min_u16 %0, %0, %2" : "=&v"(d) : "v"(u), "v"(ones));
+    return d;
+}
+
+__device__ __forceinline__ uint32_t dot2_add(uint32_t a, uint32_t ones, uint32_t acc)
+{
+    typedef unsigned short u2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_udot2(__builtin_bit_cast(u2, a), __builtin_bit_cast(u2, ones), acc, false);
+}
+
+// Rounds (over the NDW words) in which the key is outside the query's window.
+template <int NDW>
+__device__ __forceinline__ uint32_t rounds_outside(const uint32_t (&q1)[NDW], const uint32_t* kc,
+                                                   uint32_t ones)
+{
+    uint32_t w[NDW];
+    if constexpr (NDW == 1) {
+        w[0] = kc[0];
+    } else if constexpr (NDW == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(kc);
+        w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < NDW / 4; ++h) {
+            const uint4 x = *reinterpret_cast<const uint4*>(kc + 4 * h);
+            w[4 * h] = x.x; w[4 * h + 1] = x.y; w[4 * h + 2] = x.z; w[4 * h + 3] = x.w;
+        }
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) acc = dot2_add(pk_ge2(pk_sub_u16(w[i], q1[i]), ones), ones, acc);
+    return acc;
+}
+
+template <typename T, int D, int C, int NDW>
+struct Lds {
+    static constexpr int KROW = D + 16 / (int)sizeof(T);   // qk row, padded by 16 bytes
+    static constexpr int VROW = C + 4;                      // v^T row (one slot's keys)
+    T k[2][C * KROW];
+    T vt[2][D * VROW];
+    int pos[2][C];
+    uint32_t cid[2][C * NDW];
+};
+
+template <typename T, int D, int C, int NDW>
+__global__ __launch_bounds__(2 * C)
+void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
+                  const int32_t* __restrict__ perm, const int16_t* __restrict__ cid,
+                  T* __restrict__ o_rounds, float* __restrict__ lse, int L, int n_r, int causal,
+                  float scale_log2, int nruns)
+{
+    using M = Mfma<T>;
+    using S = Lds<T, D, C, NDW>;
+    constexpr int NTH = 2 * C;
+    constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+    constexpr int KROW = S::KROW, VROW = S::VROW;
+    constexpr int CT = C / 32, NKT = 2 * CT, DT = D / 32;
+    constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
+    constexpr int GPT = C * VPR / NTH;                 // 16-byte pieces per thread per tensor
+    constexpr int RSTEP = NTH / VPR;                   // rows between a thread's pieces
+    __shared__ __attribute__((aligned(16))) S sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int grow = tid / VPR, gpiece = tid % VPR;   // gather: rows grow + i*RSTEP, piece gpiece
+
+    int bid = blockIdx.x;
+    const int r = bid % n_r;
+    bid /= n_r;
+    const int run = bid % nruns;
+    const long bh = bid / nruns;
+    const int nchunks = L / C;
+    const int k0 = run * RUN, k1 = min(k0 + RUN, nchunks);
+
+    const T* qb = qk + bh * (long)L * D;
+    const T* vb = v + bh * (long)L * D;
+    const int32_t* pr = perm + (bh * n_r + r) * (long)L;
+    const int16_t* cb = cid + bh * (long)L * n_r;
+    T* ob = o_rounds + (bh * n_r + r) * (long)L * D;
+    float* lb = lse + (bh * n_r + r) * (long)L;
+    const uint32_t ones = 0x00010001u;
+
+    // positions come from the caller's perm: keep every gather inside the row
+    auto position = [&](int kk, int row) { return min(max(pr[kk * C + row], 0), L - 1); };
+
+    int gpos[GPT];         // positions of this thread's gather rows, next chunk to load
+    int mypos = 0;         // position of row tid (tid < C), next chunk to load
+    u32x4 kreg[GPT], vreg[GPT];
+    uint32_t creg[NDW];
+    int rpos = 0;          // position of row tid for the chunk held in registers
+
+    auto fetch_positions = [&](int kk) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) gpos[i] = position(kk, grow + i * RSTEP);
+        if (tid < C) mypos = position(kk, tid);
+    };
+    auto fetch_rows = [&]() {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            kreg[i] = *reinterpret_cast<const u32x4*>(qb + (long)gpos[i] * D + gpiece * VE);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vb + (long)gpos[i] * D + gpiece * VE);
+        }
+        rpos = mypos;
+        if (tid < C) {
+            const int16_t* cr = cb + (long)mypos * n_r;
+#pragma unroll
+            for (int w = 0; w < NDW; ++w) {
+                const uint32_t lo = (2 * w < n_r) ? (uint16_t)cr[2 * w] : 0u;
+                const uint32_t hi = (2 * w + 1 < n_r) ? (uint16_t)cr[2 * w + 1] : 0u;
+                creg[w] = lo | (hi << 16);
+            }
+        }
+    };
+    auto store_rows = [&](int sl) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int row = grow + i * RSTEP;
+            *reinterpret_cast<u32x4*>(&sm.k[sl][row * KROW + gpiece * VE]) = kreg[i];
+            const u32x4 wv = vreg[i];
+#pragma unroll
+            for (int x = 0; x < VE; ++x) {
+                T e;
+                if constexpr (sizeof(T) == 2) e = bf16_t{(uint16_t)(wv[x >> 1] >> (16 * (x & 1)))};
+                else e = __uint_as_float(wv[x]);
+                sm.vt[sl][(gpiece * VE + x) * VROW + row] = e;
+            }
+        }
+        if (tid < C) {
+            sm.pos[sl][tid] = rpos;
+#pragma unroll
+            for (int w = 0; w < NDW; ++w) sm.cid[sl][tid * NDW + w] = creg[w];
+        }
+    };
+
+    const int kfirst = max(k0 - 1, 0);
+    fetch_positions(kfirst);
+    fetch_rows();
+    if (kfirst + 1 < k1) fetch_positions(kfirst + 1);
+
+    for (int k = kfirst; k < k1; ++k) {
+        const int cur = k & 1, prv = cur ^ 1;
+        store_rows(cur);               // slot of chunk k-2, released by the last barrier
+        __syncthreads();
+        if (k + 1 < k1) {
+            fetch_rows();              // chunk k+1 (positions fetched an iteration ago)
+            if (k + 2 < k1) fetch_positions(k + 2);
+        }
+        if (k >= k0) {
+            const bool has_prev = k > 0;
+            const int qrow = wave * 32 + n;
+            const int qpos = sm.pos[cur][qrow];
+
+            typename M::Frag bq[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                bq[ks] = M::load(&sm.k[cur][qrow * KROW + ks * KSTEP + hh * KPL]);
+            uint32_t q1[NDW];          // query chunk ids minus one, per half
+#pragma unroll
+            for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[cur][qrow * NDW + w], ones);
+
+            // ---- S^T tiles: tiles [0, CT) are the previous chunk, [CT, 2CT) this one
+            f32x16 s[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                s[t] = f32x16{};
+                if (t < CT && !has_prev) continue;
+                const int slk = t < CT ? prv : cur;
+                const T* kr = &sm.k[slk][((t % CT) * 32 + n) * KROW + hh * KPL];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) s[t] = M::mma(M::load(kr + ks * KSTEP), bq[ks], s[t]);
+            }
+
+            // ---- scale and duplicate counts; self penalty on the diagonal tile;
+            //      causal cut; running max
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                if (t < CT && !has_prev) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) s[t][j] = -INFINITY;
+                    continue;
+                }
+                const int slk = t < CT ? prv : cur;
+                const bool diag = t == CT + wave;   // the tile holding the queries themselves
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int krow0 = (t % CT) * 32 + 8 * g + 4 * hh;
+                    const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int j = 4 * g + x;
+                        const int kpos = x == 0 ? kp.x : x == 1 ? kp.y : x == 2 ? kp.z : kp.w;
+                        const uint32_t outs =
+                            rounds_outside<NDW>(q1, &sm.cid[slk][(krow0 + x) * NDW], ones);
+                        const float lg = __log2f((float)max(n_r - (int)outs, 1));
+                        float sc = fmaf(s[t][j], scale_log2, -lg);
+                        if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
+                        if (causal && kpos > qpos) sc = -INFINITY;
+                        s[t][j] = sc;
+                        mx = fmaxf(mx, sc);
+                    }
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+            float sum = 0.f;
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(s[t][j] - mx);
+                    s[t][j] = p;
+                    sum += p;
+                }
+            }
+            sum += __shfl_xor(sum, 32);
+
+            // ---- O^T = V^T · P^T
+            f32x16 o[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                if (t < CT && !has_prev) continue;
+                const int slk = t < CT ? prv : cur;
+                const int key0 = (t % CT) * 32;
+                if constexpr (KPL == 8) {
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        bf16x8 b;
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) b[x] = (__bf16)s[t][8 * half + x];
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const T* vr = &sm.vt[slk][(dt * 32 + n) * VROW + key0 + 16 * half + 4 * hh];
+                            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr);
+                            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 8);
+                            const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                            o[dt] = M::mma(a, b, o[dt]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = key0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const float a = to_f32(sm.vt[slk][(dt * 32 + n) * VROW + key]);
+                            o[dt] = M::mma(a, s[t][j], o[dt]);
+                        }
+                    }
+                }
+            }
+
+            // ---- normalise, store the query's row and its lse
+            const float inv = 1.f / sum;
+            T* orow = ob + (long)qpos * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = dt * 32 + 8 * g + 4 * hh;
+                    if constexpr (sizeof(T) == 2) {
+                        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[dt][4 * g + 0] * inv) |
+                                            ((uint32_t)f32_to_bf16_rne(o[dt][4 * g + 1] * inv) << 16);
+                        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[dt][4 * g + 2] * inv) |
+                                            ((uint32_t)f32_to_bf16_rne(o[dt][4 * g + 3] * inv) << 16);
+                        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+                    } else {
+                        *reinterpret_cast<float4*>(orow + d0) =
+                            make_float4(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv,
+                                        o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+                    }
+                }
+            }
+            if (hh == 0) lb[qpos] = (mx + __log2f(sum)) * LN2;
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T, int D, int C, int NDW>
+hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
+                      void* o_rounds, float* lse, long bh, int L, int n_r, int causal, float scale,
+                      hipStream_t s)
+{
+    const int nchunks = L / C;
+    const int nruns = (nchunks + RUN - 1) / RUN;
+    const long blocks = bh * nruns * n_r;
+    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW>), dim3((unsigned)blocks), dim3(2 * C), 0, s,
+                       static_cast<const T*>(qk), static_cast<const T*>(v), perm, cid,
+                       static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns);
+    return hipGetLastError();
+}
+
+// Dispatch on the number of packed chunk-id words (1, 2, 4 or 8 for up to 16 rounds).
+template <typename T, int D, int C>
+hipError_t launch_ndw(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
+                      void* o, float* lse, long bh, int L, int n_r, int causal, float scale,
+                      hipStream_t s)
+{
+    if (n_r <= 2) return launch_one<T, D, C, 1>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (n_r <= 4) return launch_one<T, D, C, 2>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (n_r <= 8) return launch_one<T, D, C, 4>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    return launch_one<T, D, C, 8>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+}
+
+}  // namespace attn
+}  // namespace lshk

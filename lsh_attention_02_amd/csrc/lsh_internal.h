@@ -31,6 +31,18 @@ hipError_t launch_chunk_attn(int dtype, int d_head, int chunk, const void* qk, c
                              long bh, int L, int n_rounds, int causal, float scale,
                              hipStream_t stream);
 
+namespace attn {
+// One instantiation unit per element type / head size (compiled in parallel).
+#define LSH_ATTN_LAUNCH_ARGS                                                                    \
+    int chunk, const void *qk, const void *v, const int32_t *perm, const int16_t *cid,          \
+        void *o_rounds, float *lse, long bh, int L, int n_rounds, int causal, float scale,       \
+        hipStream_t stream
+hipError_t launch_bf16_d64(LSH_ATTN_LAUNCH_ARGS);
+hipError_t launch_bf16_d128(LSH_ATTN_LAUNCH_ARGS);
+hipError_t launch_f32_d64(LSH_ATTN_LAUNCH_ARGS);
+hipError_t launch_f32_d128(LSH_ATTN_LAUNCH_ARGS);
+}  // namespace attn
+
 hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
                           long bh, int L, int n_rounds, hipStream_t stream);
 
