@@ -11,20 +11,21 @@
 // for i holds j) makes the round combine equal to attention over the union of
 // the rounds' windows.
 //
-// Workgroup = C/32 waves; it walks a run of consecutive chunks of one
+// Workgroup = C/16 waves; it walks a run of consecutive chunks of one
 // (b, h, r).  Each chunk's qk rows (row-major) and v rows (transposed) are
 // gathered once into LDS and kept for the next chunk, whose look-back window
 // they form.  The rows of chunk k+1 are loaded into registers while chunk k is
 // computed (positions two chunks ahead), so the gathers overlap the math.
-// Wave w takes the 32 queries in rows 32w.. of the chunk:
+// Wave w takes the 16 queries in rows 16w.. of the chunk (16x16 MFMA tiles,
+// so that four waves share one chunk's LDS tiles and each SIMD holds two waves):
 //   S^T[key, q] = K[key, :] · Q[q, :]     (A = key rows, B = query rows)
-// so each lane holds one query's scores as registers (keys 8(j/4)+4h+(j%4) of
-// each 32-key tile), the softmax is in-register plus one exchange between the
-// two half-waves, and the probabilities feed the PV product directly as the B
-// operand:
+// so each lane holds one query's scores as registers (keys 4(l/16)+j of each
+// 16-key tile), the softmax is in-register plus two cross-lane exchanges, and
+// the probabilities feed the PV product directly as the B operand:
 //   O^T[d, q] = V^T[d, key] · P^T[key, q]
 // with V^T read from LDS in the same key order.  Rows of o_rounds and lse go
-// back to original position order.  Scores are kept in base 2 (exp2/log2).
+// back to original position order.  Scores are kept in base 2 (exp2/log2);
+// -log2 N comes from a small LDS table indexed by the rounds outside.
 //
 // Duplicate counts: chunk ids of all rounds are packed two per 32-bit word
 // (NDW words per token, padded with equal values on both sides, which always
@@ -97,28 +98,30 @@ struct Lds {
     T vt[2][D * VROW];
     int pos[2][C];
     uint32_t cid[2][C * NDW];
+    float neg_log2[32];            // neg_log2[o] = -log2(n_rounds - o), o rounds outside
 };
 
 template <typename T, int D, int C, int NDW>
-__global__ __launch_bounds__(2 * C)
+__global__ __launch_bounds__(4 * C)
 void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                   const int32_t* __restrict__ perm, const int16_t* __restrict__ cid,
                   T* __restrict__ o_rounds, float* __restrict__ lse, int L, int n_r, int causal,
                   float scale_log2, int nruns)
 {
-    using M = Mfma<T>;
+    using M = Mfma16<T>;
     using S = Lds<T, D, C, NDW>;
-    constexpr int NTH = 2 * C;
+    constexpr int NTH = 4 * C;                         // C/16 waves of 16 queries
     constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
     constexpr int KROW = S::KROW, VROW = S::VROW;
-    constexpr int CT = C / 32, NKT = 2 * CT, DT = D / 32;
+    constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
     constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
     constexpr int GPT = C * VPR / NTH;                 // 16-byte pieces per thread per tensor
     constexpr int RSTEP = NTH / VPR;                   // rows between a thread's pieces
+    static_assert(GPT >= 1 && C * VPR % NTH == 0, "gather tiling");
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 31, hh = lane >> 5;
+    const int r16 = lane & 15, g = lane >> 4;          // MFMA 16x16 lane coordinates
     const int grow = tid / VPR, gpiece = tid % VPR;   // gather: rows grow + i*RSTEP, piece gpiece
 
     int bid = blockIdx.x;
@@ -136,6 +139,8 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     T* ob = o_rounds + (bh * n_r + r) * (long)L * D;
     float* lb = lse + (bh * n_r + r) * (long)L;
     const uint32_t ones = 0x00010001u;
+
+    if (tid < 32) sm.neg_log2[tid] = tid < n_r ? -__log2f((float)(n_r - tid)) : 0.f;
 
     // positions come from the caller's perm: keep every gather inside the row
     auto position = [&](int kk, int row) { return min(max(pr[kk * C + row], 0), L - 1); };
@@ -204,25 +209,26 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
         }
         if (k >= k0) {
             const bool has_prev = k > 0;
-            const int qrow = wave * 32 + n;
+            const int qrow = wave * 16 + r16;
             const int qpos = sm.pos[cur][qrow];
 
             typename M::Frag bq[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                bq[ks] = M::load(&sm.k[cur][qrow * KROW + ks * KSTEP + hh * KPL]);
+                bq[ks] = M::load(&sm.k[cur][qrow * KROW + ks * KSTEP + g * KPL]);
             uint32_t q1[NDW];          // query chunk ids minus one, per half
 #pragma unroll
             for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[cur][qrow * NDW + w], ones);
 
-            // ---- S^T tiles: tiles [0, CT) are the previous chunk, [CT, 2CT) this one
-            f32x16 s[NKT];
+            // ---- S^T tiles of 16 keys: [0, CT) previous chunk, [CT, 2CT) this one.
+            //      Lane (r16, g) holds query r16 against keys 4g + j of each tile.
+            f32x4 s[NKT];
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
-                s[t] = f32x16{};
+                s[t] = f32x4{};
                 if (t < CT && !has_prev) continue;
                 const int slk = t < CT ? prv : cur;
-                const T* kr = &sm.k[slk][((t % CT) * 32 + n) * KROW + hh * KPL];
+                const T* kr = &sm.k[slk][((t % CT) * 16 + r16) * KROW + g * KPL];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) s[t] = M::mma(M::load(kr + ks * KSTEP), bq[ks], s[t]);
             }
@@ -234,103 +240,106 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             for (int t = 0; t < NKT; ++t) {
                 if (t < CT && !has_prev) {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) s[t][j] = -INFINITY;
+                    for (int j = 0; j < 4; ++j) s[t][j] = -INFINITY;
                     continue;
                 }
                 const int slk = t < CT ? prv : cur;
                 const bool diag = t == CT + wave;   // the tile holding the queries themselves
+                const int krow0 = (t % CT) * 16 + 4 * g;
+                const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int krow0 = (t % CT) * 32 + 8 * g + 4 * hh;
-                    const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int j = 4 * g + x;
-                        const int kpos = x == 0 ? kp.x : x == 1 ? kp.y : x == 2 ? kp.z : kp.w;
-                        const uint32_t outs =
-                            rounds_outside<NDW>(q1, &sm.cid[slk][(krow0 + x) * NDW], ones);
-                        const float lg = __log2f((float)max(n_r - (int)outs, 1));
-                        float sc = fmaf(s[t][j], scale_log2, -lg);
-                        if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
-                        if (causal && kpos > qpos) sc = -INFINITY;
-                        s[t][j] = sc;
-                        mx = fmaxf(mx, sc);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
+                    const uint32_t outs =
+                        rounds_outside<NDW>(q1, &sm.cid[slk][(krow0 + j) * NDW], ones);
+                    float sc = fmaf(s[t][j], scale_log2, sm.neg_log2[outs & 31]);
+                    if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
+                    if (causal && kpos > qpos) sc = -INFINITY;
+                    s[t][j] = sc;
+                    mx = fmaxf(mx, sc);
                 }
             }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
 
             float sum = 0.f;
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < 4; ++j) {
                     const float p = __builtin_amdgcn_exp2f(s[t][j] - mx);
                     s[t][j] = p;
                     sum += p;
                 }
             }
+            sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
 
-            // ---- O^T = V^T · P^T
-            f32x16 o[DT];
+            // ---- O^T = V^T · P^T.  Lane (r16, g): row d = 16*dt + r16 of V^T;
+            //      P^T column = query r16, keys 4g + j of the tile(s).
+            f32x4 o[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+            for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
+            if constexpr (KPL == 8) {
+                // one instruction covers two 16-key tiles: slot i < 4 is key 4g+i of
+                // tile t0, slot i >= 4 is key 4g+i-4 of tile t0+1
 #pragma unroll
-            for (int t = 0; t < NKT; ++t) {
-                if (t < CT && !has_prev) continue;
-                const int slk = t < CT ? prv : cur;
-                const int key0 = (t % CT) * 32;
-                if constexpr (KPL == 8) {
+                for (int t0 = 0; t0 < NKT; t0 += 2) {
+                    if (t0 < CT && !has_prev) continue;
+                    const int slk = t0 < CT ? prv : cur;
+                    const int key0 = (t0 % CT) * 16 + 4 * g;
+                    bf16x8 b;
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        bf16x8 b;
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) b[x] = (__bf16)s[t][8 * half + x];
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            const T* vr = &sm.vt[slk][(dt * 32 + n) * VROW + key0 + 16 * half + 4 * hh];
-                            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr);
-                            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 8);
-                            const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                            o[dt] = M::mma(a, b, o[dt]);
-                        }
+                    for (int x = 0; x < 4; ++x) {
+                        b[x] = (__bf16)s[t0][x];
+                        b[4 + x] = (__bf16)s[t0 + 1][x];
                     }
-                } else {
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = key0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const T* vr = &sm.vt[slk][(dt * 16 + r16) * VROW + key0];
+                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr);
+                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 16);
+                        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        o[dt] = M::mma(a, b, o[dt]);
+                    }
+                }
+            } else {
+                // one instruction per key column j: lane group g holds key 4g+j
+#pragma unroll
+                for (int t = 0; t < NKT; ++t) {
+                    if (t < CT && !has_prev) continue;
+                    const int slk = t < CT ? prv : cur;
+                    const int key0 = (t % CT) * 16 + 4 * g;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
 #pragma unroll
                         for (int dt = 0; dt < DT; ++dt) {
-                            const float a = to_f32(sm.vt[slk][(dt * 32 + n) * VROW + key]);
+                            const float a = to_f32(sm.vt[slk][(dt * 16 + r16) * VROW + key0 + j]);
                             o[dt] = M::mma(a, s[t][j], o[dt]);
                         }
                     }
                 }
             }
 
-            // ---- normalise, store the query's row and its lse
+            // ---- normalise, store the query's row and its lse.  Lane (r16, g)
+            //      holds d = 16*dt + 4g + j of query r16.
             const float inv = 1.f / sum;
             T* orow = ob + (long)qpos * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = dt * 32 + 8 * g + 4 * hh;
-                    if constexpr (sizeof(T) == 2) {
-                        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[dt][4 * g + 0] * inv) |
-                                            ((uint32_t)f32_to_bf16_rne(o[dt][4 * g + 1] * inv) << 16);
-                        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[dt][4 * g + 2] * inv) |
-                                            ((uint32_t)f32_to_bf16_rne(o[dt][4 * g + 3] * inv) << 16);
-                        *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
-                    } else {
-                        *reinterpret_cast<float4*>(orow + d0) =
-                            make_float4(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv,
-                                        o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-                    }
+                const int d0 = dt * 16 + 4 * g;
+                if constexpr (sizeof(T) == 2) {
+                    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[dt][0] * inv) |
+                                        ((uint32_t)f32_to_bf16_rne(o[dt][1] * inv) << 16);
+                    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[dt][2] * inv) |
+                                        ((uint32_t)f32_to_bf16_rne(o[dt][3] * inv) << 16);
+                    *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+                } else {
+                    *reinterpret_cast<float4*>(orow + d0) =
+                        make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
                 }
             }
-            if (hh == 0) lb[qpos] = (mx + __log2f(sum)) * LN2;
+            if (g == 0) lb[qpos] = (mx + __log2f(sum)) * LN2;
         }
         __syncthreads();
     }
@@ -344,7 +353,7 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
     const int nchunks = L / C;
     const int nruns = (nchunks + RUN - 1) / RUN;
     const long blocks = bh * nruns * n_r;
-    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW>), dim3((unsigned)blocks), dim3(2 * C), 0, s,
+    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const T*>(qk), static_cast<const T*>(v), perm, cid,
                        static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns);
     return hipGetLastError();

@@ -52,6 +52,35 @@ template <> struct Mfma<float> {
     static __device__ __forceinline__ Frag zero() { return 0.f; }
 };
 
+// 16x16 tiles (wave64): D[16x16] += A[16xK] * B[Kx16], K = 4*KPL per instruction.
+//   lane l: A operand = row (l % 16), k = KPL*(l / 16) + [0, KPL)
+//           B operand = col (l % 16), k = KPL*(l / 16) + [0, KPL)
+//           D element j (0..3) = row 4*(l/16) + j, col (l % 16)
+// bf16: v_mfma_f32_16x16x32_bf16 (KPL = 8); f32: v_mfma_f32_16x16x4_f32 (KPL = 1).
+template <typename T> struct Mfma16;
+
+template <> struct Mfma16<bf16_t> {
+    static constexpr int KPL = 8;
+    static constexpr int KSTEP = 32;
+    typedef bf16x8 Frag;
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ Frag load(const bf16_t* p) {
+        return *reinterpret_cast<const Frag*>(p);
+    }
+};
+
+template <> struct Mfma16<float> {
+    static constexpr int KPL = 1;
+    static constexpr int KSTEP = 4;
+    typedef float Frag;
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ Frag load(const float* p) { return *p; }
+};
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
