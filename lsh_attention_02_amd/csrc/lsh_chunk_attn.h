@@ -31,7 +31,8 @@
 // (NDW words per token, padded with equal values on both sides, which always
 // compare as inside).  For key chunk k and query chunk q of a round, the key is
 // inside the query's window when u = k - (q - 1) (mod 2^16) is 0 or 1; per word
-// that is one packed subtract, shift, min and a dot2 that adds both halves.
+// that is one packed subtract and one saturating packed add (bit 15 = outside);
+// one byte permute per two words gathers the flags and v_bcnt counts them.
 #pragma once
 
 #include "lsh_device.h"
@@ -52,24 +53,24 @@ __device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
     return d;
 }
 
-// Per 16-bit half: 1 if the half is >= 2, else 0.
-__device__ __forceinline__ uint32_t pk_ge2(uint32_t u, uint32_t ones)
+// For each 16-bit half: u = k - q1 (mod 2^16), then sat(u + 0x7FFE).  Bit 15 of
+// the result is set exactly when u >= 2, i.e. when the key lies outside the
+// query's window in that round (u is 0 or 1 inside).
+__device__ __forceinline__ uint32_t pk_outside_flags(uint32_t k, uint32_t q1)
 {
-    uint32_t d;
-    asm("v_pk_lshrrev_b16 %0, %2, %1\n\tv_pk_min_u16 %0, %0, %2" : "=&v"(d) : "v"(u), "v"(ones));
-    return d;
+    uint32_t u, t;
+    asm("v_pk_sub_u16 %0, %2, %3\n\tv_pk_add_u16 %1, %0, %4 clamp"
+        : "=&v"(u), "=v"(t)
+        : "v"(k), "v"(q1), "v"(0x7FFE7FFEu));
+    return t;
 }
 
-__device__ __forceinline__ uint32_t dot2_add(uint32_t a, uint32_t ones, uint32_t acc)
-{
-    typedef unsigned short u2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_udot2(__builtin_bit_cast(u2, a), __builtin_bit_cast(u2, ones), acc, false);
-}
-
-// Rounds (over the NDW words) in which the key is outside the query's window.
+// 8 x (number of rounds in which the key is outside the query's window).
+// v_perm_b32 selectors 8..11 replicate bit 15 / bit 31 of each source word into
+// a byte, so one perm gathers the flags of two words (four rounds) as 0x00/0xFF
+// bytes, which v_bcnt counts.
 template <int NDW>
-__device__ __forceinline__ uint32_t rounds_outside(const uint32_t (&q1)[NDW], const uint32_t* kc,
-                                                   uint32_t ones)
+__device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], const uint32_t* kc)
 {
     uint32_t w[NDW];
     if constexpr (NDW == 1) {
@@ -84,10 +85,17 @@ __device__ __forceinline__ uint32_t rounds_outside(const uint32_t (&q1)[NDW], co
             w[4 * h] = x.x; w[4 * h + 1] = x.y; w[4 * h + 2] = x.z; w[4 * h + 3] = x.w;
         }
     }
-    uint32_t acc = 0;
+    if constexpr (NDW == 1) {
+        return __builtin_popcount(__builtin_amdgcn_perm(0u, pk_outside_flags(w[0], q1[0]), 0x0C0C0908u));
+    } else {
+        uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) acc = dot2_add(pk_ge2(pk_sub_u16(w[i], q1[i]), ones), ones, acc);
-    return acc;
+        for (int i = 0; i < NDW; i += 2)
+            acc += __builtin_popcount(__builtin_amdgcn_perm(pk_outside_flags(w[i + 1], q1[i + 1]),
+                                                            pk_outside_flags(w[i], q1[i]),
+                                                            0x0B0A0908u));
+        return acc;
+    }
 }
 
 template <typename T, int D, int C, int NDW>
@@ -250,9 +258,10 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
-                    const uint32_t outs =
-                        rounds_outside<NDW>(q1, &sm.cid[slk][(krow0 + j) * NDW], ones);
-                    float sc = fmaf(s[t][j], scale_log2, sm.neg_log2[outs & 31]);
+                    const uint32_t outs8 = rounds_outside8<NDW>(q1, &sm.cid[slk][(krow0 + j) * NDW]);
+                    const float nlg = *reinterpret_cast<const float*>(
+                        reinterpret_cast<const char*>(sm.neg_log2) + ((outs8 >> 1) & 124));
+                    float sc = fmaf(s[t][j], scale_log2, nlg);
                     if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
                     s[t][j] = sc;
@@ -329,11 +338,9 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             for (int dt = 0; dt < DT; ++dt) {
                 const int d0 = dt * 16 + 4 * g;
                 if constexpr (sizeof(T) == 2) {
-                    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o[dt][0] * inv) |
-                                        ((uint32_t)f32_to_bf16_rne(o[dt][1] * inv) << 16);
-                    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o[dt][2] * inv) |
-                                        ((uint32_t)f32_to_bf16_rne(o[dt][3] * inv) << 16);
-                    *reinterpret_cast<uint2*>(orow + d0) = make_uint2(w0, w1);
+                    *reinterpret_cast<uint2*>(orow + d0) =
+                        make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                   pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
                 } else {
                     *reinterpret_cast<float4*>(orow + d0) =
                         make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);

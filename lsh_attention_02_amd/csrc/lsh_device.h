@@ -92,6 +92,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> two bfloat16 packed in a word (v_cvt_pk_bf16_f32: round to
+// nearest even; low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 

@@ -10,7 +10,10 @@
 // registers for every round.
 //
 // R streams through LDS in groups of GROUP_COLS columns, transposed to
-// [column][d] so that each MFMA A-operand read is 16 contiguous bytes.  The
+// [column][d] so that each MFMA A-operand read is 16 contiguous bytes; the
+// transpose happens in registers (VE x VE blocks) and the 16-byte pieces are
+// XOR-swizzled within each row so that stores and reads are free of LDS bank
+// conflicts.  The
 // groups of all rounds form one sequence; the next group is loaded from global
 // memory into registers while the current one feeds the MFMAs (two LDS
 // buffers, one barrier per group).
@@ -35,56 +38,88 @@ constexpr int GROUP_TILES = GROUP_COLS / 32;
 
 template <typename T, int D>
 struct HashStage {
-    static constexpr int VE = 16 / (int)sizeof(T);                // elements per 16-byte load
-    static constexpr int ROW = D + VE;                             // LDS row of R^T, +16 bytes
-    static constexpr int CHUNKS = D * GROUP_COLS / VE;             // 16-byte pieces per group
-    static constexpr int PER_THREAD = (CHUNKS + HASH_THREADS - 1) / HASH_THREADS;
-    static constexpr int COL_CHUNKS = GROUP_COLS / VE;             // pieces per d-row of a group
+    static constexpr int VE = 16 / (int)sizeof(T);                // elements per 16-byte piece
+    static constexpr int NP = D / VE;                              // pieces per R^T row
+    static constexpr int ROWB = D * (int)sizeof(T);                // bytes per R^T row (no padding)
+    static constexpr int CB = GROUP_COLS / VE;                     // column blocks per group
+    static constexpr int BLOCKS = NP * CB;                         // VE x VE blocks per group
+    static constexpr int PER_THREAD = (BLOCKS + HASH_THREADS - 1) / HASH_THREADS;
 };
 
-// Global -> registers: piece e of the group covers d = e / COL_CHUNKS,
-// columns c0 + VE * (e % COL_CHUNKS) .. +VE.  Consecutive threads read
-// consecutive pieces of a d-row of R (coalesced).
+// LDS position of 16-byte piece p of R^T row c: p ^ swz(c).  With this XOR
+// swizzle both the transposed block stores (16 lanes: one d-piece, 16 column
+// blocks) and the MFMA operand reads (16 lanes: 16 consecutive rows, one piece)
+// touch 16 distinct 16-byte bank groups.
+template <int NP>
+__device__ __forceinline__ int swz(int c) { return (c ^ (c >> 3)) & (NP - 1); }
+
+// Global -> registers: block b of the group covers d-rows VE*(b / CB) .. +VE and
+// columns c0 + VE*(b % CB) .. +VE (one 16-byte load per d-row; consecutive
+// threads read consecutive column blocks of a row, coalesced).
 template <typename T, int D, int NREG>
-__device__ __forceinline__ void stage_load(uint4 (&reg)[NREG], const T* __restrict__ Rr, int c0,
+__device__ __forceinline__ void stage_load(u32x4 (&reg)[NREG], const T* __restrict__ Rr, int c0,
                                            int ncol, bool vec_ok)
 {
     using S = HashStage<T, D>;
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-        const int e = threadIdx.x + i * HASH_THREADS;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (e < S::CHUNKS) {
-            const int d = e / S::COL_CHUNKS;
-            const int c = c0 + S::VE * (e % S::COL_CHUNKS);
-            const T* src = Rr + (long)d * ncol + c;
-            if (vec_ok && c + S::VE <= ncol) {
-                v = *reinterpret_cast<const uint4*>(src);
-            } else {
-                T* ve = reinterpret_cast<T*>(&v);
+    for (int i = 0; i < S::PER_THREAD; ++i) {
+        const int b = threadIdx.x + i * HASH_THREADS;
 #pragma unroll
-                for (int x = 0; x < S::VE; ++x)
-                    if (c + x < ncol) ve[x] = src[x];
+        for (int y = 0; y < S::VE; ++y) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (b < S::BLOCKS) {
+                const int d = S::VE * (b / S::CB) + y;
+                const int c = c0 + S::VE * (b % S::CB);
+                const T* src = Rr + (long)d * ncol + c;
+                if (vec_ok && c + S::VE <= ncol) {
+                    v = *reinterpret_cast<const u32x4*>(src);
+                } else {
+#pragma unroll
+                    for (int x = 0; x < S::VE; ++x) {
+                        if (c + x < ncol) {
+                            uint32_t e;
+                            if constexpr (sizeof(T) == 2) e = reinterpret_cast<const uint16_t*>(src)[x];
+                            else e = __float_as_uint(reinterpret_cast<const float*>(src)[x]);
+                            if constexpr (sizeof(T) == 2) v[x >> 1] |= e << (16 * (x & 1));
+                            else v[x] = e;
+                        }
+                    }
+                }
             }
+            reg[i * S::VE + y] = v;
         }
-        reg[i] = v;
     }
 }
 
-// Registers -> LDS, transposed: buf[column][d].
+// Registers -> LDS: transpose each VE x VE block in registers; column x of the
+// block becomes one 16-byte piece (VE consecutive d) of R^T row c.
 template <typename T, int D, int NREG>
-__device__ __forceinline__ void stage_store(const uint4 (&reg)[NREG], T* buf)
+__device__ __forceinline__ void stage_store(const u32x4 (&reg)[NREG], char* buf)
 {
     using S = HashStage<T, D>;
 #pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-        const int e = threadIdx.x + i * HASH_THREADS;
-        if (e < S::CHUNKS) {
-            const int d = e / S::COL_CHUNKS;
-            const int cl = S::VE * (e % S::COL_CHUNKS);
-            const T* ve = reinterpret_cast<const T*>(&reg[i]);
+    for (int i = 0; i < S::PER_THREAD; ++i) {
+        const int b = threadIdx.x + i * HASH_THREADS;
+        if (b < S::BLOCKS) {
+            const int p = b / S::CB;
+            const int cbase = S::VE * (b % S::CB);
 #pragma unroll
-            for (int x = 0; x < S::VE; ++x) buf[(cl + x) * S::ROW + d] = ve[x];
+            for (int x = 0; x < S::VE; ++x) {
+                u32x4 out;
+                if constexpr (sizeof(T) == 2) {
+                    // word w of column x = (row 2w, col x) | (row 2w+1, col x) << 16
+                    const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        out[w] = __builtin_amdgcn_perm(reg[i * 8 + 2 * w + 1][x >> 1],
+                                                       reg[i * 8 + 2 * w][x >> 1], sel);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) out[w] = reg[i * 4 + w][x];
+                }
+                const int c = cbase + x;
+                *reinterpret_cast<u32x4*>(buf + c * S::ROWB + 16 * (p ^ swz<S::NP>(c))) = out;
+            }
         }
     }
 }
@@ -97,7 +132,7 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     using M = Mfma<T>;
     using S = HashStage<T, D>;
     constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
-    __shared__ __attribute__((aligned(16))) T rt[2][GROUP_COLS * S::ROW];
+    __shared__ __attribute__((aligned(256))) char rt[2][GROUP_COLS * S::ROWB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
@@ -118,7 +153,7 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     const int ngroups = n_r * groups_per_round;
     const bool vec_ok = (ncol % S::VE) == 0;           // 16-byte aligned R rows
 
-    uint4 reg[S::PER_THREAD];
+    u32x4 reg[S::PER_THREAD * S::VE];
     stage_load<T, D>(reg, R, 0, ncol, vec_ok);
     stage_store<T, D>(reg, rt[0]);
     __syncthreads();
@@ -137,16 +172,22 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
             const int c1 = ((g + 1) % groups_per_round) * GROUP_COLS;
             stage_load<T, D>(reg, R + (long)r1 * D * ncol, c1, ncol, vec_ok);
         }
-        const T* buf = rt[g & 1];
+        const char* buf = rt[g & 1];
         const int tiles = min(GROUP_TILES, (ncol - c0 + 31) >> 5);
         for (int ct = 0; ct < tiles; ++ct) {
             f32x16 acc[HASH_NT];
 #pragma unroll
             for (int u = 0; u < HASH_NT; ++u) acc[u] = f32x16{};
-            const T* arow = buf + (ct * 32 + n) * S::ROW + hh * KPL;
+            // row c of R^T; piece of k-step ks for this half-wave: (ks*KSTEP + hh*KPL) / VE
+            const int c = ct * 32 + n;
+            const char* rowp = buf + c * S::ROWB;
+            const int sw = swz<S::NP>(c);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const typename M::Frag a = M::load(arow + ks * KSTEP);
+                const int e = ks * KSTEP + hh * KPL;                 // first element
+                const int piece = e / S::VE, within = e % S::VE;
+                const typename M::Frag a = *reinterpret_cast<const typename M::Frag*>(
+                    rowp + 16 * (piece ^ sw) + within * (int)sizeof(T));
 #pragma unroll
                 for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a, bq[u][ks], acc[u]);
             }
