@@ -98,12 +98,22 @@ __device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], c
     }
 }
 
+// V^T rows hold a slot's keys in groups of 4 consecutive keys.  Group kg of row
+// d is stored at position kg ^ vt_swz(d).  The PV operand reads (16 rows d of
+// one 16-row tile, one group each) and the transposed stores (rows 8p + x for
+// 16 pieces p, one group each) then touch distinct bank groups.
+template <int C>
+__device__ __forceinline__ int vt_swz(int d)
+{
+    return (d ^ (d >> 3)) & (C / 4 - 1);
+}
+
 template <typename T, int D, int C, int NDW>
 struct Lds {
     static constexpr int KROW = D + 16 / (int)sizeof(T);   // qk row, padded by 16 bytes
-    static constexpr int VROW = C + 4;                      // v^T row (one slot's keys)
+    static constexpr int VROWB = C * (int)sizeof(T);        // v^T row bytes (one slot's keys)
     T k[2][C * KROW];
-    T vt[2][D * VROW];
+    char vt[2][D * VROWB];
     int pos[2][C];
     uint32_t cid[2][C * NDW];
     float neg_log2[32];            // neg_log2[o] = -log2(n_rounds - o), o rounds outside
@@ -120,17 +130,17 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     using S = Lds<T, D, C, NDW>;
     constexpr int NTH = 4 * C;                         // C/16 waves of 16 queries
     constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
-    constexpr int KROW = S::KROW, VROW = S::VROW;
+    constexpr int KROW = S::KROW, VROWB = S::VROWB;
     constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
     constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
-    constexpr int GPT = C * VPR / NTH;                 // 16-byte pieces per thread per tensor
-    constexpr int RSTEP = NTH / VPR;                   // rows between a thread's pieces
-    static_assert(GPT >= 1 && C * VPR % NTH == 0, "gather tiling");
+    constexpr int EB = (int)sizeof(T);
+    // gather jobs: 4 consecutive rows x one 16-byte piece (of qk and of v)
+    constexpr int JOBS = (C / 4) * VPR;
+    constexpr int JPT = (JOBS + NTH - 1) / NTH;        // jobs per thread
     __shared__ __attribute__((aligned(16))) S sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;          // MFMA 16x16 lane coordinates
-    const int grow = tid / VPR, gpiece = tid % VPR;   // gather: rows grow + i*RSTEP, piece gpiece
 
     int bid = blockIdx.x;
     const int r = bid % n_r;
@@ -153,22 +163,32 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     // positions come from the caller's perm: keep every gather inside the row
     auto position = [&](int kk, int row) { return min(max(pr[kk * C + row], 0), L - 1); };
 
-    int gpos[GPT];         // positions of this thread's gather rows, next chunk to load
+    int gpos[JPT][4];      // positions of this thread's gather rows, next chunk to load
     int mypos = 0;         // position of row tid (tid < C), next chunk to load
-    u32x4 kreg[GPT], vreg[GPT];
+    u32x4 kreg[JPT][4], vreg[JPT][4];
     uint32_t creg[NDW];
     int rpos = 0;          // position of row tid for the chunk held in registers
 
     auto fetch_positions = [&](int kk) {
 #pragma unroll
-        for (int i = 0; i < GPT; ++i) gpos[i] = position(kk, grow + i * RSTEP);
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            const int rg = (job < JOBS ? job : 0) / VPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gpos[jb][i] = position(kk, 4 * rg + i);
+        }
         if (tid < C) mypos = position(kk, tid);
     };
     auto fetch_rows = [&]() {
 #pragma unroll
-        for (int i = 0; i < GPT; ++i) {
-            kreg[i] = *reinterpret_cast<const u32x4*>(qb + (long)gpos[i] * D + gpiece * VE);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vb + (long)gpos[i] * D + gpiece * VE);
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            const int piece = (job < JOBS ? job : 0) % VPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kreg[jb][i] = *reinterpret_cast<const u32x4*>(qb + (long)gpos[jb][i] * D + piece * VE);
+                vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + (long)gpos[jb][i] * D + piece * VE);
+            }
         }
         rpos = mypos;
         if (tid < C) {
@@ -183,16 +203,29 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     };
     auto store_rows = [&](int sl) {
 #pragma unroll
-        for (int i = 0; i < GPT; ++i) {
-            const int row = grow + i * RSTEP;
-            *reinterpret_cast<u32x4*>(&sm.k[sl][row * KROW + gpiece * VE]) = kreg[i];
-            const u32x4 wv = vreg[i];
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            if (job < JOBS) {
+                const int rg = job / VPR, piece = job % VPR;
 #pragma unroll
-            for (int x = 0; x < VE; ++x) {
-                T e;
-                if constexpr (sizeof(T) == 2) e = bf16_t{(uint16_t)(wv[x >> 1] >> (16 * (x & 1)))};
-                else e = __uint_as_float(wv[x]);
-                sm.vt[sl][(gpiece * VE + x) * VROW + row] = e;
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4*>(&sm.k[sl][(4 * rg + i) * KROW + piece * VE]) = kreg[jb][i];
+                // transpose the 4 rows x VE elements: element x of every row gives
+                // the 4 keys 4rg..4rg+3 of v^T row d = piece*VE + x
+#pragma unroll
+                for (int x = 0; x < VE; ++x) {
+                    const int d = piece * VE + x;
+                    char* dst = sm.vt[sl] + d * VROWB + 4 * EB * (rg ^ vt_swz<C>(d));
+                    if constexpr (sizeof(T) == 2) {
+                        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+                        const uint32_t w0 = __builtin_amdgcn_perm(vreg[jb][1][x >> 1], vreg[jb][0][x >> 1], sel);
+                        const uint32_t w1 = __builtin_amdgcn_perm(vreg[jb][3][x >> 1], vreg[jb][2][x >> 1], sel);
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+                    } else {
+                        const u32x4 w4 = {vreg[jb][0][x], vreg[jb][1][x], vreg[jb][2][x], vreg[jb][3][x]};
+                        *reinterpret_cast<u32x4*>(dst) = w4;
+                    }
+                }
             }
         }
         if (tid < C) {
@@ -305,9 +338,12 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     }
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const T* vr = &sm.vt[slk][(dt * 16 + r16) * VROW + key0];
-                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr);
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 16);
+                        const int d = dt * 16 + r16;
+                        const char* vr = sm.vt[slk] + d * VROWB;
+                        const int sw = vt_swz<C>(d);
+                        const int kg = key0 >> 2;          // groups kg (tile t0) and kg + 4 (t0 + 1)
+                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr + 8 * (kg ^ sw));
+                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 8 * ((kg + 4) ^ sw));
                         const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                         o[dt] = M::mma(a, b, o[dt]);
                     }
@@ -323,7 +359,9 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     for (int j = 0; j < 4; ++j) {
 #pragma unroll
                         for (int dt = 0; dt < DT; ++dt) {
-                            const float a = to_f32(sm.vt[slk][(dt * 16 + r16) * VROW + key0 + j]);
+                            const int d = dt * 16 + r16;
+                            const float a = *reinterpret_cast<const float*>(
+                                sm.vt[slk] + d * VROWB + 16 * ((key0 >> 2) ^ vt_swz<C>(d)) + 4 * j);
                             o[dt] = M::mma(a, s[t][j], o[dt]);
                         }
                     }
