@@ -182,14 +182,21 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
             const int c = ct * 32 + n;
             const char* rowp = buf + c * S::ROWB;
             const int sw = swz<S::NP>(c);
+            // all of the tile's operand reads first (kept there by the scheduling
+            // barrier), so that their LDS latency is paid once per tile
+            typename M::Frag a[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int e = ks * KSTEP + hh * KPL;                 // first element
                 const int piece = e / S::VE, within = e % S::VE;
-                const typename M::Frag a = *reinterpret_cast<const typename M::Frag*>(
+                a[ks] = *reinterpret_cast<const typename M::Frag*>(
                     rowp + 16 * (piece ^ sw) + within * (int)sizeof(T));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a, bq[u][ks], acc[u]);
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a[ks], bq[u][ks], acc[u]);
             }
             const int cb = c0 + ct * 32 + 4 * hh;
             if (c0 + ct * 32 + 32 <= ncol) {
