@@ -15,6 +15,9 @@ workload.
 Other modes:
     --copy-calibration   run only a plain 1 GiB device copy (for scaling the
                          FETCH_SIZE / WRITE_SIZE counters)
+    --pmc-summary F W CF CW   turn four rocprofv3 --pmc output folders (FETCH_SIZE
+                         and WRITE_SIZE on the benchmark, then on the copy) into
+                         profiles/pmc_traffic.json (no GPU needed)
 """
 from __future__ import annotations
 
@@ -22,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,10 +35,19 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 METRIC = "LSH-attn fwd tokens/s at L=64K, 8 heads, 8 rounds; % MFMA/HBM peak"
-KERNEL_SOURCES = {"lsh_hash": "lsh_hash.hip", "lsh_sort": "lsh_sort.hip",
-                  "lsh_chunk_attn": "lsh_chunk_attn.hip", "lsh_combine_rounds": "lsh_combine.hip"}
+# Sources whose text decides each call's kernels (device helpers included): the
+# committed counter figures are only used while these files are unchanged.
+KERNEL_SOURCES = {
+    "lsh_hash": ["lsh_hash.hip", "lsh_device.h"],
+    "lsh_sort": ["lsh_sort.hip"],
+    "lsh_chunk_attn": ["lsh_chunk_attn.h", "lsh_chunk_attn.hip", "lsh_chunk_attn_bf16_d64.hip",
+                       "lsh_chunk_attn_bf16_d128.hip", "lsh_chunk_attn_f32_d64.hip",
+                       "lsh_chunk_attn_f32_d128.hip", "lsh_device.h"],
+    "lsh_combine_rounds": ["lsh_combine.hip", "lsh_device.h"],
+}
 KERNEL_SYMBOLS = {"lsh_hash": "k_hash", "lsh_sort": "k_sort_*", "lsh_chunk_attn": "k_chunk_attn",
                   "lsh_combine_rounds": "k_combine"}
+PMC_TRAFFIC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
 def algorithmic_work(w):
@@ -84,17 +97,18 @@ def roofline_entry(name, w, ms):
 
 
 def source_sha(name):
-    path = os.path.join(ROOT, "lsh_attention_02_amd", "csrc", KERNEL_SOURCES[name])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "lsh_attention_02_amd", "csrc", fn), "rb") as f:
+            h.update(fn.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def traffic_for(name, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(PMC_TRAFFIC):
         return None
-    with open(path) as f:
+    with open(PMC_TRAFFIC) as f:
         rec = json.load(f)
     ent = rec.get("kernels", {}).get(name)
     if not ent or ent.get("workload") != workload or ent.get("source_sha256") != source_sha(name):
@@ -102,8 +116,9 @@ def traffic_for(name, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x):
-    """The oracle on one (batch row, head) of the workload, scaled to all heads."""
+def cpu_baseline(w, x, min_seconds=10.0):
+    """The oracle on whole (batch row, head) slices of the workload, one after
+    another until about `min_seconds` of CPU work is done, scaled to all heads."""
     import numpy as np
     import oracle.lsh_oracle as O
     try:
@@ -111,31 +126,111 @@ def cpu_baseline(w, x):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = 1
-    qk = x["qk"][:1, :1].astype(np.float64)
-    v = x["v"][:1, :1].astype(np.float64)
     R = x["R"].astype(np.float64)
-    t0 = time.perf_counter()
-    out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(out["o"]).all()
     heads = w.batch * w.heads
-    tokens_per_s = w.batch * w.seq_len / (dt * heads)
+    done, dt = 0, 0.0
+    while done < heads and dt < min_seconds:
+        b, h = divmod(done, w.heads)
+        qk = x["qk"][b:b + 1, h:h + 1].astype(np.float64)
+        v = x["v"][b:b + 1, h:h + 1].astype(np.float64)
+        t0 = time.perf_counter()
+        out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
+        dt += time.perf_counter() - t0
+        assert np.isfinite(out["o"]).all()
+        done += 1
+    tokens_per_s = w.batch * w.seq_len * done / (dt * heads)
     return {"value": round(tokens_per_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch row 0, head 0 of {heads} (all {w.n_rounds} rounds, all "
-                      f"{w.seq_len} positions) in {dt:.1f} s; value = B*L / (time * B*H)"}
+            "sample": f"{done} of {heads} (batch row, head) slices, each with all {w.n_rounds} "
+                      f"rounds over all {w.seq_len} positions, in {dt:.1f} s; "
+                      f"value = B*L*slices / (time * B*H)"}
+
+
+def pmc_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """HBM bytes per launch of each call from rocprofv3 counter CSVs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, each from a run of its own)
+    are scaled by what the same counter reads for the 1 GiB device copy of
+    --copy-calibration (rocclr's copyBuffer kernel), so that the factor turns
+    the counter into bytes the way a copy of known size defines them."""
+    import csv
+    import collections
+
+    def per_kernel(d, counter):
+        sums = collections.defaultdict(list)
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    sums[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return sums
+
+    def copy_factor(d, counter, nbytes):
+        vals = [v for k, vs in per_kernel(d, counter).items() if "copyBuffer" in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no copyBuffer dispatch with {counter} in {d}")
+        return nbytes / (1024.0 * sum(vals) / len(vals))
+
+    gib = float(1 << 30)
+    ff = copy_factor(copy_fetch_dir, "FETCH_SIZE", gib)
+    wf = copy_factor(copy_write_dir, "WRITE_SIZE", gib)
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    from synthetic_inputs import WORKLOADS
+    work = algorithmic_work(WORKLOADS[workload])
+    kernels = {}
+    for name, sym in KERNEL_SYMBOLS.items():
+        prefix = sym.rstrip("*")
+
+        def per_launch(table):
+            # Launch count = dispatches of the call's first kernel; the sort's
+            # three kernels add up to one call.
+            hits = {k: v for k, v in table.items()
+                    if re.search(r"::" + re.escape(prefix) + r"\w*[<(]", k)}
+            if not hits:
+                return None
+            launches = max(len(v) for v in hits.values())
+            return sum(sum(v) for v in hits.values()) / launches
+        f_kib, w_kib = per_launch(fetch), per_launch(write)
+        if f_kib is None or w_kib is None:
+            continue
+        hbm = 1024.0 * (f_kib * ff + w_kib * wf)
+        kernels[name] = {
+            "workload": workload, "source_sha256": source_sha(name),
+            "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+            "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": work[name]["bytes"],
+            "traffic_over_algorithmic": round(hbm / work[name]["bytes"], 3),
+        }
+    rec = {"fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "calibration": "1 GiB device copy (bench.py --copy-calibration), counter read "
+                          "per copyBuffer dispatch",
+           "commands": commands, "kernels": kernels}
+    with open(PMC_TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def copy_calibration():
+    """A plain 1 GiB device-to-device copy: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters, and the practical HBM copy bandwidth."""
     import torch
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     b = torch.empty_like(a)
     a.fill_(1)
-    for _ in range(3):
-        b.copy_(a)
+    b.copy_(a)
     torch.cuda.synchronize()
+    reps = 5
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
     print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
-                      "launches": 3}))
+                      "launches": reps + 1, "ms_per_copy": round(ms, 4),
+                      "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
 def main():
@@ -146,7 +241,19 @@ def main():
     ap.add_argument("--workload", default="paper_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/pmc_traffic.json from rocprofv3 --pmc output folders")
     args = ap.parse_args()
+    if args.pmc_summary:
+        fd, wd, cfd, cwd = args.pmc_summary
+        cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python bench.py "
+               "--steps 2 --warmup 1 --no-cpu-baseline --workload " + args.workload)
+        ccmd = "rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python bench.py --copy-calibration"
+        pmc_summary(args.workload, fd, wd, cfd, cwd,
+                    [cmd.format(c="FETCH_SIZE", d=fd), cmd.format(c="WRITE_SIZE", d=wd),
+                     ccmd.format(c="FETCH_SIZE", d=cfd), ccmd.format(c="WRITE_SIZE", d=cwd)])
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the forward pass shards over batch rows and heads "
