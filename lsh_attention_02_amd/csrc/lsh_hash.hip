@@ -158,14 +158,37 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     stage_store<T, D>(reg, rt[0]);
     __syncthreads();
 
-    float bestv[HASH_NT];
-    int besti[HASH_NT];
+    // Per token tile u, over the round so far: the largest |p| among this lane's
+    // columns, the 32-column tile of the round that holds it (-1: none yet) and
+    // that tile's 16 values of this lane.  A tile replaces the record only when
+    // its maximum is strictly larger, and the first matching entry of the kept
+    // tile is taken at the end of the round, so the lowest column wins exact ties.
+    float bmag[HASH_NT];
+    int btile[HASH_NT];
+    f32x16 keep[HASH_NT];
+
+    // Byte offsets of the tile-0 operand pieces of this lane (row n), per k-step.
+    // Within a group, the swizzle of row 32*ct + n is swz(n) ^ (4*ct mod NP) (the
+    // two parts occupy disjoint bits), which maps k-step ks of tile ct onto the
+    // piece that k-step ks ^ kx(ct) has in tile 0; only a constant offset of
+    // 32*ct rows remains, folded into the LDS instruction.
+    constexpr bool kTable = NKS <= 8;
+    int off0[kTable ? NKS : 1];
+    if constexpr (kTable) {
+        const int sw0 = swz<S::NP>(n);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int e = ks * KSTEP + hh * KPL;
+            off0[ks] = n * S::ROWB + 16 * ((e / S::VE) ^ sw0) + (e % S::VE) * (int)sizeof(T);
+        }
+    }
+
     for (int g = 0; g < ngroups; ++g) {
         const int r = g / groups_per_round;
         const int c0 = (g % groups_per_round) * GROUP_COLS;
         if (c0 == 0) {
 #pragma unroll
-            for (int u = 0; u < HASH_NT; ++u) { bestv[u] = 0.f; besti[u] = INT_MAX; }
+            for (int u = 0; u < HASH_NT; ++u) { bmag[u] = 0.f; btile[u] = -1; keep[u] = f32x16{}; }
         }
         if (g + 1 < ngroups) {
             const int r1 = (g + 1) / groups_per_round;
@@ -173,64 +196,69 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
             stage_load<T, D>(reg, R + (long)r1 * D * ncol, c1, ncol, vec_ok);
         }
         const char* buf = rt[g & 1];
+        // R^T rows past ncol hold zeros (stage_load), so their projections are
+        // exactly 0 and can never beat a record: no column test is needed.
         const int tiles = min(GROUP_TILES, (ncol - c0 + 31) >> 5);
-        for (int ct = 0; ct < tiles; ++ct) {
-            f32x16 acc[HASH_NT];
 #pragma unroll
-            for (int u = 0; u < HASH_NT; ++u) acc[u] = f32x16{};
-            // row c of R^T; piece of k-step ks for this half-wave: (ks*KSTEP + hh*KPL) / VE
-            const int c = ct * 32 + n;
-            const char* rowp = buf + c * S::ROWB;
-            const int sw = swz<S::NP>(c);
-            // all of the tile's operand reads first (kept there by the scheduling
-            // barrier), so that their LDS latency is paid once per tile
-            typename M::Frag a[NKS];
+        for (int ct = 0; ct < GROUP_TILES; ++ct) {
+            if (ct < tiles) {
+                f32x16 acc[HASH_NT];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int e = ks * KSTEP + hh * KPL;                 // first element
-                const int piece = e / S::VE, within = e % S::VE;
-                a[ks] = *reinterpret_cast<const typename M::Frag*>(
-                    rowp + 16 * (piece ^ sw) + within * (int)sizeof(T));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < HASH_NT; ++u) acc[u] = f32x16{};
+                // all of the tile's operand reads first (kept there by the
+                // scheduling barrier), so that their LDS latency is paid once
+                typename M::Frag a[NKS];
+                if constexpr (kTable) {
+                    const int kx = ((4 * ct) & (S::NP - 1)) * S::VE / KSTEP;   // constant once unrolled
+                    const char* tb = buf + ct * 32 * S::ROWB;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+                    for (int ks = 0; ks < NKS; ++ks)
+                        a[ks] = *reinterpret_cast<const typename M::Frag*>(tb + off0[ks ^ kx]);
+                } else {
+                    const int c = ct * 32 + n;
+                    const char* rowp = buf + c * S::ROWB;
+                    const int sw = swz<S::NP>(c);
 #pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a[ks], bq[u][ks], acc[u]);
-            }
-            const int cb = c0 + ct * 32 + 4 * hh;
-            if (c0 + ct * 32 + 32 <= ncol) {
-#pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float v = acc[u][j];
-                        if (fabsf(v) > fabsf(bestv[u])) {
-                            bestv[u] = v;
-                            besti[u] = cb + 8 * (j >> 2) + (j & 3);
-                        }
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int e = ks * KSTEP + hh * KPL;
+                        a[ks] = *reinterpret_cast<const typename M::Frag*>(
+                            rowp + 16 * ((e / S::VE) ^ sw) + (e % S::VE) * (int)sizeof(T));
                     }
                 }
-            } else {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                    for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a[ks], bq[u][ks], acc[u]);
+                }
+                const int tile = (c0 >> 5) + ct;
 #pragma unroll
                 for (int u = 0; u < HASH_NT; ++u) {
+                    float m = fabsf(acc[u][0]);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int col = cb + 8 * (j >> 2) + (j & 3);
-                        const float v = acc[u][j];
-                        if (col < ncol && fabsf(v) > fabsf(bestv[u])) {
-                            bestv[u] = v;
-                            besti[u] = col;
-                        }
-                    }
+                    for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(acc[u][j]));
+                    const bool up = m > bmag[u];
+                    bmag[u] = up ? m : bmag[u];
+                    btile[u] = up ? tile : btile[u];
+                    keep[u] = up ? acc[u] : keep[u];
                 }
             }
         }
         if (c0 + GROUP_COLS >= ncol) {               // last group of round r
 #pragma unroll
             for (int u = 0; u < HASH_NT; ++u) {
-                float bv = bestv[u];
-                int bi = besti[u];
+                // first kept entry with the record magnitude (one always matches:
+                // the record is one of the kept values' magnitudes)
+                int jj = 0;
+                float bv = 0.f;
+#pragma unroll
+                for (int j = 15; j >= 0; --j) {
+                    const bool hit = fabsf(keep[u][j]) == bmag[u];
+                    jj = hit ? j : jj;
+                    bv = hit ? keep[u][j] : bv;
+                }
+                int bi = btile[u] < 0 ? INT_MAX : 32 * btile[u] + 4 * hh + 8 * (jj >> 2) + (jj & 3);
+                if (btile[u] < 0) bv = 0.f;
                 const float ov = __shfl_xor(bv, 32);
                 const int oi = __shfl_xor(bi, 32);
                 if (fabsf(ov) > fabsf(bv) || (fabsf(ov) == fabsf(bv) && oi < bi)) { bv = ov; bi = oi; }
