@@ -160,13 +160,17 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 
     if (tid < 32) sm.neg_log2[tid] = tid < n_r ? -__log2f((float)(n_r - tid)) : 0.f;
 
-    // positions come from the caller's perm: keep every gather inside the row
-    auto position = [&](int kk, int row) { return min(max(pr[kk * C + row], 0), L - 1); };
+    // Loaded values are kept raw until the iteration that uses them (positions
+    // are clamped, chunk ids masked and packed there): processing a value right
+    // after its load would make the wave wait for every earlier load as well,
+    // including the gathers meant to overlap the current chunk's math.
+    // Positions come from the caller's perm: every gather stays inside the row.
+    auto clamp_pos = [&](int p) { return min(max(p, 0), L - 1); };
 
-    int gpos[JPT][4];      // positions of this thread's gather rows, next chunk to load
-    int mypos = 0;         // position of row tid (tid < C), next chunk to load
+    int gpos[JPT][4];      // raw perm entries of this thread's gather rows, next chunk to load
+    int mypos = 0;         // raw perm entry of row tid (tid < C), next chunk to load
     u32x4 kreg[JPT][4], vreg[JPT][4];
-    uint32_t creg[NDW];
+    uint32_t craw[2 * NDW];   // chunk ids of row tid per round (raw), chunk held in registers
     int rpos = 0;          // position of row tid for the chunk held in registers
 
     auto fetch_positions = [&](int kk) {
@@ -175,9 +179,9 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             const int job = tid + jb * NTH;
             const int rg = (job < JOBS ? job : 0) / VPR;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gpos[jb][i] = position(kk, 4 * rg + i);
+            for (int i = 0; i < 4; ++i) gpos[jb][i] = pr[kk * C + 4 * rg + i];
         }
-        if (tid < C) mypos = position(kk, tid);
+        mypos = pr[kk * C + tid % C];          // rows past C repeat (loads without branches)
     };
     auto fetch_rows = [&]() {
 #pragma unroll
@@ -186,20 +190,15 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             const int piece = (job < JOBS ? job : 0) % VPR;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                kreg[jb][i] = *reinterpret_cast<const u32x4*>(qb + (long)gpos[jb][i] * D + piece * VE);
-                vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + (long)gpos[jb][i] * D + piece * VE);
+                const long row = (long)clamp_pos(gpos[jb][i]) * D + piece * VE;
+                kreg[jb][i] = *reinterpret_cast<const u32x4*>(qb + row);
+                vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + row);
             }
         }
-        rpos = mypos;
-        if (tid < C) {
-            const int16_t* cr = cb + (long)mypos * n_r;
+        rpos = clamp_pos(mypos);
+        const int16_t* cr = cb + (long)rpos * n_r;
 #pragma unroll
-            for (int w = 0; w < NDW; ++w) {
-                const uint32_t lo = (2 * w < n_r) ? (uint16_t)cr[2 * w] : 0u;
-                const uint32_t hi = (2 * w + 1 < n_r) ? (uint16_t)cr[2 * w + 1] : 0u;
-                creg[w] = lo | (hi << 16);
-            }
-        }
+        for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
     };
     auto store_rows = [&](int sl) {
 #pragma unroll
@@ -230,8 +229,13 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
         }
         if (tid < C) {
             sm.pos[sl][tid] = rpos;
+            // rounds past n_r hold 0 for keys and queries alike (always inside)
 #pragma unroll
-            for (int w = 0; w < NDW; ++w) sm.cid[sl][tid * NDW + w] = creg[w];
+            for (int w = 0; w < NDW; ++w) {
+                const uint32_t lo = 2 * w < n_r ? craw[2 * w] : 0u;
+                const uint32_t hi = 2 * w + 1 < n_r ? craw[2 * w + 1] : 0u;
+                sm.cid[sl][tid * NDW + w] = lo | (hi << 16);
+            }
         }
     };
 
@@ -239,6 +243,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     fetch_positions(kfirst);
     fetch_rows();
     if (kfirst + 1 < k1) fetch_positions(kfirst + 1);
+
 
     for (int k = kfirst; k < k1; ++k) {
         const int cur = k & 1, prv = cur ^ 1;
