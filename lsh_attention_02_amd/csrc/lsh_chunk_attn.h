@@ -25,7 +25,7 @@
 //   O^T[d, q] = V^T[d, key] · P^T[key, q]
 // with V^T read from LDS in the same key order.  Rows of o_rounds and lse go
 // back to original position order.  Scores are kept in base 2 (exp2/log2);
-// -log2 N comes from a small LDS table indexed by the rounds outside.
+// -log2 N comes from a small LDS table addressed by 8 x (rounds outside).
 //
 // Duplicate counts: chunk ids of all rounds are packed two per 32-bit word
 // (NDW words per token, padded with equal values on both sides, which always
@@ -112,11 +112,13 @@ template <typename T, int D, int C, int NDW>
 struct Lds {
     static constexpr int KROW = D + 16 / (int)sizeof(T);   // qk row, padded by 16 bytes
     static constexpr int VROWB = C * (int)sizeof(T);        // v^T row bytes (one slot's keys)
+    // -log2(n_rounds - o) at byte offset 8*o, o = rounds outside (at most 16):
+    // the popcount sum 8*o addresses it directly (first member: offset 0)
+    float neg_log2[36];
     T k[2][C * KROW];
     char vt[2][D * VROWB];
     int pos[2][C];
     uint32_t cid[2][C * NDW];
-    float neg_log2[32];            // neg_log2[o] = -log2(n_rounds - o), o rounds outside
 };
 
 template <typename T, int D, int C, int NDW>
@@ -158,7 +160,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     float* lb = lse + (bh * n_r + r) * (long)L;
     const uint32_t ones = 0x00010001u;
 
-    if (tid < 32) sm.neg_log2[tid] = tid < n_r ? -__log2f((float)(n_r - tid)) : 0.f;
+    if (tid < 33) sm.neg_log2[tid] = (tid % 2 == 0 && tid / 2 < n_r) ? -__log2f((float)(n_r - tid / 2)) : 0.f;
 
     // Loaded values are kept raw until the iteration that uses them (positions
     // are clamped, chunk ids masked and packed there): processing a value right
@@ -298,7 +300,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
                     const uint32_t outs8 = rounds_outside8<NDW>(q1, &sm.cid[slk][(krow0 + j) * NDW]);
                     const float nlg = *reinterpret_cast<const float*>(
-                        reinterpret_cast<const char*>(sm.neg_log2) + ((outs8 >> 1) & 124));
+                        reinterpret_cast<const char*>(sm.neg_log2) + outs8);
                     float sc = fmaf(s[t][j], scale_log2, nlg);
                     if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
