@@ -98,14 +98,34 @@ void k_sort_scan(int32_t* __restrict__ counters, int nb, int ntiles)
     }
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by launch index, and each
+// XCD has its own L2.  The scatter's perm and cid stores are small and
+// interleaved: a perm line takes slots from every tile of its segment and a cid
+// line takes the rounds of 8 positions from every round's segment.  The launch
+// index is therefore remapped so that all workgroups sharing a key (a (batch
+// row, head) when there are at least 8 of them, else a segment) run on one XCD,
+// where the partial lines combine in L2 before they are written back.
+constexpr int NXCD = 8;
+
+struct ScatterMap {
+    long nkeys;        // keys: (batch row, head) pairs or segments
+    int per_key;       // workgroups per key
+    int rounds_per_key;   // n_r when a key is a (batch row, head), else 1
+};
+
 __global__ __launch_bounds__(SORT_THREADS)
 void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restrict__ counters,
                     int32_t* __restrict__ perm, int16_t* __restrict__ cid, int L, int nb,
-                    int nbits, int tile, int ntiles, int n_r, int chunk)
+                    int nbits, int tile, int ntiles, int n_r, int chunk, ScatterMap map)
 {
     extern __shared__ int next_slot[];
-    const long seg = blockIdx.x / ntiles;
-    const int t = blockIdx.x % ntiles;
+    const int xcd = blockIdx.x % NXCD;
+    const long j = blockIdx.x / NXCD;
+    const long key = (j / map.per_key) * NXCD + xcd;
+    if (key >= map.nkeys) return;                  // padding of the last row of keys
+    const int within = (int)(j % map.per_key);
+    const long seg = key * map.rounds_per_key + within / ntiles;
+    const int t = within % ntiles;
     const long bh = seg / n_r;
     const int r = (int)(seg % n_r);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -189,8 +209,14 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
                        n_buckets, plan.tile, plan.ntiles);
     hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)plan.nseg), dim3(SCAN_THREADS), 0, s, counters,
                        n_buckets, plan.ntiles);
-    hipLaunchKernelGGL(k_sort_scatter, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters,
-                       perm, cid, L, n_buckets, nbits, plan.tile, plan.ntiles, n_rounds, chunk);
+    ScatterMap map;
+    if (bh >= NXCD) { map.nkeys = bh; map.rounds_per_key = n_rounds; }
+    else { map.nkeys = plan.nseg; map.rounds_per_key = 1; }
+    map.per_key = map.rounds_per_key * plan.ntiles;
+    const long rows = (map.nkeys + NXCD - 1) / NXCD;
+    const unsigned sblocks = (unsigned)(rows * NXCD * map.per_key);
+    hipLaunchKernelGGL(k_sort_scatter, dim3(sblocks), dim3(SORT_THREADS), lds, s, buckets, counters,
+                       perm, cid, L, n_buckets, nbits, plan.tile, plan.ntiles, n_rounds, chunk, map);
     return hipGetLastError();
 }
 
