@@ -383,12 +383,12 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             for (int dt = 0; dt < DT; ++dt) {
                 const int d0 = dt * 16 + 4 * g;
                 if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<uint2*>(orow + d0) =
-                        make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
-                                   pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
+                    const u32x2 w = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                     pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + d0) = w;
                 } else {
-                    *reinterpret_cast<float4*>(orow + d0) =
-                        make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+                    const f32x4 w = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + d0) = w;
                 }
             }
             if (g == 0) lb[qpos] = (mx + __log2f(sum)) * LN2;

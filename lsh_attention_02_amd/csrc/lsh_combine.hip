@@ -3,6 +3,8 @@
 //   LSE_i = logsumexp_r lse[r, i],   o_i = sum_r exp(lse[r, i] - LSE_i) o_rounds[r, i].
 // Streaming and bandwidth-bound: each thread owns 16 bytes of one output row
 // and reads the same 16 bytes of that row in every round (coalesced rows).
+// Every byte is read or written once, so the loads and stores are
+// non-temporal (they do not displace cached data).
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
@@ -44,19 +46,19 @@ void k_combine(const T* __restrict__ o_rounds, const float* __restrict__ lse, T*
         if (r < n_r) {
             const float w = __expf(l[r] - m);
             wsum += w;
-            const uint4 raw = *reinterpret_cast<const uint4*>(
-                o_rounds + ((bh * n_r + r) * (long)L + i) * D + part * VE);
+            const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                o_rounds + ((bh * n_r + r) * (long)L + i) * D + part * VE));
             const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
             for (int x = 0; x < VE; ++x) acc[x] += w * to_f32(e[x]);
         }
     }
     const float inv = 1.f / wsum;
-    uint4 out;
+    u32x4 out;
     T* oe = reinterpret_cast<T*>(&out);
 #pragma unroll
     for (int x = 0; x < VE; ++x) oe[x] = from_f32<T>(acc[x] * inv);
-    *reinterpret_cast<uint4*>(o + row * D + part * VE) = out;
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(o + row * D + part * VE));
 }
 
 template <typename T, int D>
