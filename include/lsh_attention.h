@@ -41,7 +41,8 @@
  *                        larger than 2^62 bytes.
  *   LSH_ERR_UNSUPPORTED  d_head not 64 or 128; dtype not LSH_F32/LSH_BF16;
  *                        n_buckets > 32768; n_rounds > 16; chunk not 32, 64 or
- *                        128 (attention only); flags != 0.
+ *                        128 (attention only); a flag bit other than the
+ *                        LSH_FLAG_* values below.
  *   LSH_ERR_WORKSPACE    workspace smaller than lsh_sort_workspace_bytes().
  *   LSH_ERR_HIP          a kernel launch failed (hipGetLastError).
  *   Faults inside a kernel surface asynchronously at the caller's next
@@ -68,6 +69,22 @@ typedef enum lsh_status {
 
 enum { LSH_F32 = 0, LSH_BF16 = 1 };
 
+/*
+ * Variant flags (lsh_config.flags, OR-ed).  They change step 3 only; the
+ * other steps accept and ignore them.  0 is the method as described above.
+ *   LSH_FLAG_NO_DUP_CORRECTION  drop the -log N_ij term: every round is plain
+ *        softmax over its window, and the combine no longer equals attention
+ *        over the union of the rounds' windows.
+ *   LSH_FLAG_WRAP_LOOKBACK      chunk 0 of a round also attends to the last
+ *        chunk of that round (look-back around the end of the sorted order);
+ *        with a single chunk it attends to itself once.  N_ij counts the rounds
+ *        with (cid[i,r'] - cid[j,r']) mod (L / c) in {0, 1}.
+ * The pages leave both points open (they describe look-back to the previous
+ * chunk, and the duplicate-count term is the reading under which the rounds'
+ * outputs merge to attention over their union).
+ */
+enum { LSH_FLAG_NO_DUP_CORRECTION = 1, LSH_FLAG_WRAP_LOOKBACK = 2 };
+
 typedef struct lsh_config {
     int32_t batch;      /* B >= 1 */
     int32_t heads;      /* H >= 1 */
@@ -79,7 +96,7 @@ typedef struct lsh_config {
     int32_t causal;     /* 1: a query never attends to a later position */
     float scale;        /* score = scale * <qk_i, qk_j>; usually 1/sqrt(d_head) */
     int32_t dtype;      /* LSH_F32 or LSH_BF16 */
-    int32_t flags;      /* reserved, must be 0 */
+    int32_t flags;      /* LSH_FLAG_* bits, 0 for the method as described */
 } lsh_config;
 
 /*
@@ -115,11 +132,12 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
  * Step 3 — chunked attention, one output per round.  [AIS] formula and LSH
  * section; [ULT]; [MOD] "LSH attention".
  *   In round r, the query at sorted slot s (chunk k = s / c) attends to the keys
- *   in chunks k-1 and k of that round's sorted order (chunk 0: only itself).  For
- *   query i and key j:
+ *   in chunks k-1 and k of that round's sorted order (chunk 0: only itself,
+ *   unless LSH_FLAG_WRAP_LOOKBACK).  For query i and key j:
  *       s_ij = scale * <qk_i, qk_j> - log N_ij - 1e5 * [j == i]
  *   where N_ij = number of rounds r' with cid[i,r'] - cid[j,r'] in {0, 1} (the
- *   rounds whose window for i holds j); keys j > i are dropped when causal.
+ *   rounds whose window for i holds j; the term is absent with
+ *   LSH_FLAG_NO_DUP_CORRECTION); keys j > i are dropped when causal.
  *       lse_i = logsumexp_j s_ij,   o_i = sum_j exp(s_ij - lse_i) v_j.
  *   qk, v     [B, H, L, d]          dtype
  *   perm      [B, H, n_r, L]        int32, from lsh_sort

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "liblsh_attention.so")
 
 LSH_OK, LSH_ERR_INVALID_ARG, LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_ERR_HIP = range(5)
 LSH_F32, LSH_BF16 = 0, 1
+# variant flags of lsh_config.flags (see include/lsh_attention.h)
+LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK = 1, 2
 
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
             "lsh_combine_rounds", "lsh_status_string", "lsh_last_error")
@@ -55,7 +57,7 @@ class LSHConfig:
     causal: bool
     dtype: str = "bf16"            # "bf16" or "f32"
     scale: Optional[float] = None  # None: 1/sqrt(d_head)
-    flags: int = 0
+    flags: int = 0                 # LSH_FLAG_* bits; 0 is the method as described
 
     @property
     def torch_dtype(self) -> torch.dtype:

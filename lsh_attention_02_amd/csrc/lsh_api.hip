@@ -66,7 +66,8 @@ lsh_status check_config(const lsh_config* c)
         return fail(LSH_ERR_UNSUPPORTED, "dtype must be LSH_F32 or LSH_BF16");
     if (c->n_buckets > 32768) return fail(LSH_ERR_UNSUPPORTED, "n_buckets must be at most 32768");
     if (c->n_rounds > 16) return fail(LSH_ERR_UNSUPPORTED, "n_rounds must be at most 16");
-    if (c->flags != 0) return fail(LSH_ERR_UNSUPPORTED, "flags must be 0");
+    if (c->flags & ~(LSH_FLAG_NO_DUP_CORRECTION | LSH_FLAG_WRAP_LOOKBACK))
+        return fail(LSH_ERR_UNSUPPORTED, "unknown flag bit");
     const long long elem = c->dtype == LSH_BF16 ? 2 : 4;
     // the largest buffer is o_rounds [B, H, n_r, L, d]
     if (checked_product({c->batch, c->heads, c->n_rounds, c->seq_len, c->d_head, elem}) < 0)
@@ -160,7 +161,7 @@ lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v, 
     LSH_TRY(check_ptr(lse, "lse"));
     return hip_status(lshk::launch_chunk_attn(cfg->dtype, cfg->d_head, cfg->chunk, qk, v, perm, cid,
                                               o_rounds, lse, bh_of(cfg), cfg->seq_len,
-                                              cfg->n_rounds, cfg->causal, cfg->scale,
+                                              cfg->n_rounds, cfg->causal, cfg->scale, cfg->flags,
                                               static_cast<hipStream_t>(stream)),
                       "lsh_chunk_attn");
 }

@@ -65,12 +65,37 @@ __device__ __forceinline__ uint32_t pk_outside_flags(uint32_t k, uint32_t q1)
     return t;
 }
 
+// Look-back around the end of the round: the key is also inside when
+// u == nchunks (query in chunk 0, key in the last chunk; no other pair of
+// chunk ids gives that difference).  With e = u ^ nchunks per half,
+// sat(e + 0x7FFF) has bit 15 set unless e == 0, so AND-ing it into the flags
+// clears "outside" for that case.  nch2 holds nchunks in both halves.
+__device__ __forceinline__ uint32_t pk_outside_flags_wrap(uint32_t k, uint32_t q1, uint32_t nch2)
+{
+    uint32_t u, t, e, f;
+    asm("v_pk_sub_u16 %0, %4, %5\n\t"
+        "v_pk_add_u16 %1, %0, %6 clamp\n\t"
+        "v_xor_b32 %2, %0, %7\n\t"
+        "v_pk_add_u16 %3, %2, %8 clamp"
+        : "=&v"(u), "=&v"(t), "=&v"(e), "=v"(f)
+        : "v"(k), "v"(q1), "v"(0x7FFE7FFEu), "v"(nch2), "v"(0x7FFF7FFFu));
+    return t & f;
+}
+
+template <bool WRAP>
+__device__ __forceinline__ uint32_t outside_flags(uint32_t k, uint32_t q1, uint32_t nch2)
+{
+    if constexpr (WRAP) return pk_outside_flags_wrap(k, q1, nch2);
+    else return pk_outside_flags(k, q1);
+}
+
 // 8 x (number of rounds in which the key is outside the query's window).
 // v_perm_b32 selectors 8..11 replicate bit 15 / bit 31 of each source word into
 // a byte, so one perm gathers the flags of two words (four rounds) as 0x00/0xFF
 // bytes, which v_bcnt counts.
-template <int NDW>
-__device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], const uint32_t* kc)
+template <int NDW, bool WRAP>
+__device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], const uint32_t* kc,
+                                                    uint32_t nch2)
 {
     uint32_t w[NDW];
     if constexpr (NDW == 1) {
@@ -86,14 +111,15 @@ __device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], c
         }
     }
     if constexpr (NDW == 1) {
-        return __builtin_popcount(__builtin_amdgcn_perm(0u, pk_outside_flags(w[0], q1[0]), 0x0C0C0908u));
+        return __builtin_popcount(
+            __builtin_amdgcn_perm(0u, outside_flags<WRAP>(w[0], q1[0], nch2), 0x0C0C0908u));
     } else {
         uint32_t acc = 0;
 #pragma unroll
         for (int i = 0; i < NDW; i += 2)
-            acc += __builtin_popcount(__builtin_amdgcn_perm(pk_outside_flags(w[i + 1], q1[i + 1]),
-                                                            pk_outside_flags(w[i], q1[i]),
-                                                            0x0B0A0908u));
+            acc += __builtin_popcount(
+                __builtin_amdgcn_perm(outside_flags<WRAP>(w[i + 1], q1[i + 1], nch2),
+                                      outside_flags<WRAP>(w[i], q1[i], nch2), 0x0B0A0908u));
         return acc;
     }
 }
@@ -118,10 +144,12 @@ struct Lds {
     T k[2][C * KROW];
     char vt[2][D * VROWB];
     int pos[2][C];
-    uint32_t cid[2][C * NDW];
+    uint32_t cid[2][C * (NDW > 0 ? NDW : 1)];
 };
 
-template <typename T, int D, int C, int NDW>
+// NDW = 0: no duplicate-count term (LSH_FLAG_NO_DUP_CORRECTION).  WRAP: chunk 0
+// looks back to the last chunk of its round (LSH_FLAG_WRAP_LOOKBACK).
+template <typename T, int D, int C, int NDW, bool WRAP>
 __global__ __launch_bounds__(4 * C)
 void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                   const int32_t* __restrict__ perm, const int16_t* __restrict__ cid,
@@ -159,6 +187,8 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     T* ob = o_rounds + (bh * n_r + r) * (long)L * D;
     float* lb = lse + (bh * n_r + r) * (long)L;
     const uint32_t ones = 0x00010001u;
+    const uint32_t nch2 = (uint32_t)nchunks * 0x00010001u;
+    constexpr int NW = NDW > 0 ? NDW : 1;              // array extent when NDW = 0
 
     if (tid < 33) sm.neg_log2[tid] = (tid % 2 == 0 && tid / 2 < n_r) ? -__log2f((float)(n_r - tid / 2)) : 0.f;
 
@@ -172,7 +202,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     int gpos[JPT][4];      // raw perm entries of this thread's gather rows, next chunk to load
     int mypos = 0;         // raw perm entry of row tid (tid < C), next chunk to load
     u32x4 kreg[JPT][4], vreg[JPT][4];
-    uint32_t craw[2 * NDW];   // chunk ids of row tid per round (raw), chunk held in registers
+    uint32_t craw[2 * NW];    // chunk ids of row tid per round (raw), chunk held in registers
     int rpos = 0;          // position of row tid for the chunk held in registers
 
     auto fetch_positions = [&](int kk) {
@@ -198,9 +228,11 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             }
         }
         rpos = clamp_pos(mypos);
-        const int16_t* cr = cb + (long)rpos * n_r;
+        if constexpr (NDW > 0) {
+            const int16_t* cr = cb + (long)rpos * n_r;
 #pragma unroll
-        for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
+            for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
+        }
     };
     auto store_rows = [&](int sl) {
 #pragma unroll
@@ -233,7 +265,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             sm.pos[sl][tid] = rpos;
             // rounds past n_r hold 0 for keys and queries alike (always inside)
 #pragma unroll
-            for (int w = 0; w < NDW; ++w) {
+            for (int w = 0; w < NDW; ++w) {   // nothing when NDW = 0
                 const uint32_t lo = 2 * w < n_r ? craw[2 * w] : 0u;
                 const uint32_t hi = 2 * w + 1 < n_r ? craw[2 * w + 1] : 0u;
                 sm.cid[sl][tid * NDW + w] = lo | (hi << 16);
@@ -241,22 +273,32 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
         }
     };
 
-    const int kfirst = max(k0 - 1, 0);
-    fetch_positions(kfirst);
+    // Iteration it handles chunk chunk_of(it).  When chunk k0 has a look-back
+    // chunk (k0 - 1, or the last chunk when wrapping around), iteration 0 only
+    // loads it; the chunks k0 .. k1-1 follow.
+    const bool lookback = k0 > 0 || (WRAP && nchunks > 1);
+    const int it0 = lookback ? 1 : 0;
+    const int nit = (k1 - k0) + it0;
+    auto chunk_of = [&](int it) {
+        const int c = k0 - it0 + it;
+        return c < 0 ? c + nchunks : c;
+    };
+
+    fetch_positions(chunk_of(0));
     fetch_rows();
-    if (kfirst + 1 < k1) fetch_positions(kfirst + 1);
+    if (1 < nit) fetch_positions(chunk_of(1));
 
 
-    for (int k = kfirst; k < k1; ++k) {
-        const int cur = k & 1, prv = cur ^ 1;
-        store_rows(cur);               // slot of chunk k-2, released by the last barrier
+    for (int it = 0; it < nit; ++it) {
+        const int cur = it & 1, prv = cur ^ 1;
+        store_rows(cur);               // slot of iteration it-2, released by the last barrier
         __syncthreads();
-        if (k + 1 < k1) {
-            fetch_rows();              // chunk k+1 (positions fetched an iteration ago)
-            if (k + 2 < k1) fetch_positions(k + 2);
+        if (it + 1 < nit) {
+            fetch_rows();              // iteration it+1 (positions fetched an iteration ago)
+            if (it + 2 < nit) fetch_positions(chunk_of(it + 2));
         }
-        if (k >= k0) {
-            const bool has_prev = k > 0;
+        if (it >= it0) {
+            const bool has_prev = it > 0;
             const int qrow = wave * 16 + r16;
             const int qpos = sm.pos[cur][qrow];
 
@@ -264,7 +306,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 bq[ks] = M::load(&sm.k[cur][qrow * KROW + ks * KSTEP + g * KPL]);
-            uint32_t q1[NDW];          // query chunk ids minus one, per half
+            uint32_t q1[NW];           // query chunk ids minus one, per half
 #pragma unroll
             for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[cur][qrow * NDW + w], ones);
 
@@ -298,9 +340,13 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
-                    const uint32_t outs8 = rounds_outside8<NDW>(q1, &sm.cid[slk][(krow0 + j) * NDW]);
-                    const float nlg = *reinterpret_cast<const float*>(
-                        reinterpret_cast<const char*>(sm.neg_log2) + outs8);
+                    float nlg = 0.f;
+                    if constexpr (NDW > 0) {
+                        const uint32_t outs8 = rounds_outside8<NDW, WRAP>(
+                            q1, &sm.cid[slk][(krow0 + j) * NDW], nch2);
+                        nlg = *reinterpret_cast<const float*>(
+                            reinterpret_cast<const char*>(sm.neg_log2) + outs8);
+                    }
                     float sc = fmaf(s[t][j], scale_log2, nlg);
                     if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
@@ -397,7 +443,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     }
 }
 
-template <typename T, int D, int C, int NDW>
+template <typename T, int D, int C, int NDW, bool WRAP>
 hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
                       void* o_rounds, float* lse, long bh, int L, int n_r, int causal, float scale,
                       hipStream_t s)
@@ -405,22 +451,36 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
     const int nchunks = L / C;
     const int nruns = (nchunks + RUN - 1) / RUN;
     const long blocks = bh * nruns * n_r;
-    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
+    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW, WRAP>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const T*>(qk), static_cast<const T*>(v), perm, cid,
                        static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns);
     return hipGetLastError();
 }
 
-// Dispatch on the number of packed chunk-id words (1, 2, 4 or 8 for up to 16 rounds).
-template <typename T, int D, int C>
+// Dispatch on the number of packed chunk-id words (1, 2, 4 or 8 for up to 16
+// rounds; 0 without the duplicate-count term).
+template <typename T, int D, int C, bool WRAP>
 hipError_t launch_ndw(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
                       void* o, float* lse, long bh, int L, int n_r, int causal, float scale,
-                      hipStream_t s)
+                      bool dup, hipStream_t s)
 {
-    if (n_r <= 2) return launch_one<T, D, C, 1>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    if (n_r <= 4) return launch_one<T, D, C, 2>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    if (n_r <= 8) return launch_one<T, D, C, 4>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    return launch_one<T, D, C, 8>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (!dup) return launch_one<T, D, C, 0, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (n_r <= 2) return launch_one<T, D, C, 1, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (n_r <= 4) return launch_one<T, D, C, 2, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    if (n_r <= 8) return launch_one<T, D, C, 4, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+    return launch_one<T, D, C, 8, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+}
+
+// Dispatch on the variant flags (LSH_FLAG_NO_DUP_CORRECTION = 1, LSH_FLAG_WRAP_LOOKBACK = 2).
+template <typename T, int D, int C>
+hipError_t launch_flags(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
+                        void* o, float* lse, long bh, int L, int n_r, int causal, float scale,
+                        int flags, hipStream_t s)
+{
+    const bool dup = !(flags & 1);
+    if (flags & 2)
+        return launch_ndw<T, D, C, true>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
+    return launch_ndw<T, D, C, false>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
 }
 
 }  // namespace attn

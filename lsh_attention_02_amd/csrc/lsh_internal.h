@@ -28,7 +28,7 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
 
 hipError_t launch_chunk_attn(int dtype, int d_head, int chunk, const void* qk, const void* v,
                              const int32_t* perm, const int16_t* cid, void* o_rounds, float* lse,
-                             long bh, int L, int n_rounds, int causal, float scale,
+                             long bh, int L, int n_rounds, int causal, float scale, int flags,
                              hipStream_t stream);
 
 namespace attn {
@@ -36,7 +36,7 @@ namespace attn {
 #define LSH_ATTN_LAUNCH_ARGS                                                                    \
     int chunk, const void *qk, const void *v, const int32_t *perm, const int16_t *cid,          \
         void *o_rounds, float *lse, long bh, int L, int n_rounds, int causal, float scale,       \
-        hipStream_t stream
+        int flags, hipStream_t stream
 hipError_t launch_bf16_d64(LSH_ATTN_LAUNCH_ARGS);
 hipError_t launch_bf16_d128(LSH_ATTN_LAUNCH_ARGS);
 hipError_t launch_f32_d64(LSH_ATTN_LAUNCH_ARGS);

@@ -34,13 +34,15 @@ notes):
   * inside a window there is no same-bucket mask: the attended set of a round
     is the chunk window;
   * chunk 0 has no previous chunk (no wrap-around) and look-back stays inside
-    a round; chunk must divide L;
+    a round; chunk must divide L.  The variant wrap=True gives chunk 0 the last
+    chunk of its round as look-back (a window is a set of chunks, so a single
+    chunk is attended once);
   * the self score carries a penalty of SELF_PENALTY score units in every
     round, so "self only if nothing else" is decided over all rounds together;
   * the score of key j for query i in a round is lowered by log N_ij, where
     N_ij is the number of rounds whose window for i contains j (duplicate-count
     correction); with it, the combined output equals attention over the union
-    of the rounds' windows;
+    of the rounds' windows.  The variant dup_correct=False leaves it out;
   * R has shape [n_rounds, d, n_buckets/2] and is shared by every batch row and
     head, as in [ULT]'s example;
   * ties in the argmax go to the first index, as in [ULT]'s example.
@@ -156,29 +158,47 @@ def sort_rounds(buckets: np.ndarray, n_buckets: int, chunk: int):
 
 
 # --------------------------------------------------------------------------- 3. attend
-def window_slots(k: int, chunk: int) -> np.ndarray:
-    """Sorted slots attended by chunk k: the previous chunk (if k >= 1) and chunk k.
+def window_chunks(k: int, nchunks: int, wrap: bool = False):
+    """Chunks attended by chunk k, in slot order: the previous chunk, then k.
 
     [AIS], [ULT]: the sorted sequence is cut into equal chunks and each chunk
-    attends to itself and to the chunk before it.  Chunk 0 has no predecessor.
+    attends to itself and to the chunk before it.  Chunk 0 has no predecessor,
+    unless wrap, where it is the last chunk of the round.  A window is a set:
+    a chunk never appears twice (one chunk in all, with wrap).
     """
-    return np.arange(max(k - 1, 0) * chunk, (k + 1) * chunk)
+    if k >= 1:
+        return [k - 1, k]
+    if wrap and nchunks > 1:
+        return [nchunks - 1, 0]
+    return [0]
 
 
-def duplicate_counts(cid_q: np.ndarray, cid_k: np.ndarray) -> np.ndarray:
+def window_slots(k: int, chunk: int, nchunks: int = 0, wrap: bool = False) -> np.ndarray:
+    """Sorted slots of the chunks that chunk k attends to (see window_chunks)."""
+    return np.concatenate([np.arange(c * chunk, (c + 1) * chunk)
+                           for c in window_chunks(k, nchunks, wrap)])
+
+
+def duplicate_counts(cid_q: np.ndarray, cid_k: np.ndarray, nchunks: int = 0,
+                     wrap: bool = False) -> np.ndarray:
     """N[i, j] = number of rounds whose window for query i contains key j.
 
     cid_q [nq, n_r], cid_k [nk, n_r] are chunk ids per round.  Key j lies in the
     window of query i in round r exactly when its chunk is the query's chunk or
-    the one before it: cid_q[i, r] - cid_k[j, r] is 0 or 1.
+    the one before it: cid_q[i, r] - cid_k[j, r] is 0 or 1; with wrap, the
+    chunk before chunk 0 is the last one, so the difference is taken modulo
+    the number of chunks.
     """
     diff = cid_q[:, None, :].astype(np.int64) - cid_k[None, :, :].astype(np.int64)
+    if wrap:
+        diff = np.mod(diff, nchunks)
     return ((diff == 0) | (diff == 1)).sum(axis=2)
 
 
 def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
                     cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
-                    query_slots: Optional[np.ndarray] = None, dup_correct: bool = True):
+                    query_slots: Optional[np.ndarray] = None, dup_correct: bool = True,
+                    wrap: bool = False):
     """One round's attention for the queries of sorted chunk k.
 
     qk_bh, v_bh [L, d] (one batch row and head), perm_r [L] (this round's sorted
@@ -188,17 +208,21 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
     positions; the query itself is removed because shared QK makes it the most
     similar key).  Returns (positions of the queries, o [nq, d], lse [nq]) with
     lse = logsumexp_j s_ij and o = sum_j softmax(s)_ij v_j ([AIS] formula).
-    query_slots restricts the queries to some sorted slots of chunk k.
+    query_slots restricts the queries to some sorted slots of chunk k.  The
+    variants dup_correct=False (no log N_ij term) and wrap=True (chunk 0 looks
+    back to the last chunk) change the window and its scores as described in
+    window_chunks and duplicate_counts.
     """
+    nchunks = len(perm_r) // chunk
     q_slots = np.arange(k * chunk, (k + 1) * chunk) if query_slots is None else np.asarray(query_slots)
-    k_slots = window_slots(k, chunk)
+    k_slots = window_slots(k, chunk, nchunks, wrap)
     qi = perm_r[q_slots].astype(np.int64)
     kj = perm_r[k_slots].astype(np.int64)
     q = np.asarray(qk_bh[qi], dtype=np.float64)
     kk = np.asarray(qk_bh[kj], dtype=np.float64)
     s = scale * (q @ kk.T)
     if dup_correct:
-        s = s - np.log(duplicate_counts(cid_bh[qi], cid_bh[kj]))
+        s = s - np.log(duplicate_counts(cid_bh[qi], cid_bh[kj], nchunks, wrap))
     s = s - SELF_PENALTY * (qi[:, None] == kj[None, :])
     if causal:
         s = np.where(kj[None, :] > qi[:, None], -np.inf, s)
@@ -211,7 +235,8 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
 
 
 def attention_rounds(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.ndarray,
-                     chunk: int, causal: bool, scale: float, dup_correct: bool = True):
+                     chunk: int, causal: bool, scale: float, dup_correct: bool = True,
+                     wrap: bool = False):
     """Every round's output in original position order.
 
     -> o_r float64 [B, H, n_r, L, d], lse float64 [B, H, n_r, L].
@@ -227,20 +252,21 @@ def attention_rounds(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.nd
             for r in range(n_r):
                 for k in range(L // chunk):
                     qi, o, l = chunk_attention(qk[b, h], v[b, h], perm[b, h, r], cid[b, h],
-                                               k, chunk, causal, scale, dup_correct=dup_correct)
+                                               k, chunk, causal, scale, dup_correct=dup_correct,
+                                               wrap=wrap)
                     o_r[b, h, r, qi] = o
                     lse[b, h, r, qi] = l
     return o_r, lse
 
 
 def attention_one(qk_bh, v_bh, perm_bh, cid_bh, r: int, pos: int, chunk: int,
-                  causal: bool, scale: float, dup_correct: bool = True):
+                  causal: bool, scale: float, dup_correct: bool = True, wrap: bool = False):
     """Round r's (o, lse) for the single query at position ``pos`` (sampled checks)."""
     slot = int(cid_bh[pos, r]) * chunk
     seg = perm_bh[r]
     slot += int(np.nonzero(seg[slot:slot + chunk] == pos)[0][0])
     _, o, l = chunk_attention(qk_bh, v_bh, seg, cid_bh, slot // chunk, chunk, causal, scale,
-                              query_slots=np.array([slot]), dup_correct=dup_correct)
+                              query_slots=np.array([slot]), dup_correct=dup_correct, wrap=wrap)
     return o[0], float(l[0])
 
 
@@ -266,13 +292,15 @@ def default_scale(d_head: int) -> float:
 
 
 def forward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, n_buckets: int, chunk: int,
-            causal: bool, scale: Optional[float] = None, dup_correct: bool = True):
+            causal: bool, scale: Optional[float] = None, dup_correct: bool = True,
+            wrap: bool = False):
     """All four steps.  Returns a dict with every intermediate (float64 / int)."""
     if scale is None:
         scale = default_scale(qk.shape[-1])
     buckets, margins = hash_buckets(qk, R)
     perm, cid = sort_rounds(buckets, n_buckets, chunk)
-    o_r, lse = attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct)
+    o_r, lse = attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct,
+                                wrap=wrap)
     o, LSE = combine_rounds(o_r, lse)
     return {"buckets": buckets, "margins": margins, "perm": perm, "cid": cid,
             "o_rounds": o_r, "lse": lse, "o": o, "LSE": LSE}

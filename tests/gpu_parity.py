@@ -41,9 +41,15 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
-def cfg_of(w: Workload, scale=None) -> lsh.LSHConfig:
+def cfg_of(w: Workload, scale=None, flags=0) -> lsh.LSHConfig:
     return lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
-                         w.causal, dtype=w.dtype, scale=scale)
+                         w.causal, dtype=w.dtype, scale=scale, flags=flags)
+
+
+def variant(flags: int) -> dict:
+    """The oracle's switches for the library's LSH_FLAG_* bits."""
+    return {"dup_correct": not (flags & lsh.LSH_FLAG_NO_DUP_CORRECTION),
+            "wrap": bool(flags & lsh.LSH_FLAG_WRAP_LOOKBACK)}
 
 
 def upload(w: Workload, x: Dict[str, np.ndarray], device="cuda:0"):
@@ -52,8 +58,8 @@ def upload(w: Workload, x: Dict[str, np.ndarray], device="cuda:0"):
     return {k: torch.from_numpy(x[k]).to(device).to(dt).contiguous() for k in ("qk", "v", "R")}
 
 
-def run_gpu(w: Workload, x, scale=None, device="cuda:0"):
-    cfg = cfg_of(w, scale)
+def run_gpu(w: Workload, x, scale=None, device="cuda:0", flags=0):
+    cfg = cfg_of(w, scale, flags)
     t = upload(w, x, device)
     out = lsh.forward(cfg, t["qk"], t["v"], t["R"], return_all=True)
     torch.cuda.synchronize()
@@ -88,17 +94,18 @@ def check_hash(gpu_b: np.ndarray, ref_b: np.ndarray, margins: np.ndarray, what: 
     return {"near_ties": int(near.sum()), "near_tie_mismatches": int(mism.sum()), "hashes": int(mism.size)}
 
 
-def full_parity(w: Workload, scale=None, x=None) -> dict:
+def full_parity(w: Workload, scale=None, x=None, flags=0) -> dict:
     """Every output of every step against the oracle (small workloads)."""
     t0 = time.time()
     x = make_inputs(w) if x is None else x
-    cfg, _, g = run_gpu(w, x, scale)
+    cfg, _, g = run_gpu(w, x, scale, flags=flags)
+    var = variant(flags)
     sc = cfg.score_scale
     qk = x["qk"].astype(np.float64)
     v = x["v"].astype(np.float64)
     R = x["R"].astype(np.float64)
     gb = to_np(g["buckets"])
-    rep = {"workload": w.name}
+    rep = {"workload": w.name, "flags": flags}
     # hash
     ob, om = O.hash_buckets(qk, R)
     rep.update(check_hash(gb, ob, om, w.name))
@@ -107,7 +114,7 @@ def full_parity(w: Workload, scale=None, x=None) -> dict:
     assert np.array_equal(to_np(g["perm"]), sp), f"{w.name}: perm differs from the stable sort"
     assert np.array_equal(to_np(g["cid"]), sc_id), f"{w.name}: cid differs"
     # attention fed the GPU's perm/cid
-    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc)
+    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc, **var)
     rep["o_rounds_err"] = rel_err(to_np(g["o_rounds"]), o_r)
     assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
     rep["lse_abs_err"] = check_lse(to_np(g["lse"]), lse, w.dtype, w.name)
@@ -120,7 +127,7 @@ def full_parity(w: Workload, scale=None, x=None) -> dict:
     rep["heads_bucket_exact"] = f"{int(same.sum())}/{same.size}"
     if same.any():
         pf, cf = O.sort_rounds(ob, w.n_buckets, w.chunk)
-        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc)
+        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc, **var)
         of, _ = O.combine_rounds(of_r, lf)
         go = to_np(g["o"])
         rep["forward_err"] = rel_err(go[same], of[same])
@@ -148,17 +155,18 @@ def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, 
     assert np.array_equal(gc.astype(np.int64), want), f"{what}: cid differs from slot // chunk"
 
 
-def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0) -> dict:
+def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int = 0) -> dict:
     """Full-size workload: every sort output, sampled hashes, rows and tokens."""
     t0 = time.time()
-    log(f"[sampled] {w.name}: generating inputs")
+    log(f"[sampled] {w.name} flags {flags}: generating inputs")
     x = make_inputs(w)
     log(f"[sampled] {w.name}: running the GPU path ({time.time() - t0:.1f}s)")
-    cfg, t, g = run_gpu(w, x)
+    cfg, t, g = run_gpu(w, x, flags=flags)
+    var = variant(flags)
     sc = cfg.score_scale
     B, H, L, d, n_r = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
     rng = np.random.default_rng(seed)
-    rep = {"workload": w.name}
+    rep = {"workload": w.name, "flags": flags}
     gb = to_np(g["buckets"])
     gp = to_np(g["perm"])
     gc = to_np(g["cid"])
@@ -183,7 +191,7 @@ def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0) -> dict:
     for s in range(n_samples):
         b, h = sb[s], sh[s]
         ref_o[s], ref_l[s] = O.attention_one(x["qk"][b, h], x["v"][b, h], gp[b, h], gc[b, h],
-                                             int(sr[s]), int(si[s]), w.chunk, w.causal, sc)
+                                             int(sr[s]), int(si[s]), w.chunk, w.causal, sc, **var)
     rep["o_rounds_err"] = rel_err(g_or, ref_o)
     assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
     rep["lse_abs_err"] = check_lse(g_lse, ref_l, w.dtype, w.name)

@@ -26,6 +26,12 @@ What pins what:
            on the query itself when it has company);
          - causal: position 0 returns its own value exactly;
          - combine: one round is the identity; equal lse gives the mean.
+  variants - wrap-around look-back: union brute force with circular chunk
+           distance; two chunks give full attention (without wrap they would
+           not);
+         - no duplicate correction: each round equals plain softmax over its
+           brute-force window (o and lse); with one round the correction is
+           a no-op.
 """
 from __future__ import annotations
 
@@ -190,12 +196,46 @@ def check_full_attention(L=40, d=8, nb=6, n_r=3, causal=False, scale=None, seed=
     assert err < TOL_COMBINED, err
 
 
-def check_union(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13, dup_correct=True):
+def check_union(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13, dup_correct=True,
+                wrap=False):
     w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
-    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=dup_correct)
-    ref = RF.union_attention(qk[0, 0], v[0, 0], out["buckets"][0, 0], chunk, causal, 1.0 / math.sqrt(d))
+    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=dup_correct, wrap=wrap)
+    ref = RF.union_attention(qk[0, 0], v[0, 0], out["buckets"][0, 0], chunk, causal,
+                             1.0 / math.sqrt(d), wrap=wrap)
     err = np.max(np.abs(out["o"][0, 0] - ref))
     assert err < TOL_COMBINED, err
+
+
+def check_wrap_two_chunks(L=40, d=8, nb=6, n_r=3, causal=False, seed=18):
+    """With wrap-around and two chunks, both chunks see the whole sequence in
+    every round, so the forward is textbook full attention with the self-mask;
+    without wrap the first chunk would see only itself."""
+    w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=L // 2, causal=causal, seed=seed)
+    out = _forward(w, qk[0, 0], v[0, 0], R, wrap=True)
+    ref = RF.full_attention_self_masked(qk[0, 0], v[0, 0], causal, 1.0 / math.sqrt(d))
+    err = np.max(np.abs(out["o"][0, 0] - ref))
+    assert err < TOL_COMBINED, err
+
+
+def check_rounds_without_correction(L=48, d=8, nb=6, n_r=3, chunk=8, causal=True, seed=19,
+                                    wrap=False):
+    """Without the duplicate-count term every round is plain softmax attention
+    over that round's window (o_rounds and lse, round by round)."""
+    w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
+    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=False, wrap=wrap)
+    W = RF.brute_windows(out["buckets"][0, 0], chunk, causal, wrap)
+    for r in range(n_r):
+        o, lse = RF.round_attention(qk[0, 0], v[0, 0], W[r], 1.0 / math.sqrt(d))
+        assert np.max(np.abs(out["o_rounds"][0, 0, r] - o)) < 1e-12
+        assert np.max(np.abs(out["lse"][0, 0, r] - lse) / np.maximum(1.0, np.abs(lse))) < 1e-13
+
+
+def check_single_round_correction_free(seed=20):
+    """With one round every duplicate count is 1, so the correction changes nothing."""
+    w, qk, v, R = small_case(L=48, d=8, nb=6, n_r=1, chunk=8, causal=True, seed=seed)
+    a = _forward(w, qk[0, 0], v[0, 0], R)
+    b = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=False)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
 
 
 def union_has_duplicates(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13) -> bool:
@@ -276,4 +316,13 @@ ALL_CHECKS = {
     "onehot_values": check_onehot_values,
     "causal_first": check_causal_first_position,
     "combine": check_combine,
+    "union_wrap": lambda: check_union(wrap=True, nb=4, chunk=8, L=40, seed=21),
+    "union_wrap_causal": lambda: check_union(wrap=True, causal=True, n_r=4, nb=4, chunk=4, L=32,
+                                             seed=22),
+    "wrap_two_chunks": check_wrap_two_chunks,
+    "wrap_two_chunks_causal": lambda: check_wrap_two_chunks(causal=True, seed=23),
+    "rounds_without_correction": check_rounds_without_correction,
+    "rounds_without_correction_wrap": lambda: check_rounds_without_correction(wrap=True,
+                                                                              causal=False, seed=24),
+    "single_round_correction_free": check_single_round_correction_free,
 }

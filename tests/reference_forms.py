@@ -16,7 +16,12 @@ function with it.  Each is slow (Python loops) and meant for small inputs.
   brute force (Python's sorted() on (bucket, position), then slot // chunk),
   and each query attends, with plain softmax weights, to the union of the keys
   its windows hold across rounds (minus itself unless nothing else is there).
-  The duplicate-count corrected multi-round output must equal this.
+  The duplicate-count corrected multi-round output must equal this.  With
+  wrap, the chunk before the first is the last one.
+
+* round_attention: one round without the duplicate-count term, plain softmax
+  over the round's window; the variant without the correction must give it
+  round by round.
 """
 from __future__ import annotations
 
@@ -50,23 +55,53 @@ def brute_chunk_of(buckets_r, chunk: int) -> list:
     return chunk_of
 
 
-def brute_windows(buckets: np.ndarray, chunk: int, causal: bool):
-    """W[r][i] = set of keys in query i's window in round r (after the causal cut)."""
+def brute_windows(buckets: np.ndarray, chunk: int, causal: bool, wrap: bool = False):
+    """W[r][i] = set of keys in query i's window in round r (after the causal cut).
+
+    Key j is in the window when its chunk is the query's chunk or the one just
+    before it; with wrap, the chunk before the first is the last, i.e. the
+    chunk distance is counted around a circle of L / chunk chunks.
+    """
     n_r, L = buckets.shape
+    nchunks = L // chunk
     W = []
     for r in range(n_r):
         c = brute_chunk_of(buckets[r], chunk)
-        W.append([{j for j in range(L) if c[i] - c[j] in (0, 1) and (not causal or j <= i)}
+        W.append([{j for j in range(L)
+                   if ((c[i] - c[j]) % nchunks if wrap else c[i] - c[j]) in (0, 1)
+                   and (not causal or j <= i)}
                   for i in range(L)])
     return W
 
 
+def round_attention(qk: np.ndarray, v: np.ndarray, window: list, scale: float):
+    """One round without the duplicate-count term: query i attends with plain
+    softmax weights to the keys of its window other than itself (to itself only
+    when the window holds nothing else).  window[i] is a set of positions.
+    Returns (o [L, d], lse [L]) with lse the log of the softmax denominator."""
+    qk = np.asarray(qk, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    L = qk.shape[0]
+    out = np.empty_like(v)
+    lse = np.empty(L)
+    for i in range(L):
+        keys = sorted(window[i] - {i}) or [i]
+        s = scale * (qk[keys] @ qk[i])
+        if keys == [i]:
+            s = s - 1.0e5            # the self penalty of the method, alone in the window
+        m = s.max()
+        w = np.exp(s - m)
+        lse[i] = m + np.log(w.sum())
+        out[i] = (w / w.sum()) @ v[keys]
+    return out, lse
+
+
 def union_attention(qk: np.ndarray, v: np.ndarray, buckets: np.ndarray, chunk: int,
-                    causal: bool, scale: float) -> np.ndarray:
+                    causal: bool, scale: float, wrap: bool = False) -> np.ndarray:
     """buckets [n_r, L] of one (batch row, head)."""
     qk = np.asarray(qk, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    W = brute_windows(buckets, chunk, causal)
+    W = brute_windows(buckets, chunk, causal, wrap)
     L = qk.shape[0]
     out = np.empty_like(v)
     for i in range(L):

@@ -55,6 +55,13 @@ def test_exports_match_header(lib):
         assert hasattr(lib, name), name
 
 
+def test_flag_values_match_header():
+    text = open(os.path.join(ROOT, "include", "lsh_attention.h")).read()
+    vals = dict(re.findall(r"(LSH_FLAG_\w+)\s*=\s*(\d+)", text))
+    assert vals == {"LSH_FLAG_NO_DUP_CORRECTION": str(B.LSH_FLAG_NO_DUP_CORRECTION),
+                    "LSH_FLAG_WRAP_LOOKBACK": str(B.LSH_FLAG_WRAP_LOOKBACK)}
+
+
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(B.CConfig) == 11 * 4
     assert [f[0] for f in B.CConfig._fields_] == ["batch", "heads", "seq_len", "d_head", "n_buckets",
@@ -82,7 +89,8 @@ BAD_CONFIGS = [
     (dict(d_head=96), B.LSH_ERR_UNSUPPORTED, "d_head"),
     (dict(n_buckets=65536), B.LSH_ERR_UNSUPPORTED, "32768"),
     (dict(n_rounds=17), B.LSH_ERR_UNSUPPORTED, "16"),
-    (dict(flags=1), B.LSH_ERR_UNSUPPORTED, "flags"),
+    (dict(flags=4), B.LSH_ERR_UNSUPPORTED, "flag"),
+    (dict(flags=-1), B.LSH_ERR_UNSUPPORTED, "flag"),
     # o_rounds = 2^20 * 2^10 * 16 * 2^20 * 128 float32 = 2^63 bytes
     (dict(batch=1 << 20, heads=1 << 10, seq_len=1 << 20, chunk=1024, n_rounds=16, d_head=128,
           dtype="f32"), B.LSH_ERR_INVALID_ARG, "2^62"),

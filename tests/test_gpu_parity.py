@@ -22,8 +22,8 @@ def W(name, **kw) -> Workload:
 
 
 # Small workloads the oracle finishes in seconds; several tiles of every kernel
-# and ragged tails (L not a multiple of the hash tile of 256 tokens, chunk
-# counts not a multiple of the attention run of 8 chunks, partial column tiles).
+# and ragged tails (L not a multiple of the hash workgroup's 512 tokens, chunk
+# counts not a multiple of the attention run of 16 chunks, partial column tiles).
 SMALL = {
     "tiny_f32": WORKLOADS["tiny_f32"],
     "short_4k": WORKLOADS["short_4k"],
@@ -50,6 +50,46 @@ def test_full_parity(name):
     w = SMALL[name]
     scale = 1.0 if name == "f32_d128_r2_scale1" else None
     GP.full_parity(w, scale=scale)
+
+
+# Variant flags: LSH_FLAG_NO_DUP_CORRECTION (1), LSH_FLAG_WRAP_LOOKBACK (2) and
+# both, on cases with several 16-chunk attention runs (the wrapped look-back of
+# chunk 0 and of every later run), one chunk, 16 rounds, f32 and d128.
+FLAG_CASES = {
+    "short_4k": WORKLOADS["short_4k"],
+    "ragged_b2h3_L1344_nb10_r3": SMALL["ragged_b2h3_L1344_nb10_r3"],
+    "d128_L2048_r4": SMALL["d128_L2048_r4"],
+    "chunk32_noncausal_r5": SMALL["chunk32_noncausal_r5"],
+    "f32_chunk128_d64": SMALL["f32_chunk128_d64"],
+    "rounds16_buckets1000": SMALL["rounds16_buckets1000"],
+    "one_chunk": SMALL["one_chunk"],
+    "two_chunks_nb2": SMALL["two_chunks_nb2"],
+}
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("name", sorted(FLAG_CASES))
+def test_variant_parity(name, flags):
+    GP.full_parity(FLAG_CASES[name], flags=flags)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wrap_two_chunks_is_full_attention(causal):
+    """With the wrapped look-back and two chunks, both chunks see the whole
+    sequence in every round: textbook attention with the self-mask."""
+    w = W("wrap2", seq_len=256, n_buckets=16, n_rounds=3, chunk=128, causal=causal,
+          seed=121 + causal)
+    x = make_inputs(w)
+    _, _, g = GP.run_gpu(w, x, flags=lsh.LSH_FLAG_WRAP_LOOKBACK)
+    ref = RF.full_attention_self_masked(x["qk"][0, 0], x["v"][0, 0], causal, 1 / np.sqrt(64))
+    err = GP.rel_err(GP.to_np(g["o"])[0, 0], ref)
+    assert err <= GP.GATE["bf16"], err
+
+
+def test_full_size_sampled_variants():
+    """paper_64k with both variant flags, in the benchmark's launch configuration."""
+    GP.sampled_parity(WORKLOADS["paper_64k"], n_samples=512,
+                      flags=lsh.LSH_FLAG_NO_DUP_CORRECTION | lsh.LSH_FLAG_WRAP_LOOKBACK)
 
 
 def test_native_library_is_loaded():

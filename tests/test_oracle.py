@@ -84,11 +84,11 @@ def _unstable_sort(keys, n_keys):
     return np.lexsort((-np.arange(keys.size), keys))
 
 
-def _own_chunk_only(k, chunk):
+def _own_chunk_only(k, chunk, *_):
     return np.arange(k * chunk, (k + 1) * chunk)
 
 
-def _two_back(k, chunk):
+def _two_back(k, chunk, *_):
     own = np.arange(k * chunk, (k + 1) * chunk)
     return own if k < 2 else np.concatenate([np.arange((k - 2) * chunk, (k - 1) * chunk), own])
 
@@ -117,21 +117,36 @@ def _values_are_keys(a, k):
     return a, k
 
 
+def _correction_always_on(a, k):
+    k["dup_correct"] = True
+    return a, k
+
+
+_WINDOW_CHUNKS_ORIG = O.window_chunks
+
+
 MUTATIONS = {
     "hash drops the negated half": ("bucket_from_projection", _argmax_positive_half_only, "hash_antipodal"),
     "hash takes argmin": ("bucket_from_projection", _argmin_labels, "hash_labels"),
     "sort not stable": ("stable_counting_sort", _unstable_sort, "sort_library"),
     "no look-back chunk": ("window_slots", _own_chunk_only, "union"),
     "look-back two chunks": ("window_slots", _two_back, "union"),
-    "duplicate counts dropped": ("duplicate_counts", lambda q, k: np.ones((len(q), len(k))), "union"),
+    "duplicate counts dropped": ("duplicate_counts", lambda q, k, *_: np.ones((len(q), len(k))), "union"),
     "log of duplicate count dropped": ("duplicate_counts",
-                                       lambda q, k: np.exp(_DUP_ORIG(q, k)),
+                                       lambda q, k, *a: np.exp(_DUP_ORIG(q, k, *a)),
                                        "union"),
     "no self penalty": ("SELF_PENALTY", 0.0, "full_attention"),
     "causal flag ignored": ("chunk_attention", "ignore_causal", "full_attention_causal"),
     "keys used as values": ("chunk_attention", "values_are_keys", "full_attention"),
     "scale dropped": ("default_scale", lambda d: 1.0, "full_attention"),
     "rounds averaged": ("combine_rounds", _mean_combine, "union"),
+    "wrap-around ignored": ("window_chunks", lambda k, n, wrap=False: _WINDOW_CHUNKS_ORIG(k, n, False),
+                            "wrap_two_chunks"),
+    "wrap-around missing from the counts": ("duplicate_counts",
+                                            lambda q, k, n=0, wrap=False: _DUP_ORIG(q, k, n, False),
+                                            "union_wrap"),
+    "correction applied when switched off": ("chunk_attention", "correction_always_on",
+                                             "rounds_without_correction"),
 }
 
 
@@ -143,6 +158,8 @@ def test_mutation_is_caught(name, monkeypatch):
         repl = _wrap(orig, _ignore_causal)
     elif repl == "values_are_keys":
         repl = _wrap(orig, _values_are_keys)
+    elif repl == "correction_always_on":
+        repl = _wrap(orig, _correction_always_on)
     monkeypatch.setattr(O, attr, repl)
     with pytest.raises((AssertionError, IndexError, ValueError)):
         P.ALL_CHECKS[check]()
