@@ -116,7 +116,7 @@ def traffic_for(name, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, min_seconds=10.0):
+def cpu_baseline(w, x, min_seconds=10.0, flags=0):
     """The oracle on whole (batch row, head) slices of the workload, one after
     another until about `min_seconds` of CPU work is done, scaled to all heads."""
     import numpy as np
@@ -134,7 +134,8 @@ def cpu_baseline(w, x, min_seconds=10.0):
         qk = x["qk"][b:b + 1, h:h + 1].astype(np.float64)
         v = x["v"][b:b + 1, h:h + 1].astype(np.float64)
         t0 = time.perf_counter()
-        out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal)
+        out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal, dup_correct=not (flags & 1),
+                        wrap=bool(flags & 2))
         dt += time.perf_counter() - t0
         assert np.isfinite(out["o"]).all()
         done += 1
@@ -239,6 +240,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="paper_64k")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4,
@@ -274,7 +277,7 @@ def main():
     dev = torch.device("cuda:0")
     x = make_inputs(w)
     cfg = lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
-                        w.causal, dtype=w.dtype)
+                        w.causal, dtype=w.dtype, flags=args.flags)
     tdt = cfg.torch_dtype
     qk = torch.from_numpy(x["qk"]).to(dev).to(tdt)
     v = torch.from_numpy(x["v"]).to(dev).to(tdt)
@@ -329,7 +332,8 @@ def main():
     dominant = max(per_call, key=per_call.get)
     roof = roofline_entry(dominant, w, per_call[dominant])
     work = algorithmic_work(w)[dominant]
-    roof["traffic"] = traffic_for(dominant, w.name)
+    # the committed counters were taken on the method without variant flags
+    roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 else None
     roof["kernel"] = KERNEL_SYMBOLS[dominant]
     roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
     kernels = {}
@@ -345,11 +349,11 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": d,
                    "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
-                   "causal": w.causal},
+                   "causal": w.causal, "flags": args.flags},
         "roofline": roof, "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x)
+        result["cpu_baseline"] = cpu_baseline(w, x, flags=args.flags)
     print(json.dumps(result), flush=True)
 
 

@@ -86,6 +86,14 @@ def test_wrap_two_chunks_is_full_attention(causal):
     assert err <= GP.GATE["bf16"], err
 
 
+def test_maximum_sizes_sampled():
+    """The largest chunk count (32767: chunk ids fill int16) and bucket count
+    (32768) the boundary accepts, with two rounds at L = 32767 * 32."""
+    w = W("max_sizes", seq_len=32767 * 32, chunk=32, n_buckets=32768, n_rounds=2, causal=True,
+          seed=130)
+    GP.sampled_parity(w, n_samples=256)
+
+
 def test_full_size_sampled_variants():
     """paper_64k with both variant flags, in the benchmark's launch configuration."""
     GP.sampled_parity(WORKLOADS["paper_64k"], n_samples=512,
