@@ -43,6 +43,10 @@ notes):
     N_ij is the number of rounds whose window for i contains j (duplicate-count
     correction); with it, the combined output equals attention over the union
     of the rounds' windows.  The variant dup_correct=False leaves it out;
+  * inside a window every key is attended, whatever its bucket.  The variant
+    same_bucket=True keeps only keys in the query's bucket of that round
+    ([MOD] "LSH attention": the set P_i of keys hashed like the query), and
+    N_ij then counts the rounds where j is in the window and in i's bucket;
   * R has shape [n_rounds, d, n_buckets/2] and is shared by every batch row and
     head, as in [ULT]'s example;
   * ties in the argmax go to the first index, as in [ULT]'s example.
@@ -180,25 +184,30 @@ def window_slots(k: int, chunk: int, nchunks: int = 0, wrap: bool = False) -> np
 
 
 def duplicate_counts(cid_q: np.ndarray, cid_k: np.ndarray, nchunks: int = 0,
-                     wrap: bool = False) -> np.ndarray:
+                     wrap: bool = False, bkt_q: Optional[np.ndarray] = None,
+                     bkt_k: Optional[np.ndarray] = None) -> np.ndarray:
     """N[i, j] = number of rounds whose window for query i contains key j.
 
     cid_q [nq, n_r], cid_k [nk, n_r] are chunk ids per round.  Key j lies in the
     window of query i in round r exactly when its chunk is the query's chunk or
     the one before it: cid_q[i, r] - cid_k[j, r] is 0 or 1; with wrap, the
     chunk before chunk 0 is the last one, so the difference is taken modulo
-    the number of chunks.
+    the number of chunks.  With bucket ids (bkt_q [nq, n_r], bkt_k [nk, n_r])
+    a round counts only when the two buckets are equal as well.
     """
     diff = cid_q[:, None, :].astype(np.int64) - cid_k[None, :, :].astype(np.int64)
     if wrap:
         diff = np.mod(diff, nchunks)
-    return ((diff == 0) | (diff == 1)).sum(axis=2)
+    inside = (diff == 0) | (diff == 1)
+    if bkt_q is not None:
+        inside &= bkt_q[:, None, :] == bkt_k[None, :, :]
+    return inside.sum(axis=2)
 
 
 def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
                     cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
                     query_slots: Optional[np.ndarray] = None, dup_correct: bool = True,
-                    wrap: bool = False):
+                    wrap: bool = False, bkt_bh: Optional[np.ndarray] = None, r: int = 0):
     """One round's attention for the queries of sorted chunk k.
 
     qk_bh, v_bh [L, d] (one batch row and head), perm_r [L] (this round's sorted
@@ -211,7 +220,9 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
     query_slots restricts the queries to some sorted slots of chunk k.  The
     variants dup_correct=False (no log N_ij term) and wrap=True (chunk 0 looks
     back to the last chunk) change the window and its scores as described in
-    window_chunks and duplicate_counts.
+    window_chunks and duplicate_counts.  With bkt_bh [L, n_r] (bucket of every
+    position in every round; r is this round) the window keeps only the keys
+    in the query's bucket of round r (the same-bucket variant).
     """
     nchunks = len(perm_r) // chunk
     q_slots = np.arange(k * chunk, (k + 1) * chunk) if query_slots is None else np.asarray(query_slots)
@@ -221,8 +232,14 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
     q = np.asarray(qk_bh[qi], dtype=np.float64)
     kk = np.asarray(qk_bh[kj], dtype=np.float64)
     s = scale * (q @ kk.T)
+    if bkt_bh is not None:
+        s = np.where(bkt_bh[kj, r][None, :] != bkt_bh[qi, r][:, None], -np.inf, s)
     if dup_correct:
-        s = s - np.log(duplicate_counts(cid_bh[qi], cid_bh[kj], nchunks, wrap))
+        bq = None if bkt_bh is None else bkt_bh[qi]
+        bk = None if bkt_bh is None else bkt_bh[kj]
+        N = duplicate_counts(cid_bh[qi], cid_bh[kj], nchunks, wrap, bq, bk)
+        # N = 0 only for keys the bucket mask has already set to -inf
+        s = s - np.log(np.maximum(N, 1))
     s = s - SELF_PENALTY * (qi[:, None] == kj[None, :])
     if causal:
         s = np.where(kj[None, :] > qi[:, None], -np.inf, s)
@@ -236,9 +253,10 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
 
 def attention_rounds(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.ndarray,
                      chunk: int, causal: bool, scale: float, dup_correct: bool = True,
-                     wrap: bool = False):
+                     wrap: bool = False, buckets: Optional[np.ndarray] = None):
     """Every round's output in original position order.
 
+    buckets [B, H, n_r, L] selects the same-bucket variant.
     -> o_r float64 [B, H, n_r, L, d], lse float64 [B, H, n_r, L].
     """
     B, H, L, d = qk.shape
@@ -249,24 +267,28 @@ def attention_rounds(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.nd
     lse = np.empty((B, H, n_r, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
+            bkt = None if buckets is None else np.asarray(buckets[b, h]).T     # [L, n_r]
             for r in range(n_r):
                 for k in range(L // chunk):
                     qi, o, l = chunk_attention(qk[b, h], v[b, h], perm[b, h, r], cid[b, h],
                                                k, chunk, causal, scale, dup_correct=dup_correct,
-                                               wrap=wrap)
+                                               wrap=wrap, bkt_bh=bkt, r=r)
                     o_r[b, h, r, qi] = o
                     lse[b, h, r, qi] = l
     return o_r, lse
 
 
 def attention_one(qk_bh, v_bh, perm_bh, cid_bh, r: int, pos: int, chunk: int,
-                  causal: bool, scale: float, dup_correct: bool = True, wrap: bool = False):
-    """Round r's (o, lse) for the single query at position ``pos`` (sampled checks)."""
+                  causal: bool, scale: float, dup_correct: bool = True, wrap: bool = False,
+                  buckets_bh: Optional[np.ndarray] = None):
+    """Round r's (o, lse) for the single query at position ``pos`` (sampled checks).
+    buckets_bh [n_r, L] selects the same-bucket variant."""
     slot = int(cid_bh[pos, r]) * chunk
     seg = perm_bh[r]
     slot += int(np.nonzero(seg[slot:slot + chunk] == pos)[0][0])
     _, o, l = chunk_attention(qk_bh, v_bh, seg, cid_bh, slot // chunk, chunk, causal, scale,
-                              query_slots=np.array([slot]), dup_correct=dup_correct, wrap=wrap)
+                              query_slots=np.array([slot]), dup_correct=dup_correct, wrap=wrap,
+                              bkt_bh=None if buckets_bh is None else np.asarray(buckets_bh).T, r=r)
     return o[0], float(l[0])
 
 
@@ -293,14 +315,14 @@ def default_scale(d_head: int) -> float:
 
 def forward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, n_buckets: int, chunk: int,
             causal: bool, scale: Optional[float] = None, dup_correct: bool = True,
-            wrap: bool = False):
+            wrap: bool = False, same_bucket: bool = False):
     """All four steps.  Returns a dict with every intermediate (float64 / int)."""
     if scale is None:
         scale = default_scale(qk.shape[-1])
     buckets, margins = hash_buckets(qk, R)
     perm, cid = sort_rounds(buckets, n_buckets, chunk)
     o_r, lse = attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct,
-                                wrap=wrap)
+                                wrap=wrap, buckets=buckets if same_bucket else None)
     o, LSE = combine_rounds(o_r, lse)
     return {"buckets": buckets, "margins": margins, "perm": perm, "cid": cid,
             "o_rounds": o_r, "lse": lse, "o": o, "LSE": LSE}

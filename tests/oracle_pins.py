@@ -31,7 +31,9 @@ What pins what:
            not);
          - no duplicate correction: each round equals plain softmax over its
            brute-force window (o and lse); with one round the correction is
-           a no-op.
+           a no-op;
+         - same-bucket mask: union brute force and per-round brute force with
+           windows restricted to the query's bucket.
 """
 from __future__ import annotations
 
@@ -197,11 +199,12 @@ def check_full_attention(L=40, d=8, nb=6, n_r=3, causal=False, scale=None, seed=
 
 
 def check_union(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=13, dup_correct=True,
-                wrap=False):
+                wrap=False, same_bucket=False):
     w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
-    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=dup_correct, wrap=wrap)
+    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=dup_correct, wrap=wrap,
+                   same_bucket=same_bucket)
     ref = RF.union_attention(qk[0, 0], v[0, 0], out["buckets"][0, 0], chunk, causal,
-                             1.0 / math.sqrt(d), wrap=wrap)
+                             1.0 / math.sqrt(d), wrap=wrap, same_bucket=same_bucket)
     err = np.max(np.abs(out["o"][0, 0] - ref))
     assert err < TOL_COMBINED, err
 
@@ -218,12 +221,12 @@ def check_wrap_two_chunks(L=40, d=8, nb=6, n_r=3, causal=False, seed=18):
 
 
 def check_rounds_without_correction(L=48, d=8, nb=6, n_r=3, chunk=8, causal=True, seed=19,
-                                    wrap=False):
+                                    wrap=False, same_bucket=False):
     """Without the duplicate-count term every round is plain softmax attention
     over that round's window (o_rounds and lse, round by round)."""
     w, qk, v, R = small_case(L=L, d=d, nb=nb, n_r=n_r, chunk=chunk, causal=causal, seed=seed)
-    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=False, wrap=wrap)
-    W = RF.brute_windows(out["buckets"][0, 0], chunk, causal, wrap)
+    out = _forward(w, qk[0, 0], v[0, 0], R, dup_correct=False, wrap=wrap, same_bucket=same_bucket)
+    W = RF.brute_windows(out["buckets"][0, 0], chunk, causal, wrap, same_bucket)
     for r in range(n_r):
         o, lse = RF.round_attention(qk[0, 0], v[0, 0], W[r], 1.0 / math.sqrt(d))
         assert np.max(np.abs(out["o_rounds"][0, 0, r] - o)) < 1e-12
@@ -325,4 +328,9 @@ ALL_CHECKS = {
     "rounds_without_correction_wrap": lambda: check_rounds_without_correction(wrap=True,
                                                                               causal=False, seed=24),
     "single_round_correction_free": check_single_round_correction_free,
+    "union_same_bucket": lambda: check_union(same_bucket=True, nb=4, chunk=8, L=48, seed=25),
+    "union_same_bucket_causal": lambda: check_union(same_bucket=True, causal=True, n_r=4, nb=4,
+                                                    chunk=4, L=32, seed=26),
+    "rounds_without_correction_same_bucket": lambda: check_rounds_without_correction(
+        same_bucket=True, nb=4, seed=27),
 }

@@ -17,7 +17,8 @@ function with it.  Each is slow (Python loops) and meant for small inputs.
   and each query attends, with plain softmax weights, to the union of the keys
   its windows hold across rounds (minus itself unless nothing else is there).
   The duplicate-count corrected multi-round output must equal this.  With
-  wrap, the chunk before the first is the last one.
+  wrap, the chunk before the first is the last one; with the same-bucket
+  mask, a window keeps only the keys in the query's bucket of that round.
 
 * round_attention: one round without the duplicate-count term, plain softmax
   over the round's window; the variant without the correction must give it
@@ -55,12 +56,14 @@ def brute_chunk_of(buckets_r, chunk: int) -> list:
     return chunk_of
 
 
-def brute_windows(buckets: np.ndarray, chunk: int, causal: bool, wrap: bool = False):
+def brute_windows(buckets: np.ndarray, chunk: int, causal: bool, wrap: bool = False,
+                  same_bucket: bool = False):
     """W[r][i] = set of keys in query i's window in round r (after the causal cut).
 
     Key j is in the window when its chunk is the query's chunk or the one just
     before it; with wrap, the chunk before the first is the last, i.e. the
-    chunk distance is counted around a circle of L / chunk chunks.
+    chunk distance is counted around a circle of L / chunk chunks; with
+    same_bucket, j must also share the query's bucket in that round.
     """
     n_r, L = buckets.shape
     nchunks = L // chunk
@@ -69,7 +72,8 @@ def brute_windows(buckets: np.ndarray, chunk: int, causal: bool, wrap: bool = Fa
         c = brute_chunk_of(buckets[r], chunk)
         W.append([{j for j in range(L)
                    if ((c[i] - c[j]) % nchunks if wrap else c[i] - c[j]) in (0, 1)
-                   and (not causal or j <= i)}
+                   and (not causal or j <= i)
+                   and (not same_bucket or int(buckets[r][j]) == int(buckets[r][i]))}
                   for i in range(L)])
     return W
 
@@ -97,11 +101,12 @@ def round_attention(qk: np.ndarray, v: np.ndarray, window: list, scale: float):
 
 
 def union_attention(qk: np.ndarray, v: np.ndarray, buckets: np.ndarray, chunk: int,
-                    causal: bool, scale: float, wrap: bool = False) -> np.ndarray:
+                    causal: bool, scale: float, wrap: bool = False,
+                    same_bucket: bool = False) -> np.ndarray:
     """buckets [n_r, L] of one (batch row, head)."""
     qk = np.asarray(qk, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    W = brute_windows(buckets, chunk, causal, wrap)
+    W = brute_windows(buckets, chunk, causal, wrap, same_bucket)
     L = qk.shape[0]
     out = np.empty_like(v)
     for i in range(L):

@@ -122,6 +122,11 @@ def _correction_always_on(a, k):
     return a, k
 
 
+def _bucket_mask_ignored(a, k):
+    k["bkt_bh"] = None
+    return a, k
+
+
 _WINDOW_CHUNKS_ORIG = O.window_chunks
 
 
@@ -143,10 +148,14 @@ MUTATIONS = {
     "wrap-around ignored": ("window_chunks", lambda k, n, wrap=False: _WINDOW_CHUNKS_ORIG(k, n, False),
                             "wrap_two_chunks"),
     "wrap-around missing from the counts": ("duplicate_counts",
-                                            lambda q, k, n=0, wrap=False: _DUP_ORIG(q, k, n, False),
+                                            lambda q, k, n=0, wrap=False, *b: _DUP_ORIG(q, k, n, False, *b),
                                             "union_wrap"),
     "correction applied when switched off": ("chunk_attention", "correction_always_on",
                                              "rounds_without_correction"),
+    "same-bucket mask ignored": ("chunk_attention", "bucket_mask_ignored", "union_same_bucket"),
+    "buckets missing from the counts": ("duplicate_counts",
+                                        lambda q, k, n=0, wrap=False, *b: _DUP_ORIG(q, k, n, wrap),
+                                        "union_same_bucket"),
 }
 
 
@@ -160,6 +169,8 @@ def test_mutation_is_caught(name, monkeypatch):
         repl = _wrap(orig, _values_are_keys)
     elif repl == "correction_always_on":
         repl = _wrap(orig, _correction_always_on)
+    elif repl == "bucket_mask_ignored":
+        repl = _wrap(orig, _bucket_mask_ignored)
     monkeypatch.setattr(O, attr, repl)
     with pytest.raises((AssertionError, IndexError, ValueError)):
         P.ALL_CHECKS[check]()
