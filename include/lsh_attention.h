@@ -79,11 +79,22 @@ enum { LSH_F32 = 0, LSH_BF16 = 1 };
  *        chunk of that round (look-back around the end of the sorted order);
  *        with a single chunk it attends to itself once.  N_ij counts the rounds
  *        with (cid[i,r'] - cid[j,r']) mod (L / c) in {0, 1}.
- * The pages leave both points open (they describe look-back to the previous
- * chunk, and the duplicate-count term is the reading under which the rounds'
- * outputs merge to attention over their union).
+ *   LSH_FLAG_SAME_BUCKET        inside the window, only keys in the query's
+ *        bucket of that round are attended ([MOD] "LSH attention": the set
+ *        P_i), and N_ij counts the rounds where j is in the window and in i's
+ *        bucket.  lsh_sort then writes window ids instead of chunk ids:
+ *        cid[b,h,pos,r] = slot / c + 2 * (number of non-empty buckets below the
+ *        position's bucket in round r), stored as an unsigned 16-bit value;
+ *        two ids differ by 0 or 1 exactly when the buckets are equal and the
+ *        chunks differ by 0 or 1.  Needs L/c - 1 + 2 (min(nb, L) - 1) <= 65534
+ *        and cannot be combined with LSH_FLAG_WRAP_LOOKBACK (LSH_ERR_UNSUPPORTED).
+ * Every call of one forward pass must get the same flags.  The pages leave
+ * these points open (they describe look-back to the previous chunk; [MOD]'s
+ * per-bucket set P_i and the chunk windows of [AIS] and [ULT] disagree; the
+ * duplicate-count term is the reading under which the rounds' outputs merge
+ * to attention over their union).
  */
-enum { LSH_FLAG_NO_DUP_CORRECTION = 1, LSH_FLAG_WRAP_LOOKBACK = 2 };
+enum { LSH_FLAG_NO_DUP_CORRECTION = 1, LSH_FLAG_WRAP_LOOKBACK = 2, LSH_FLAG_SAME_BUCKET = 4 };
 
 typedef struct lsh_config {
     int32_t batch;      /* B >= 1 */
@@ -122,8 +133,9 @@ size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
  *   buckets    [B, H, n_r, L]   int32 in, values in [0, nb) (not checked)
  *   perm       [B, H, n_r, L]   int32 out: perm[b,h,r,slot] = position
  *   cid        [B, H, L, n_r]   int16 out: cid[b,h,pos,r] = slot(pos) / chunk
- *   workspace  device scratch of at least lsh_sort_workspace_bytes(cfg) bytes;
- *              its contents on entry do not matter.
+ *   workspace  device scratch of at least lsh_sort_workspace_bytes(cfg) bytes
+ *              (larger with LSH_FLAG_SAME_BUCKET); its contents on entry do
+ *              not matter.
  */
 lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm,
                     int16_t* cid, void* workspace, size_t workspace_bytes, void* stream);

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "liblsh_attention.so")
 LSH_OK, LSH_ERR_INVALID_ARG, LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_ERR_HIP = range(5)
 LSH_F32, LSH_BF16 = 0, 1
 # variant flags of lsh_config.flags (see include/lsh_attention.h)
-LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK = 1, 2
+LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2, 4
 
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
             "lsh_combine_rounds", "lsh_status_string", "lsh_last_error")

@@ -66,8 +66,18 @@ lsh_status check_config(const lsh_config* c)
         return fail(LSH_ERR_UNSUPPORTED, "dtype must be LSH_F32 or LSH_BF16");
     if (c->n_buckets > 32768) return fail(LSH_ERR_UNSUPPORTED, "n_buckets must be at most 32768");
     if (c->n_rounds > 16) return fail(LSH_ERR_UNSUPPORTED, "n_rounds must be at most 16");
-    if (c->flags & ~(LSH_FLAG_NO_DUP_CORRECTION | LSH_FLAG_WRAP_LOOKBACK))
+    if (c->flags & ~(LSH_FLAG_NO_DUP_CORRECTION | LSH_FLAG_WRAP_LOOKBACK | LSH_FLAG_SAME_BUCKET))
         return fail(LSH_ERR_UNSUPPORTED, "unknown flag bit");
+    if ((c->flags & LSH_FLAG_SAME_BUCKET) && (c->flags & LSH_FLAG_WRAP_LOOKBACK))
+        return fail(LSH_ERR_UNSUPPORTED, "LSH_FLAG_SAME_BUCKET cannot be combined with LSH_FLAG_WRAP_LOOKBACK");
+    if (c->flags & LSH_FLAG_SAME_BUCKET) {
+        // window ids chunk + 2 * bucket rank must fit in 16 bits (at most 65534)
+        const long long last = (long long)(c->seq_len / c->chunk - 1) +
+                               2LL * ((long long)(c->n_buckets < c->seq_len ? c->n_buckets : c->seq_len) - 1);
+        if (last > 65534)
+            return fail(LSH_ERR_UNSUPPORTED,
+                        "LSH_FLAG_SAME_BUCKET needs L/chunk - 1 + 2 (min(n_buckets, L) - 1) <= 65534");
+    }
     const long long elem = c->dtype == LSH_BF16 ? 2 : 4;
     // the largest buffer is o_rounds [B, H, n_r, L, d]
     if (checked_product({c->batch, c->heads, c->n_rounds, c->seq_len, c->d_head, elem}) < 0)
@@ -121,11 +131,17 @@ lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_
                       "lsh_hash");
 }
 
+// counters, then (same-bucket variant) one rank per (segment, bucket)
+size_t ranks_of(const lsh_config* cfg, const lshk::SortPlan& p)
+{
+    return (cfg->flags & LSH_FLAG_SAME_BUCKET) ? (size_t)p.nseg * cfg->n_buckets : 0;
+}
+
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg)
 {
     if (check_config(cfg) != LSH_OK) return 0;
     const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
-    return p.counters * sizeof(int32_t);
+    return (p.counters + ranks_of(cfg, p)) * sizeof(int32_t);
 }
 
 lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm, int16_t* cid,
@@ -137,11 +153,13 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
     LSH_TRY(check_ptr(cid, "cid"));
     LSH_TRY(check_ptr(workspace, "workspace"));
     const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
-    if (workspace_bytes < p.counters * sizeof(int32_t))
+    if (workspace_bytes < (p.counters + ranks_of(cfg, p)) * sizeof(int32_t))
         return fail(LSH_ERR_WORKSPACE, "workspace smaller than lsh_sort_workspace_bytes()");
-    return hip_status(lshk::launch_sort(buckets, perm, cid, static_cast<int32_t*>(workspace), p,
-                                        bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets,
-                                        cfg->chunk, static_cast<hipStream_t>(stream)),
+    int32_t* counters = static_cast<int32_t*>(workspace);
+    int32_t* ranks = ranks_of(cfg, p) ? counters + p.counters : nullptr;
+    return hip_status(lshk::launch_sort(buckets, perm, cid, counters, ranks, p, bh_of(cfg),
+                                        cfg->seq_len, cfg->n_rounds, cfg->n_buckets, cfg->chunk,
+                                        static_cast<hipStream_t>(stream)),
                       "lsh_sort");
 }
 

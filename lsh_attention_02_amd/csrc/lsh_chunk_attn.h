@@ -145,11 +145,15 @@ struct Lds {
     char vt[2][D * VROWB];
     int pos[2][C];
     uint32_t cid[2][C * (NDW > 0 ? NDW : 1)];
+    int rid[2][C];                 // same-bucket variant: this round's window id of each row
 };
 
 // NDW = 0: no duplicate-count term (LSH_FLAG_NO_DUP_CORRECTION).  WRAP: chunk 0
-// looks back to the last chunk of its round (LSH_FLAG_WRAP_LOOKBACK).
-template <typename T, int D, int C, int NDW, bool WRAP>
+// looks back to the last chunk of its round (LSH_FLAG_WRAP_LOOKBACK).  SAME:
+// keys outside the query's bucket of this round are dropped
+// (LSH_FLAG_SAME_BUCKET; cid then holds window ids, and the test that puts a
+// key in a query's window in a round also checks the bucket).
+template <typename T, int D, int C, int NDW, bool WRAP, bool SAME>
 __global__ __launch_bounds__(4 * C)
 void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                   const int32_t* __restrict__ perm, const int16_t* __restrict__ cid,
@@ -203,6 +207,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     int mypos = 0;         // raw perm entry of row tid (tid < C), next chunk to load
     u32x4 kreg[JPT][4], vreg[JPT][4];
     uint32_t craw[2 * NW];    // chunk ids of row tid per round (raw), chunk held in registers
+    uint32_t ridraw = 0;       // same-bucket variant: row tid's window id in this round
     int rpos = 0;          // position of row tid for the chunk held in registers
 
     auto fetch_positions = [&](int kk) {
@@ -228,11 +233,12 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             }
         }
         rpos = clamp_pos(mypos);
+        const int16_t* cr = cb + (long)rpos * n_r;
         if constexpr (NDW > 0) {
-            const int16_t* cr = cb + (long)rpos * n_r;
 #pragma unroll
             for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
         }
+        if constexpr (SAME) ridraw = (uint16_t)cr[r];
     };
     auto store_rows = [&](int sl) {
 #pragma unroll
@@ -263,6 +269,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
         }
         if (tid < C) {
             sm.pos[sl][tid] = rpos;
+            if constexpr (SAME) sm.rid[sl][tid] = (int)ridraw;
             // rounds past n_r hold 0 for keys and queries alike (always inside)
 #pragma unroll
             for (int w = 0; w < NDW; ++w) {   // nothing when NDW = 0
@@ -309,6 +316,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             uint32_t q1[NW];           // query chunk ids minus one, per half
 #pragma unroll
             for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[cur][qrow * NDW + w], ones);
+            const int rq1 = SAME ? sm.rid[cur][qrow] - 1 : 0;   // query's window id minus one
 
             // ---- S^T tiles of 16 keys: [0, CT) previous chunk, [CT, 2CT) this one.
             //      Lane (r16, g) holds query r16 against keys 4g + j of each tile.
@@ -337,6 +345,8 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 const bool diag = t == CT + wave;   // the tile holding the queries themselves
                 const int krow0 = (t % CT) * 16 + 4 * g;
                 const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
+                int4 kr = {0, 0, 0, 0};
+                if constexpr (SAME) kr = *reinterpret_cast<const int4*>(&sm.rid[slk][krow0]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
@@ -350,6 +360,11 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     float sc = fmaf(s[t][j], scale_log2, nlg);
                     if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
+                    if constexpr (SAME) {
+                        // another bucket: window ids differ by something other than 0 or 1
+                        const int kid = j == 0 ? kr.x : j == 1 ? kr.y : j == 2 ? kr.z : kr.w;
+                        if ((unsigned)(kid - rq1) > 1u) sc = -INFINITY;
+                    }
                     s[t][j] = sc;
                     mx = fmaxf(mx, sc);
                 }
@@ -443,7 +458,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     }
 }
 
-template <typename T, int D, int C, int NDW, bool WRAP>
+template <typename T, int D, int C, int NDW, bool WRAP, bool SAME>
 hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
                       void* o_rounds, float* lse, long bh, int L, int n_r, int causal, float scale,
                       hipStream_t s)
@@ -451,7 +466,7 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
     const int nchunks = L / C;
     const int nruns = (nchunks + RUN - 1) / RUN;
     const long blocks = bh * nruns * n_r;
-    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW, WRAP>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
+    hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW, WRAP, SAME>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const T*>(qk), static_cast<const T*>(v), perm, cid,
                        static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns);
     return hipGetLastError();
@@ -459,28 +474,34 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
 
 // Dispatch on the number of packed chunk-id words (1, 2, 4 or 8 for up to 16
 // rounds; 0 without the duplicate-count term).
-template <typename T, int D, int C, bool WRAP>
+template <typename T, int D, int C, bool WRAP, bool SAME>
 hipError_t launch_ndw(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
                       void* o, float* lse, long bh, int L, int n_r, int causal, float scale,
                       bool dup, hipStream_t s)
 {
-    if (!dup) return launch_one<T, D, C, 0, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    if (n_r <= 2) return launch_one<T, D, C, 1, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    if (n_r <= 4) return launch_one<T, D, C, 2, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    if (n_r <= 8) return launch_one<T, D, C, 4, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
-    return launch_one<T, D, C, 8, WRAP>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s);
+#define LSH_ONE(NDW) \
+    launch_one<T, D, C, NDW, WRAP, SAME>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, s)
+    if (!dup) return LSH_ONE(0);
+    if (n_r <= 2) return LSH_ONE(1);
+    if (n_r <= 4) return LSH_ONE(2);
+    if (n_r <= 8) return LSH_ONE(4);
+    return LSH_ONE(8);
+#undef LSH_ONE
 }
 
-// Dispatch on the variant flags (LSH_FLAG_NO_DUP_CORRECTION = 1, LSH_FLAG_WRAP_LOOKBACK = 2).
+// Dispatch on the variant flags (LSH_FLAG_NO_DUP_CORRECTION = 1,
+// LSH_FLAG_WRAP_LOOKBACK = 2, LSH_FLAG_SAME_BUCKET = 4; the host rejects 2 | 4).
 template <typename T, int D, int C>
 hipError_t launch_flags(const void* qk, const void* v, const int32_t* perm, const int16_t* cid,
                         void* o, float* lse, long bh, int L, int n_r, int causal, float scale,
                         int flags, hipStream_t s)
 {
     const bool dup = !(flags & 1);
+    if (flags & 4)
+        return launch_ndw<T, D, C, false, true>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
     if (flags & 2)
-        return launch_ndw<T, D, C, true>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
-    return launch_ndw<T, D, C, false>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
+        return launch_ndw<T, D, C, true, false>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
+    return launch_ndw<T, D, C, false, false>(qk, v, perm, cid, o, lse, bh, L, n_r, causal, scale, dup, s);
 }
 
 }  // namespace attn

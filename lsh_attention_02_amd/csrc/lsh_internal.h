@@ -22,9 +22,10 @@ struct SortPlan {
 };
 SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets);
 
+// ranks: null, or nseg * n_buckets int32 of scratch for the same-bucket variant.
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
-                       const SortPlan& plan, long bh, int L, int n_rounds, int n_buckets,
-                       int chunk, hipStream_t stream);
+                       int32_t* ranks, const SortPlan& plan, long bh, int L, int n_rounds,
+                       int n_buckets, int chunk, hipStream_t stream);
 
 hipError_t launch_chunk_attn(int dtype, int d_head, int chunk, const void* qk, const void* v,
                              const int32_t* perm, const int16_t* cid, void* o_rounds, float* lse,

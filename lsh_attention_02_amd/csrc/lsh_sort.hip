@@ -13,7 +13,9 @@
 //                   equal buckets are ranked by lane with ballots; the four
 //                   waves take their offsets in order (barrier phases), so equal
 //                   buckets keep position order across the whole segment.
-// Outputs: perm[seg][slot] = position and cid[b,h][position][round] = slot / chunk.
+// Outputs: perm[seg][slot] = position and cid[b,h][position][round] = slot / chunk
+// (with the same-bucket variant: slot / chunk + 2 * rank of the bucket among the
+// segment's non-empty buckets, computed by the scan).
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
@@ -73,12 +75,14 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wave_sums, int* 
     return x;
 }
 
+// ranks (may be null): ranks[seg][b] = number of non-empty buckets below b in
+// the segment (used by the same-bucket variant's window ids).
 __global__ __launch_bounds__(SCAN_THREADS)
-void k_sort_scan(int32_t* __restrict__ counters, int nb, int ntiles)
+void k_sort_scan(int32_t* __restrict__ counters, int32_t* __restrict__ ranks, int nb, int ntiles)
 {
     __shared__ int wave_sums[SCAN_THREADS / 64];
     int32_t* c = counters + (long)blockIdx.x * ntiles * nb;
-    int carry = 0;
+    int carry = 0, rank_carry = 0;
     for (int b0 = 0; b0 < nb; b0 += SCAN_THREADS) {
         const int b = b0 + threadIdx.x;
         int tot = 0;
@@ -95,6 +99,13 @@ void k_sort_scan(int32_t* __restrict__ counters, int nb, int ntiles)
             }
         }
         carry += group_total;
+        if (ranks != nullptr) {                        // uniform over the block
+            const int nz = tot > 0 ? 1 : 0;
+            int group_nz;
+            const int incl_nz = block_inclusive_scan(nz, wave_sums, &group_nz);
+            if (b < nb) ranks[(long)blockIdx.x * nb + b] = rank_carry + incl_nz - nz;
+            rank_carry += group_nz;
+        }
     }
 }
 
@@ -115,8 +126,9 @@ struct ScatterMap {
 
 __global__ __launch_bounds__(SORT_THREADS)
 void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restrict__ counters,
-                    int32_t* __restrict__ perm, int16_t* __restrict__ cid, int L, int nb,
-                    int nbits, int tile, int ntiles, int n_r, int chunk, ScatterMap map)
+                    const int32_t* __restrict__ ranks, int32_t* __restrict__ perm,
+                    int16_t* __restrict__ cid, int L, int nb, int nbits, int tile, int ntiles,
+                    int n_r, int chunk, ScatterMap map)
 {
     extern __shared__ int next_slot[];
     const int xcd = blockIdx.x % NXCD;
@@ -167,7 +179,10 @@ void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restri
         // the sort (e.g. two overlapping calls sharing one workspace)
         if (valid && (unsigned)slot < (unsigned)L) {
             pm[slot] = p;
-            cd[(long)p * n_r + r] = (int16_t)(slot / chunk);
+            // chunk id; with ranks, the window id chunk + 2 * rank(bucket)
+            // (at most 65534, stored as the bit pattern of an unsigned 16-bit value)
+            const int id = slot / chunk + (ranks != nullptr ? 2 * ranks[seg * nb + b] : 0);
+            cd[(long)p * n_r + r] = (int16_t)(uint16_t)id;
         }
     }
 }
@@ -190,8 +205,8 @@ SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets)
 }
 
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
-                       const SortPlan& plan, long bh, int L, int n_rounds, int n_buckets,
-                       int chunk, hipStream_t s)
+                       int32_t* ranks, const SortPlan& plan, long bh, int L, int n_rounds,
+                       int n_buckets, int chunk, hipStream_t s)
 {
     const size_t lds = (size_t)n_buckets * sizeof(int);
     // Up to 32768 buckets need 128 KiB of dynamic LDS per workgroup.
@@ -208,7 +223,7 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
     hipLaunchKernelGGL(k_sort_hist, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters, L,
                        n_buckets, plan.tile, plan.ntiles);
     hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)plan.nseg), dim3(SCAN_THREADS), 0, s, counters,
-                       n_buckets, plan.ntiles);
+                       ranks, n_buckets, plan.ntiles);
     ScatterMap map;
     if (bh >= NXCD) { map.nkeys = bh; map.rounds_per_key = n_rounds; }
     else { map.nkeys = plan.nseg; map.rounds_per_key = 1; }
@@ -216,7 +231,8 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
     const long rows = (map.nkeys + NXCD - 1) / NXCD;
     const unsigned sblocks = (unsigned)(rows * NXCD * map.per_key);
     hipLaunchKernelGGL(k_sort_scatter, dim3(sblocks), dim3(SORT_THREADS), lds, s, buckets, counters,
-                       perm, cid, L, n_buckets, nbits, plan.tile, plan.ntiles, n_rounds, chunk, map);
+                       ranks, perm, cid, L, n_buckets, nbits, plan.tile, plan.ntiles, n_rounds,
+                       chunk, map);
     return hipGetLastError();
 }
 

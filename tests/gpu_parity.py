@@ -47,9 +47,29 @@ def cfg_of(w: Workload, scale=None, flags=0) -> lsh.LSHConfig:
 
 
 def variant(flags: int) -> dict:
-    """The oracle's switches for the library's LSH_FLAG_* bits."""
+    """The oracle's switches for the library's LSH_FLAG_* bits (the same-bucket
+    variant also needs the buckets, passed separately)."""
     return {"dup_correct": not (flags & lsh.LSH_FLAG_NO_DUP_CORRECTION),
             "wrap": bool(flags & lsh.LSH_FLAG_WRAP_LOOKBACK)}
+
+
+def same_bucket(flags: int) -> bool:
+    return bool(flags & lsh.LSH_FLAG_SAME_BUCKET)
+
+
+def window_ids(chunk_ids: np.ndarray, buckets: np.ndarray, n_buckets: int) -> np.ndarray:
+    """What lsh_sort writes into cid with LSH_FLAG_SAME_BUCKET (the header's
+    definition): chunk id + 2 * number of non-empty buckets below the position's
+    bucket in that round.  chunk_ids [B, H, L, n_r], buckets [B, H, n_r, L]."""
+    B, H, n_r, L = buckets.shape
+    out = chunk_ids.astype(np.int64).copy()
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_r):
+                nonempty = np.bincount(buckets[b, h, r], minlength=n_buckets) > 0
+                rank = np.cumsum(nonempty) - nonempty
+                out[b, h, :, r] += 2 * rank[buckets[b, h, r]]
+    return out
 
 
 def upload(w: Workload, x: Dict[str, np.ndarray], device="cuda:0"):
@@ -112,9 +132,15 @@ def full_parity(w: Workload, scale=None, x=None, flags=0) -> dict:
     # sort of the GPU's own buckets
     sp, sc_id = O.sort_rounds(gb, w.n_buckets, w.chunk)
     assert np.array_equal(to_np(g["perm"]), sp), f"{w.name}: perm differs from the stable sort"
-    assert np.array_equal(to_np(g["cid"]), sc_id), f"{w.name}: cid differs"
-    # attention fed the GPU's perm/cid
-    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc, **var)
+    gcid = to_np(g["cid"])
+    if same_bucket(flags):
+        assert np.array_equal(gcid.view(np.uint16), window_ids(sc_id, gb, w.n_buckets)), \
+            f"{w.name}: window ids differ"
+    else:
+        assert np.array_equal(gcid, sc_id), f"{w.name}: cid differs"
+    # attention fed the GPU's perm (and its buckets for the same-bucket mask)
+    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc, **var,
+                                  buckets=gb if same_bucket(flags) else None)
     rep["o_rounds_err"] = rel_err(to_np(g["o_rounds"]), o_r)
     assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
     rep["lse_abs_err"] = check_lse(to_np(g["lse"]), lse, w.dtype, w.name)
@@ -127,7 +153,8 @@ def full_parity(w: Workload, scale=None, x=None, flags=0) -> dict:
     rep["heads_bucket_exact"] = f"{int(same.sum())}/{same.size}"
     if same.any():
         pf, cf = O.sort_rounds(ob, w.n_buckets, w.chunk)
-        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc, **var)
+        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc, **var,
+                                      buckets=ob if same_bucket(flags) else None)
         of, _ = O.combine_rounds(of_r, lf)
         go = to_np(g["o"])
         rep["forward_err"] = rel_err(go[same], of[same])
@@ -138,8 +165,10 @@ def full_parity(w: Workload, scale=None, x=None, flags=0) -> dict:
 
 
 # --------------------------------------------------------------------------- full-size, sampled
-def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, what: str) -> None:
-    """The properties that determine the stable sort uniquely, checked on every segment."""
+def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, what: str,
+                    n_buckets: int = 0, flags: int = 0) -> np.ndarray:
+    """The properties that determine the stable sort uniquely, checked on every
+    segment.  Returns the chunk ids [B, H, L, n_r] (slot // chunk)."""
     B, H, n_r, L = gb.shape
     b2 = gb.reshape(-1, L).astype(np.int64)
     p2 = gp.reshape(-1, L).astype(np.int64)
@@ -152,7 +181,12 @@ def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, 
     slot = np.empty_like(p2)
     np.put_along_axis(slot, p2, np.broadcast_to(np.arange(L), p2.shape), axis=1)
     want = (slot // chunk).reshape(B, H, n_r, L).transpose(0, 1, 3, 2)
-    assert np.array_equal(gc.astype(np.int64), want), f"{what}: cid differs from slot // chunk"
+    if same_bucket(flags):
+        assert np.array_equal(gc.view(np.uint16), window_ids(want, gb, n_buckets)), \
+            f"{what}: window ids differ"
+    else:
+        assert np.array_equal(gc.astype(np.int64), want), f"{what}: cid differs from slot // chunk"
+    return want
 
 
 def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int = 0) -> dict:
@@ -171,7 +205,7 @@ def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int
     gp = to_np(g["perm"])
     gc = to_np(g["cid"])
     log(f"[sampled] {w.name}: sort properties ({time.time() - t0:.1f}s)")
-    sort_properties(gb, gp, gc, w.chunk, w.name)
+    chunk_ids = sort_properties(gb, gp, gc, w.chunk, w.name, w.n_buckets, flags)
     # sampled hashes
     sb, sh, sr, si = (rng.integers(0, B, n_samples), rng.integers(0, H, n_samples),
                       rng.integers(0, n_r, n_samples), rng.integers(0, L, n_samples))
@@ -190,8 +224,10 @@ def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int
     ref_l = np.empty(n_samples)
     for s in range(n_samples):
         b, h = sb[s], sh[s]
-        ref_o[s], ref_l[s] = O.attention_one(x["qk"][b, h], x["v"][b, h], gp[b, h], gc[b, h],
-                                             int(sr[s]), int(si[s]), w.chunk, w.causal, sc, **var)
+        ref_o[s], ref_l[s] = O.attention_one(x["qk"][b, h], x["v"][b, h], gp[b, h],
+                                             chunk_ids[b, h], int(sr[s]), int(si[s]), w.chunk,
+                                             w.causal, sc, **var,
+                                             buckets_bh=gb[b, h] if same_bucket(flags) else None)
     rep["o_rounds_err"] = rel_err(g_or, ref_o)
     assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "o_rounds", rep["o_rounds_err"])
     rep["lse_abs_err"] = check_lse(g_lse, ref_l, w.dtype, w.name)

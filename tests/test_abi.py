@@ -59,7 +59,8 @@ def test_flag_values_match_header():
     text = open(os.path.join(ROOT, "include", "lsh_attention.h")).read()
     vals = dict(re.findall(r"(LSH_FLAG_\w+)\s*=\s*(\d+)", text))
     assert vals == {"LSH_FLAG_NO_DUP_CORRECTION": str(B.LSH_FLAG_NO_DUP_CORRECTION),
-                    "LSH_FLAG_WRAP_LOOKBACK": str(B.LSH_FLAG_WRAP_LOOKBACK)}
+                    "LSH_FLAG_WRAP_LOOKBACK": str(B.LSH_FLAG_WRAP_LOOKBACK),
+                    "LSH_FLAG_SAME_BUCKET": str(B.LSH_FLAG_SAME_BUCKET)}
 
 
 def test_struct_layout_matches_header():
@@ -89,7 +90,9 @@ BAD_CONFIGS = [
     (dict(d_head=96), B.LSH_ERR_UNSUPPORTED, "d_head"),
     (dict(n_buckets=65536), B.LSH_ERR_UNSUPPORTED, "32768"),
     (dict(n_rounds=17), B.LSH_ERR_UNSUPPORTED, "16"),
-    (dict(flags=4), B.LSH_ERR_UNSUPPORTED, "flag"),
+    (dict(flags=8), B.LSH_ERR_UNSUPPORTED, "flag"),
+    (dict(flags=6), B.LSH_ERR_UNSUPPORTED, "WRAP"),
+    (dict(flags=4, seq_len=32767 * 32, chunk=32, n_buckets=32768), B.LSH_ERR_UNSUPPORTED, "65534"),
     (dict(flags=-1), B.LSH_ERR_UNSUPPORTED, "flag"),
     # o_rounds = 2^20 * 2^10 * 16 * 2^20 * 128 float32 = 2^63 bytes
     (dict(batch=1 << 20, heads=1 << 10, seq_len=1 << 20, chunk=1024, n_rounds=16, d_head=128,
@@ -162,9 +165,15 @@ def test_sort_workspace(lib):
     for kw, counters in cases:
         c = cfg(**kw)
         assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * counters, kw
-    c = cfg()
-    need = lib.lsh_sort_workspace_bytes(raw(c))
-    assert lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == B.LSH_ERR_WORKSPACE
+    # same-bucket variant: plus one int32 rank per (segment, bucket)
+    for kw, counters in cases:
+        c = cfg(flags=B.LSH_FLAG_SAME_BUCKET, **kw)
+        nseg = c.batch * c.heads * c.n_rounds
+        assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * (counters + nseg * c.n_buckets), kw
+    for flags in (0, B.LSH_FLAG_SAME_BUCKET):
+        c = cfg(flags=flags)
+        need = lib.lsh_sort_workspace_bytes(raw(c))
+        assert lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == B.LSH_ERR_WORKSPACE
 
 
 def test_binding_rejects_host_tensors(lib):

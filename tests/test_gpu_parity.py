@@ -52,9 +52,10 @@ def test_full_parity(name):
     GP.full_parity(w, scale=scale)
 
 
-# Variant flags: LSH_FLAG_NO_DUP_CORRECTION (1), LSH_FLAG_WRAP_LOOKBACK (2) and
-# both, on cases with several 16-chunk attention runs (the wrapped look-back of
-# chunk 0 and of every later run), one chunk, 16 rounds, f32 and d128.
+# Variant flags: LSH_FLAG_NO_DUP_CORRECTION (1), LSH_FLAG_WRAP_LOOKBACK (2), both,
+# LSH_FLAG_SAME_BUCKET (4) and 4 without the correction, on cases with several
+# 16-chunk attention runs (the wrapped look-back of chunk 0 and of every later
+# run), one chunk, 16 rounds, f32 and d128.
 FLAG_CASES = {
     "short_4k": WORKLOADS["short_4k"],
     "ragged_b2h3_L1344_nb10_r3": SMALL["ragged_b2h3_L1344_nb10_r3"],
@@ -67,7 +68,7 @@ FLAG_CASES = {
 }
 
 
-@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("flags", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("name", sorted(FLAG_CASES))
 def test_variant_parity(name, flags):
     GP.full_parity(FLAG_CASES[name], flags=flags)
@@ -94,10 +95,11 @@ def test_maximum_sizes_sampled():
     GP.sampled_parity(w, n_samples=256)
 
 
-def test_full_size_sampled_variants():
-    """paper_64k with both variant flags, in the benchmark's launch configuration."""
-    GP.sampled_parity(WORKLOADS["paper_64k"], n_samples=512,
-                      flags=lsh.LSH_FLAG_NO_DUP_CORRECTION | lsh.LSH_FLAG_WRAP_LOOKBACK)
+@pytest.mark.parametrize("flags", [lsh.LSH_FLAG_NO_DUP_CORRECTION | lsh.LSH_FLAG_WRAP_LOOKBACK,
+                                   lsh.LSH_FLAG_SAME_BUCKET])
+def test_full_size_sampled_variants(flags):
+    """paper_64k with variant flags, in the benchmark's launch configuration."""
+    GP.sampled_parity(WORKLOADS["paper_64k"], n_samples=512, flags=flags)
 
 
 def test_native_library_is_loaded():
