@@ -15,7 +15,8 @@ Sources (page title, section):
         "Locality sensitive hashing", "LSH attention", "Multi-round LSH attention".
   [AIS] ai-scholar.tech article on Reformer, section "变形金刚有哪些问题？" (the
         scaled dot-product attention formula) and section "什么是本地敏感散列（LSH）？"
-        (bucket, sort, equal chunks, attend to own and previous chunk).
+        (bucket, sort, equal chunks, attend to own and previous chunk); its
+        experiment set-up (d_model 1024, 8 heads) sizes the layer around them.
 
 The steps, in the pages' order:
   1. hash     bucket = first index of the maximum of [x R_r, -x R_r]      [ULT], [MOD]
@@ -326,3 +327,44 @@ def forward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, n_buckets: int, chunk:
     o, LSE = combine_rounds(o_r, lse)
     return {"buckets": buckets, "margins": margins, "perm": perm, "cid": cid,
             "o_rounds": o_r, "lse": lse, "o": o, "LSE": LSE}
+
+
+# --------------------------------------------------------------------------- the layer around it
+# The attention layer ([MOD] "LSH attention": queries and keys come from one
+# shared projection; [AIS] set-up: d_model 1024, 8 heads): x is projected to
+# the shared qk and to v, split into heads (column h*d + c of the projection is
+# element c of head h), attended head by head, the heads merged back and
+# projected out.  Weights are [out, in] like a linear layer's.
+def split_heads(t: np.ndarray, heads: int) -> np.ndarray:
+    """[B, L, H*d] -> [B, H, L, d] (column h*d + c is element c of head h)."""
+    B, L, hd = t.shape
+    return t.reshape(B, L, heads, hd // heads).transpose(0, 2, 1, 3)
+
+
+def merge_heads(t: np.ndarray) -> np.ndarray:
+    """[B, H, L, d] -> [B, L, H*d], the inverse of split_heads."""
+    B, H, L, d = t.shape
+    return t.transpose(0, 2, 1, 3).reshape(B, L, H * d)
+
+
+def project_in(x: np.ndarray, w_qk: np.ndarray, w_v: np.ndarray, heads: int):
+    """qk = x w_qk^T and v = x w_v^T in float64, split into heads: [B, H, L, d] each."""
+    x = np.asarray(x, dtype=np.float64)
+    qk = x @ np.asarray(w_qk, dtype=np.float64).T
+    v = x @ np.asarray(w_v, dtype=np.float64).T
+    return split_heads(qk, heads), split_heads(v, heads)
+
+
+def project_out(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """y = merge_heads(o) w_o^T in float64: [B, L, d_model]."""
+    return merge_heads(np.asarray(o, dtype=np.float64)) @ np.asarray(w_o, dtype=np.float64).T
+
+
+def layer_forward(x: np.ndarray, w_qk: np.ndarray, w_v: np.ndarray, w_o: np.ndarray,
+                  R: np.ndarray, heads: int, n_buckets: int, chunk: int, causal: bool,
+                  scale: Optional[float] = None, **variants):
+    """The whole layer; returns the forward() dict plus qk, v and y."""
+    qk, v = project_in(x, w_qk, w_v, heads)
+    out = forward(qk, v, R, n_buckets, chunk, causal, scale=scale, **variants)
+    out.update(qk=qk, v=v, y=project_out(out["o"], w_o))
+    return out

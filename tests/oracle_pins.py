@@ -34,6 +34,9 @@ What pins what:
            a no-op;
          - same-bucket mask: union brute force and per-round brute force with
            windows restricted to the query's bucket.
+  layer  - both projections against Python loops over their definitions;
+         - identity weights reduce the layer to the four steps on the input's
+           head slices; permuting heads consistently changes nothing.
 """
 from __future__ import annotations
 
@@ -303,6 +306,71 @@ def check_combine(seed=17):
     assert np.max(np.abs(LSE - (0.7 + math.log(5)))) < 1e-14
 
 
+# --------------------------------------------------------------------------- the layer
+def _layer_case(B=2, L=24, d_model=12, H=2, d=4, seed=28):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, L, d_model))
+    w_qk = rng.standard_normal((H * d, d_model))
+    w_v = rng.standard_normal((H * d, d_model))
+    w_o = rng.standard_normal((d_model, H * d))
+    return x, w_qk, w_v, w_o
+
+
+def check_projections_brute_force():
+    """Both projections against Python loops over the definitions (non-square
+    weights, so a transposed operand fails)."""
+    H, d = 2, 4
+    x, w_qk, w_v, w_o = _layer_case(H=H, d=d)
+    B, L, dm = x.shape
+    qk, v = O.project_in(x, w_qk, w_v, H)
+    o = np.random.default_rng(29).standard_normal((B, H, L, d))
+    y = O.project_out(o, w_o)
+    for b in range(B):
+        for i in range(L):
+            for h in range(H):
+                for c in range(d):
+                    ref_q = sum(x[b, i, k] * w_qk[h * d + c, k] for k in range(dm))
+                    ref_v = sum(x[b, i, k] * w_v[h * d + c, k] for k in range(dm))
+                    assert abs(qk[b, h, i, c] - ref_q) < 1e-12 and abs(v[b, h, i, c] - ref_v) < 1e-12
+            for n in range(dm):
+                ref_y = sum(o[b, h, i, c] * w_o[n, h * d + c] for h in range(H) for c in range(d))
+                assert abs(y[b, i, n] - ref_y) < 1e-12
+
+
+def check_identity_layer(seed=30):
+    """With d_model = H*d and identity weights the layer is the four steps on the
+    input's head slices (built here with loops) and their outputs side by side."""
+    H, d, B, L = 2, 8, 1, 32
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, L, H * d))
+    eye = np.eye(H * d)
+    R = rng.standard_normal((3, d, 3))
+    out = O.layer_forward(x, eye, eye, eye, R, H, 6, 8, True)
+    heads = np.empty((B, H, L, d))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                heads[b, h, i] = x[b, i, h * d:(h + 1) * d]
+    ref = O.forward(heads, heads, R, 6, 8, True)
+    for b in range(B):
+        for i in range(L):
+            for h in range(H):
+                assert np.max(np.abs(out["y"][b, i, h * d:(h + 1) * d] - ref["o"][b, h, i])) < 1e-12
+
+
+def check_head_permutation(seed=31):
+    """Permuting the heads consistently in w_qk, w_v and w_o leaves the layer's
+    output unchanged (heads are attended independently with the shared R)."""
+    H, d = 3, 4
+    x, w_qk, w_v, w_o = _layer_case(B=1, L=32, d_model=10, H=H, d=d, seed=seed)
+    R = np.random.default_rng(seed + 1).standard_normal((2, d, 2))
+    perm = [2, 0, 1]
+    rows = np.concatenate([np.arange(h * d, (h + 1) * d) for h in perm])
+    a = O.layer_forward(x, w_qk, w_v, w_o, R, H, 4, 8, False)
+    b = O.layer_forward(x, w_qk[rows], w_v[rows], w_o[:, rows], R, H, 4, 8, False)
+    assert np.max(np.abs(a["y"] - b["y"])) < 1e-12
+
+
 ALL_CHECKS = {
     "hash_demo": check_hash_demo,
     "hash_labels": check_hash_labels,
@@ -333,4 +401,7 @@ ALL_CHECKS = {
                                                     chunk=4, L=32, seed=26),
     "rounds_without_correction_same_bucket": lambda: check_rounds_without_correction(
         same_bucket=True, nb=4, seed=27),
+    "projections_brute_force": check_projections_brute_force,
+    "identity_layer": check_identity_layer,
+    "head_permutation": check_head_permutation,
 }

@@ -155,6 +155,38 @@ def test_attn_chunk_support(lib):
     assert lib.lsh_chunk_attn(raw(c), NULL, NULL, NULL, NULL, NULL, NULL, NULL) == B.LSH_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("which", range(5))
+def test_project_in_pointer_checks(lib, which):
+    c = cfg()
+    args = [FAKE] * 5
+    args[which] = NULL
+    assert lib.lsh_project_in(raw(c), 512, *args, NULL) == B.LSH_ERR_INVALID_ARG
+    args[which] = MISALIGNED
+    assert lib.lsh_project_in(raw(c), 512, *args, NULL) == B.LSH_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", range(3))
+def test_project_out_pointer_checks(lib, which):
+    c = cfg()
+    args = [FAKE] * 3
+    args[which] = NULL
+    assert lib.lsh_project_out(raw(c), 512, *args, NULL) == B.LSH_ERR_INVALID_ARG
+
+
+def test_projection_config_checks(lib):
+    c = cfg()
+    for d_model in (0, -64, 96, 65600):
+        assert lib.lsh_project_in(raw(c), d_model, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
+        assert "d_model" in lib.lsh_last_error().decode()
+        assert lib.lsh_project_out(raw(c), d_model, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
+    c = cfg(dtype="f32")
+    assert lib.lsh_project_in(raw(c), 512, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_UNSUPPORTED
+    assert lib.lsh_project_out(raw(c), 512, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_UNSUPPORTED
+    c = cfg(batch=1 << 12, seq_len=1 << 20, chunk=128)      # B * L = 2^32
+    assert lib.lsh_project_in(raw(c), 512, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
+    assert "2^31" in lib.lsh_last_error().decode()
+
+
 def test_sort_workspace(lib):
     # tile = smallest power of two >= max(2048, 4 * n_buckets), at most 65536, at most L;
     # one int32 counter per (segment, tile, bucket)

@@ -130,6 +130,14 @@ def _bucket_mask_ignored(a, k):
 _WINDOW_CHUNKS_ORIG = O.window_chunks
 
 
+def _weights_read_as_in_out(x, w_qk, w_v, heads):
+    """The [out, in] weights' memory taken as [in, out] (a layout mix-up)."""
+    x = np.asarray(x, dtype=np.float64)
+    qk = x @ np.reshape(w_qk, (w_qk.shape[1], w_qk.shape[0]))
+    v = x @ np.reshape(w_v, (w_v.shape[1], w_v.shape[0]))
+    return O.split_heads(qk, heads), O.split_heads(v, heads)
+
+
 MUTATIONS = {
     "hash drops the negated half": ("bucket_from_projection", _argmax_positive_half_only, "hash_antipodal"),
     "hash takes argmin": ("bucket_from_projection", _argmin_labels, "hash_labels"),
@@ -153,6 +161,11 @@ MUTATIONS = {
     "correction applied when switched off": ("chunk_attention", "correction_always_on",
                                              "rounds_without_correction"),
     "same-bucket mask ignored": ("chunk_attention", "bucket_mask_ignored", "union_same_bucket"),
+    "heads split in the wrong order": ("split_heads",
+                                       lambda t, H: t.reshape(t.shape[0], t.shape[1], t.shape[2] // H, H)
+                                       .transpose(0, 3, 1, 2), "identity_layer"),
+    "projection weight read as [in, out]": ("project_in", _weights_read_as_in_out,
+                                            "projections_brute_force"),
     "buckets missing from the counts": ("duplicate_counts",
                                         lambda q, k, n=0, wrap=False, *b: _DUP_ORIG(q, k, n, wrap),
                                         "union_same_bucket"),
