@@ -170,6 +170,27 @@ lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v,
 lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
                               const float* lse, void* o, void* stream);
 
+/*
+ * Projections of the LSH-attention layer around steps 1-4 (bfloat16 only).
+ * [MOD] "LSH attention": queries and keys share one projection; [AIS]
+ * experiment set-up: d_model 1024 and 8 heads.  Weights are stored like a
+ * linear layer's, [out, in]; products accumulate in fp32; outputs are rounded to
+ * nearest even.
+ *   lsh_project_in:   qk[b,h,i,c] = sum_k x[b,i,k] * w_qk[h*d + c, k]
+ *                     v[b,h,i,c]  = sum_k x[b,i,k] * w_v[h*d + c, k]
+ *     x [B, L, d_model];  w_qk, w_v [H*d, d_model];  qk, v [B, H, L, d] out
+ *     (the layout steps 1-4 take).
+ *   lsh_project_out:  y[b,i,n] = sum_{h,c} o[b,h,i,c] * w_o[n, h*d + c]
+ *     o [B, H, L, d] (from lsh_combine_rounds);  w_o [d_model, H*d];
+ *     y [B, L, d_model] out.
+ * Errors as above, and: d_model not a positive multiple of 64 or above 65536,
+ * or B*L >= 2^31 (LSH_ERR_INVALID_ARG); dtype not LSH_BF16 (LSH_ERR_UNSUPPORTED).
+ */
+lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x, const void* w_qk,
+                          const void* w_v, void* qk, void* v, void* stream);
+lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o, const void* w_o,
+                           void* y, void* stream);
+
 /* Static description of a status code. */
 const char* lsh_status_string(lsh_status status);
 

@@ -8,6 +8,6 @@ package is its Python binding.  Build the library with
 from ._binding import (EXPORTED, LIB_PATH, LSH_BF16, LSH_ERR_HIP, LSH_ERR_INVALID_ARG,  # noqa: F401
                        LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_F32, LSH_FLAG_NO_DUP_CORRECTION,
                        LSH_FLAG_SAME_BUCKET, LSH_FLAG_WRAP_LOOKBACK, LSH_OK, CConfig,
-                       LSHConfig, LSHError, forward, load_library, lsh_chunk_attn,
-                       lsh_combine_rounds, lsh_hash, lsh_sort, lsh_sort_workspace_bytes,
-                       sort_workspace)
+                       LSHConfig, LSHError, forward, layer_forward, load_library, lsh_chunk_attn,
+                       lsh_combine_rounds, lsh_hash, lsh_project_in, lsh_project_out, lsh_sort,
+                       lsh_sort_workspace_bytes, sort_workspace)

@@ -26,7 +26,8 @@ LSH_F32, LSH_BF16 = 0, 1
 LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2, 4
 
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
-            "lsh_combine_rounds", "lsh_status_string", "lsh_last_error")
+            "lsh_combine_rounds", "lsh_project_in", "lsh_project_out", "lsh_status_string",
+            "lsh_last_error")
 
 
 class LSHError(RuntimeError):
@@ -92,7 +93,10 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_sort.argtypes = [CP, P, P, P, P, ctypes.c_size_t, P]
     lib.lsh_chunk_attn.argtypes = [CP, P, P, P, P, P, P, P]
     lib.lsh_combine_rounds.argtypes = [CP, P, P, P, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds"):
+    lib.lsh_project_in.argtypes = [CP, I32, P, P, P, P, P, P]
+    lib.lsh_project_out.argtypes = [CP, I32, P, P, P, P]
+    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_project_in",
+              "lsh_project_out"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
     lib.lsh_status_string.restype = ctypes.c_char_p
@@ -242,3 +246,59 @@ def forward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, R: torch.Tensor,
         return {"buckets": buckets, "perm": perm, "cid": cid, "o_rounds": o_rounds,
                 "lse": lse, "o": o}
     return o
+
+
+def lsh_project_in(cfg: LSHConfig, d_model: int, x: torch.Tensor, w_qk: torch.Tensor,
+                   w_v: torch.Tensor, qk: Optional[torch.Tensor] = None,
+                   v: Optional[torch.Tensor] = None, stream=None):
+    """Layer input projections: (qk, v), each [B, H, L, d] bf16, from x [B, L, d_model]
+    and the weights w_qk, w_v [H*d, d_model] (see lsh_project_in in the header)."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    B, L, hd = cfg.batch, cfg.seq_len, cfg.heads * cfg.d_head
+    _expect(x, "x", (B, L, d_model), cfg.torch_dtype)
+    dev = x.device
+    _expect(w_qk, "w_qk", (hd, d_model), cfg.torch_dtype, dev)
+    _expect(w_v, "w_v", (hd, d_model), cfg.torch_dtype, dev)
+    if qk is None:
+        qk = torch.empty(sh["qk"], dtype=cfg.torch_dtype, device=dev)
+    if v is None:
+        v = torch.empty(sh["v"], dtype=cfg.torch_dtype, device=dev)
+    _expect(qk, "qk", sh["qk"], cfg.torch_dtype, dev)
+    _expect(v, "v", sh["v"], cfg.torch_dtype, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_project_in(ctypes.byref(c), int(d_model), _ptr(x), _ptr(w_qk), _ptr(w_v),
+                              _ptr(qk), _ptr(v), _stream(dev, stream)), "lsh_project_in")
+    return qk, v
+
+
+def lsh_project_out(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torch.Tensor,
+                    y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Layer output projection: y [B, L, d_model] bf16 from o [B, H, L, d] and
+    w_o [d_model, H*d] (see lsh_project_out in the header)."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(o, "o", sh["o"], cfg.torch_dtype)
+    dev = o.device
+    _expect(w_o, "w_o", (d_model, cfg.heads * cfg.d_head), cfg.torch_dtype, dev)
+    if y is None:
+        y = torch.empty((cfg.batch, cfg.seq_len, d_model), dtype=cfg.torch_dtype, device=dev)
+    _expect(y, "y", (cfg.batch, cfg.seq_len, d_model), cfg.torch_dtype, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_project_out(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(y),
+                               _stream(dev, stream)), "lsh_project_out")
+    return y
+
+
+def layer_forward(cfg: LSHConfig, x: torch.Tensor, w_qk: torch.Tensor, w_v: torch.Tensor,
+                  w_o: torch.Tensor, R: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                  stream=None, return_all: bool = False):
+    """The LSH-attention layer: projections in, the four steps, projection out.
+    Returns y [B, L, d_model] (or a dict with every intermediate)."""
+    d_model = x.shape[-1]
+    qk, v = lsh_project_in(cfg, d_model, x, w_qk, w_v, stream=stream)
+    out = forward(cfg, qk, v, R, workspace=workspace, stream=stream, return_all=True)
+    y = lsh_project_out(cfg, d_model, out["o"], w_o, stream=stream)
+    if return_all:
+        return dict(out, qk=qk, v=v, y=y)
+    return y

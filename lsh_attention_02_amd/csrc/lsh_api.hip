@@ -100,6 +100,19 @@ lsh_status hip_status(hipError_t e, const char* what)
         if (_s != LSH_OK) return _s;           \
     } while (0)
 
+lsh_status check_layer(const lsh_config* cfg, int32_t d_model)
+{
+    LSH_TRY(check_config(cfg));
+    if (d_model <= 0 || d_model % 64 || d_model > 65536)
+        return fail(LSH_ERR_INVALID_ARG, "d_model must be a positive multiple of 64, at most 65536");
+    if ((long long)cfg->batch * cfg->seq_len >= (1LL << 31))
+        return fail(LSH_ERR_INVALID_ARG, "batch * seq_len must be below 2^31");
+    if (checked_product({cfg->batch, cfg->seq_len, d_model, 2}) < 0)
+        return fail(LSH_ERR_INVALID_ARG, "a buffer would exceed 2^62 bytes");
+    if (cfg->dtype != LSH_BF16) return fail(LSH_ERR_UNSUPPORTED, "the projections support LSH_BF16 only");
+    return LSH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +208,34 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds, const
                                            cfg->seq_len, cfg->n_rounds,
                                            static_cast<hipStream_t>(stream)),
                       "lsh_combine_rounds");
+}
+
+lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x, const void* w_qk,
+                          const void* w_v, void* qk, void* v, void* stream)
+{
+    LSH_TRY(check_layer(cfg, d_model));
+    LSH_TRY(check_ptr(x, "x"));
+    LSH_TRY(check_ptr(w_qk, "w_qk"));
+    LSH_TRY(check_ptr(w_v, "w_v"));
+    LSH_TRY(check_ptr(qk, "qk"));
+    LSH_TRY(check_ptr(v, "v"));
+    return hip_status(lshk::launch_project_in(x, w_qk, w_v, qk, v, (long)cfg->batch * cfg->seq_len,
+                                              cfg->seq_len, cfg->heads, cfg->d_head, d_model,
+                                              static_cast<hipStream_t>(stream)),
+                      "lsh_project_in");
+}
+
+lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o, const void* w_o,
+                           void* y, void* stream)
+{
+    LSH_TRY(check_layer(cfg, d_model));
+    LSH_TRY(check_ptr(o, "o"));
+    LSH_TRY(check_ptr(w_o, "w_o"));
+    LSH_TRY(check_ptr(y, "y"));
+    return hip_status(lshk::launch_project_out(o, w_o, y, (long)cfg->batch * cfg->seq_len,
+                                               cfg->seq_len, cfg->heads, cfg->d_head, d_model,
+                                               static_cast<hipStream_t>(stream)),
+                      "lsh_project_out");
 }
 
 }  // extern "C"

@@ -47,4 +47,10 @@ hipError_t launch_f32_d128(LSH_ATTN_LAUNCH_ARGS);
 hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
                           long bh, int L, int n_rounds, hipStream_t stream);
 
+// Layer projections (bf16): rows = B * L; H heads of size D; d_model a multiple of 64.
+hipError_t launch_project_in(const void* x, const void* w_qk, const void* w_v, void* qk, void* v,
+                             long rows, int L, int H, int D, int d_model, hipStream_t stream);
+hipError_t launch_project_out(const void* o, const void* w_o, void* y, long rows, int L, int H,
+                              int D, int d_model, hipStream_t stream);
+
 }  // namespace lshk

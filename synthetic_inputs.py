@@ -143,3 +143,21 @@ def make_inputs(w: Workload, seed: int | None = None) -> Dict[str, np.ndarray]:
     v = _normal(rng, (B, H, L, d))
     R = _normal(rng, (w.n_rounds, d, w.n_buckets // 2))
     return {"qk": _storage(qk, w.dtype), "v": _storage(v, w.dtype), "R": _storage(R, w.dtype)}
+
+
+def make_layer_inputs(w: Workload, d_model: int, seed: int | None = None) -> Dict[str, np.ndarray]:
+    """Draw the inputs of the attention layer around workload ``w``:
+    x [B, L, d_model] ~ N(0, 1); the weights w_qk, w_v [H*d, d_model] and
+    w_o [d_model, H*d] ~ N(0, 1/fan_in), so that the projections keep unit
+    scale; R as in make_inputs.  Drawn in that order from PCG64(seed, default
+    the workload's seed + 1000), rounded to ``w.dtype``; float32 arrays."""
+    rng = np.random.Generator(np.random.PCG64((w.seed + 1000) if seed is None else seed))
+    B, H, L, d = w.batch, w.heads, w.seq_len, w.d_head
+    hd = H * d
+    x = _normal(rng, (B, L, d_model))
+    w_qk = _normal(rng, (hd, d_model)) * np.float32(1.0 / np.sqrt(d_model))
+    w_v = _normal(rng, (hd, d_model)) * np.float32(1.0 / np.sqrt(d_model))
+    w_o = _normal(rng, (d_model, hd)) * np.float32(1.0 / np.sqrt(hd))
+    R = _normal(rng, (w.n_rounds, d, w.n_buckets // 2))
+    return {k: _storage(a, w.dtype) for k, a in
+            (("x", x), ("w_qk", w_qk), ("w_v", w_v), ("w_o", w_o), ("R", R))}

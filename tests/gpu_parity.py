@@ -29,7 +29,7 @@ import torch
 
 import lsh_attention_02_amd as lsh
 import oracle.lsh_oracle as O
-from synthetic_inputs import Workload, make_inputs
+from synthetic_inputs import Workload, make_inputs, make_layer_inputs
 
 GATE = {"f32": 1e-5, "bf16": 2e-2}
 LSE_ATOL = {"f32": 2e-5, "bf16": 1e-3}
@@ -242,4 +242,34 @@ def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int
     assert rep["combine_err"] <= GATE[w.dtype], (w.name, "combine", rep["combine_err"])
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[sampled] {rep}")
+    return rep
+
+
+# --------------------------------------------------------------------------- the layer
+GATE_PROJ = 1e-2     # bf16 outputs of fp32-accumulated products: rounding 2^-9 relative
+
+
+def layer_parity(w: Workload, d_model: int, flags: int = 0) -> dict:
+    """Layered: the GPU's projections against the oracle's on the same bf16
+    inputs; the four steps on the GPU's qk and v (as in full_parity); the
+    output projection of the GPU's o."""
+    t0 = time.time()
+    x = make_layer_inputs(w, d_model)
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous() for k, a in x.items()}
+    cfg = cfg_of(w, flags=flags)
+    g = lsh.layer_forward(cfg, t["x"], t["w_qk"], t["w_v"], t["w_o"], t["R"], return_all=True)
+    torch.cuda.synchronize()
+    rep = {"workload": w.name, "d_model": d_model, "flags": flags}
+    qk_ref, v_ref = O.project_in(x["x"], x["w_qk"], x["w_v"], w.heads)
+    rep["qk_err"] = rel_err(to_np(g["qk"]), qk_ref)
+    rep["v_err"] = rel_err(to_np(g["v"]), v_ref)
+    assert rep["qk_err"] <= GATE_PROJ and rep["v_err"] <= GATE_PROJ, rep
+    core = full_parity(w, x={"qk": to_np(g["qk"]), "v": to_np(g["v"]), "R": x["R"]}, flags=flags)
+    rep["core_o_rounds_err"] = core["o_rounds_err"]
+    y_ref = O.project_out(to_np(g["o"]).astype(np.float64), x["w_o"])
+    rep["y_err"] = rel_err(to_np(g["y"]), y_ref)
+    assert rep["y_err"] <= GATE_PROJ, rep
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[layer] {rep}")
     return rep

@@ -102,6 +102,30 @@ def test_full_size_sampled_variants(flags):
     GP.sampled_parity(WORKLOADS["paper_64k"], n_samples=512, flags=flags)
 
 
+# The attention layer (projections around the four steps).  Ragged: 1344 rows
+# and 192 output columns are not multiples of the 128 x 128 GEMM tile.
+LAYER_CASES = {
+    "b2_L512_dm256_h4_d64": (W("layer_a", batch=2, heads=4, seq_len=512, n_buckets=16, seed=140), 256),
+    "L1024_dm512_h4_d128": (W("layer_b", heads=4, seq_len=1024, d_head=128, n_buckets=32,
+                               n_rounds=4, seed=141), 512),
+    "ragged_L1344_dm192_h3": (W("layer_c", heads=3, seq_len=1344, n_buckets=10, n_rounds=3,
+                                causal=False, seed=142), 192),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_CASES))
+def test_layer_parity(name):
+    w, d_model = LAYER_CASES[name]
+    GP.layer_parity(w, d_model)
+
+
+def test_layer_parity_paper_shape_same_bucket():
+    """d_model 1024 and 8 heads of 128, as the pages' set-up, at L = 2048, with the
+    same-bucket variant."""
+    w = W("layer_paper", heads=8, seq_len=2048, d_head=128, n_buckets=64, n_rounds=4, seed=143)
+    GP.layer_parity(w, 1024, flags=lsh.LSH_FLAG_SAME_BUCKET)
+
+
 def test_native_library_is_loaded():
     lsh.load_library()
     with open("/proc/self/maps") as f:
