@@ -16,10 +16,10 @@
 //
 // Workgroup tile 128 x 128, K step 64, 4 waves of 64 x 64 (2 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16).  Both operand tiles are row-major in LDS with the
-// eight 16-byte pieces of each 128-byte row XOR-swizzled by (row & 7), so the
-// MFMA operand reads (8 rows, one piece) and the row stores are free of bank
-// conflicts.  The next K step is loaded into registers while the current one is
-// multiplied (two LDS buffers, one barrier per step).
+// eight 16-byte pieces of each 128-byte row XOR-swizzled by row, so the MFMA
+// operand reads (16 rows, one piece) and the row stores are free of bank
+// conflicts.  The next two K steps are loaded into registers while the current
+// one is multiplied (two register sets, two LDS buffers, one barrier per step).
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
@@ -37,34 +37,57 @@ enum { OUT_ROWS = 0, OUT_HEADS = 1 };
 struct LinShape {
     int M, N, K;        // y [M, N] = x [M, K] * w[N, K]^T
     int L, H, D;        // sequence length, heads, head size (head-major addressing)
+    int mt, nt;         // tiles along M and N
+    int nmat;           // matrices (2: the qk and v projections share one launch)
+    int per_xcd;        // tiles per XCD (see the tile mapping in k_linear)
 };
 
-// Address of the 8 input elements x[m, k .. k+7] (k a multiple of 8, inside one head).
-template <int IN>
-__device__ __forceinline__ const bf16_t* in_ptr(const bf16_t* x, const LinShape& s, int m, int k)
+constexpr int NXCD = 8;
+
+// Row m = b*L + i of a tile whose first row m0 = b0*L + i0: (b, i) by carrying
+// from (b0, i0), so the division by L happens once per tile.
+struct RowPos { int b, i; };
+
+__device__ __forceinline__ RowPos row_pos(RowPos base, int r, int L)
+{
+    RowPos p{base.b, base.i + r};
+    while (p.i >= L) { p.i -= L; ++p.b; }        // at most 128 / L steps
+    return p;
+}
+
+// Address of the 8 input elements x[m, k .. k+7] (k a multiple of 8, inside one
+// head of D elements).
+template <int IN, int D>
+__device__ __forceinline__ const bf16_t* in_ptr(const bf16_t* x, const LinShape& s, int m,
+                                                RowPos p, int k)
 {
     if constexpr (IN == IN_ROWS) {
         return x + (long)m * s.K + k;
     } else {
-        const int b = m / s.L, i = m % s.L, h = k / s.D, c = k % s.D;
-        return x + (((long)b * s.H + h) * s.L + i) * s.D + c;
+        const int h = k / D, c = k % D;
+        return x + (((long)p.b * s.H + h) * s.L + p.i) * D + c;
     }
 }
 
-template <int OUT>
-__device__ __forceinline__ long out_index(const LinShape& s, int m, int n)
+template <int OUT, int D>
+__device__ __forceinline__ long out_index(const LinShape& s, int m, RowPos p, int n)
 {
     if constexpr (OUT == OUT_ROWS) {
         return (long)m * s.N + n;
     } else {
-        const int b = m / s.L, i = m % s.L, h = n / s.D, c = n % s.D;
-        return (((long)b * s.H + h) * s.L + i) * s.D + c;
+        const int h = n / D, c = n % D;
+        return (((long)p.b * s.H + h) * s.L + p.i) * D + c;
     }
 }
 
-__device__ __forceinline__ int lin_swz(int row, int piece) { return piece ^ (row & 7); }
+// The LDS has 64 banks of 4 bytes and serves a 16-byte read for 16 lanes per
+// clock.  An operand read takes one 16-byte piece of 16 consecutive rows: rows
+// alternate between the two 32-bank halves (a row is 128 bytes), and XOR with
+// (row / 2) % 8 gives the 8 rows of each half 8 different pieces.  The row
+// stores (8 lanes cover one row) stay conflict-free under any permutation.
+__device__ __forceinline__ int lin_swz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
-template <int IN, int OUT>
+template <int IN, int OUT, int D>
 __global__ __launch_bounds__(LIN_THREADS)
 void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
               const bf16_t* __restrict__ w1, bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
@@ -73,29 +96,53 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
     __shared__ __attribute__((aligned(16))) bf16_t sa[2][LIN_BM * LIN_BK];
     __shared__ __attribute__((aligned(16))) bf16_t sw[2][LIN_BN * LIN_BK];
 
-    const bf16_t* __restrict__ w = blockIdx.z ? w1 : w0;
-    bf16_t* __restrict__ y = blockIdx.z ? y1 : y0;
+    // Workgroups are dispatched to the 8 XCDs round-robin by launch index, and
+    // each XCD has its own L2.  Each XCD takes a contiguous run of tiles in
+    // (matrix, row tile, column tile) order, so the column tiles that share an
+    // input row tile run on one XCD and read it from its L2.
+    const int t = (blockIdx.x % NXCD) * s.per_xcd + blockIdx.x / NXCD;
+    if (t >= s.nmat * s.mt * s.nt) return;            // padding of the last XCD's run
+    const int z = t / (s.mt * s.nt), tm = (t / s.nt) % s.mt, tn = t % s.nt;
+    const bf16_t* __restrict__ w = z ? w1 : w0;
+    bf16_t* __restrict__ y = z ? y1 : y0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m0 = blockIdx.y * LIN_BM, n0 = blockIdx.x * LIN_BN;
+    const int m0 = tm * LIN_BM, n0 = tn * LIN_BN;
+    const RowPos base{m0 / s.L, m0 % s.L};
 
-    // operand loads: piece p = tid + 256*i covers row p / 8, 16-byte piece p % 8
-    u32x4 ra[LIN_LOADS], rw[LIN_LOADS];
-    auto load = [&](int k0) {
+    // Operand loads: piece p = tid + 256*i covers row p / 8, 16-byte piece p % 8.
+    // Rows past M or N repeat the last row: they only reach outputs that are not
+    // stored.
+    // Two register sets hold K steps kt+1 and kt+2 while step kt is multiplied,
+    // so a load has two steps of math to arrive.  Loads past the last step
+    // repeat the last step (in bounds, never stored): the loop body has no
+    // branches, which lets the compiler wait for exactly the older set.
+    u32x4 ra[2][LIN_LOADS], rw[2][LIN_LOADS];
+    const int nk = s.K / LIN_BK;
+    RowPos lrow[LIN_LOADS];                           // (b, i) of each load's row (head-major input)
+    int lm[LIN_LOADS], ln[LIN_LOADS];
+#pragma unroll
+    for (int i = 0; i < LIN_LOADS; ++i) {
+        const int row = (tid + LIN_THREADS * i) / LIN_PIECES;
+        lm[i] = min(m0 + row, s.M - 1);
+        ln[i] = min(n0 + row, s.N - 1);
+        lrow[i] = row_pos(base, lm[i] - m0, s.L);
+    }
+    auto load = [&](int set, int kt) {
+        const int k0 = min(kt, nk - 1) * LIN_BK;
 #pragma unroll
         for (int i = 0; i < LIN_LOADS; ++i) {
-            const int p = tid + LIN_THREADS * i, row = p / LIN_PIECES, piece = p % LIN_PIECES;
-            const int m = m0 + row, n = n0 + row, k = k0 + 8 * piece;
-            ra[i] = m < s.M ? *reinterpret_cast<const u32x4*>(in_ptr<IN>(x, s, m, k)) : u32x4{};
-            rw[i] = n < s.N ? *reinterpret_cast<const u32x4*>(w + (long)n * s.K + k) : u32x4{};
+            const int k = k0 + 8 * ((tid + LIN_THREADS * i) % LIN_PIECES);
+            ra[set][i] = *reinterpret_cast<const u32x4*>(in_ptr<IN, D>(x, s, lm[i], lrow[i], k));
+            rw[set][i] = *reinterpret_cast<const u32x4*>(w + (long)ln[i] * s.K + k);
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int set, int buf) {
 #pragma unroll
         for (int i = 0; i < LIN_LOADS; ++i) {
             const int p = tid + LIN_THREADS * i, row = p / LIN_PIECES, piece = p % LIN_PIECES;
             const int off = row * LIN_BK + 8 * lin_swz(row, piece);
-            *reinterpret_cast<u32x4*>(&sa[buf][off]) = ra[i];
-            *reinterpret_cast<u32x4*>(&sw[buf][off]) = rw[i];
+            *reinterpret_cast<u32x4*>(&sa[buf][off]) = ra[set][i];
+            *reinterpret_cast<u32x4*>(&sw[buf][off]) = rw[set][i];
         }
     };
 
@@ -107,55 +154,101 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-    const int nk = s.K / LIN_BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load((kt + 1) * LIN_BK);
+    // The MFMA computes the transposed tile, D[n][m] (weights as the row
+    // operand): lane (r32, kh) then holds, for each group of four registers,
+    // four consecutive output columns of one row, stored with one 8-byte write.
+    // The fragments of sub-step ks+1 are read while sub-step ks multiplies: the
+    // group barriers ask the scheduler for one LDS read after each MFMA (left to
+    // itself it waits for each sub-step's reads before its first MFMA).
+    auto read_frags = [&](int buf, int ks, bf16x8 (&fa)[2], bf16x8 (&fw)[2]) {
+        const int piece = 2 * ks + kh;                // k = 16 ks + 8 kh .. +8
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ra_row = 64 * wm + 32 * t + r32, rw_row = 64 * wn + 32 * t + r32;
+            fa[t] = *reinterpret_cast<const bf16x8*>(&sa[buf][ra_row * LIN_BK + 8 * lin_swz(ra_row, piece)]);
+            fw[t] = *reinterpret_cast<const bf16x8*>(&sw[buf][rw_row * LIN_BK + 8 * lin_swz(rw_row, piece)]);
+        }
+    };
+    auto multiply = [&](int buf) {
+        bf16x8 fa[2][2], fw[2][2];
+        read_frags(buf, 0, fa[0], fw[0]);
 #pragma unroll
         for (int ks = 0; ks < LIN_BK / 16; ++ks) {
-            const int piece = 2 * ks + kh;            // k = 16 ks + 8 kh .. +8
-            bf16x8 fa[2], fw[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int ra_row = 64 * wm + 32 * t + r32, rw_row = 64 * wn + 32 * t + r32;
-                fa[t] = *reinterpret_cast<const bf16x8*>(&sa[buf][ra_row * LIN_BK + 8 * lin_swz(ra_row, piece)]);
-                fw[t] = *reinterpret_cast<const bf16x8*>(&sw[buf][rw_row * LIN_BK + 8 * lin_swz(rw_row, piece)]);
-            }
+            if (ks + 1 < LIN_BK / 16) read_frags(buf, ks + 1, fa[(ks + 1) & 1], fw[(ks + 1) & 1]);
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fw[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[ks & 1][b], fa[ks & 1][a],
+                                                                       acc[a][b], 0, 0, 0);
         }
-        if (kt + 1 < nk) store(buf ^ 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < LIN_BK / 16 - 1; ++ks) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+
+    // Set kt % 2 holds step kt; LDS buffer kt % 2 holds step kt while it is
+    // multiplied.  The scheduling barriers keep each load group at the top of
+    // its step (the compiler would otherwise sink the loads towards their LDS
+    // stores, which exposes the memory latency).
+    load(0, 0);
+    load(1, 1);
+    store(0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+        load(0, kt + 2);              // set 0 held step kt, already in LDS buffer 0
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(0);
+        store(1, 1);                  // step kt+1
+        __syncthreads();
+        load(1, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(1);
+        store(0, 0);                  // step kt+2 (a repeat past the end, unused)
         __syncthreads();
     }
+    if (kt < nk) multiply(0);         // odd step count: the last step is in buffer 0
 
-    // D element j of tile (a, b): row 32a + 8(j/4) + 4 kh + (j%4), column 32b + r32
+    // D element j of tile (a, b): column n = 32b + 8(j/4) + 4 kh + (j%4), row m = 32a + r32
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
+        const int r = 64 * wm + 32 * a + r32, m = m0 + r;
+        const RowPos p = row_pos(base, r, s.L);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int n = n0 + 64 * wn + 32 * b + r32;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int m = m0 + 64 * wm + 32 * a + 8 * (j >> 2) + 4 * kh + (j & 3);
-                if (m < s.M && n < s.N) y[out_index<OUT>(s, m, n)] = from_f32<bf16_t>(acc[a][b][j]);
+            for (int jg = 0; jg < 4; ++jg) {
+                const int n = n0 + 64 * wn + 32 * b + 8 * jg + 4 * kh;   // N is a multiple of 4
+                if (m < s.M && n < s.N) {
+                    const f32x16& c = acc[a][b];
+                    const u32x2 v = {pack_bf16x2(c[4 * jg], c[4 * jg + 1]),
+                                     pack_bf16x2(c[4 * jg + 2], c[4 * jg + 3])};
+                    *reinterpret_cast<u32x2*>(y + out_index<OUT, D>(s, m, p, n)) = v;
+                }
             }
         }
     }
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, int D>
 hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void* y1, int nmat,
-                  const LinShape& s, hipStream_t st)
+                  LinShape s, hipStream_t st)
 {
-    const dim3 grid((unsigned)((s.N + LIN_BN - 1) / LIN_BN), (unsigned)((s.M + LIN_BM - 1) / LIN_BM),
-                    (unsigned)nmat);
-    hipLaunchKernelGGL((k_linear<IN, OUT>), grid, dim3(LIN_THREADS), 0, st,
+    s.mt = (s.M + LIN_BM - 1) / LIN_BM;
+    s.nt = (s.N + LIN_BN - 1) / LIN_BN;
+    s.nmat = nmat;
+    const long tiles = (long)nmat * s.mt * s.nt;
+    s.per_xcd = (int)((tiles + NXCD - 1) / NXCD);
+    const dim3 grid((unsigned)((long)s.per_xcd * NXCD));
+    hipLaunchKernelGGL((k_linear<IN, OUT, D>), grid, dim3(LIN_THREADS), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w0),
                        static_cast<const bf16_t*>(w1), static_cast<bf16_t*>(y0),
                        static_cast<bf16_t*>(y1), s);
@@ -167,15 +260,17 @@ hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void*
 hipError_t launch_project_in(const void* x, const void* w_qk, const void* w_v, void* qk, void* v,
                              long rows, int L, int H, int D, int d_model, hipStream_t stream)
 {
-    const LinShape s{(int)rows, H * D, d_model, L, H, D};
-    return launch<IN_ROWS, OUT_HEADS>(x, w_qk, w_v, qk, v, 2, s, stream);
+    const LinShape s{(int)rows, H * D, d_model, L, H, D, 0, 0, 0, 0};
+    return D == 64 ? launch<IN_ROWS, OUT_HEADS, 64>(x, w_qk, w_v, qk, v, 2, s, stream)
+                   : launch<IN_ROWS, OUT_HEADS, 128>(x, w_qk, w_v, qk, v, 2, s, stream);
 }
 
 hipError_t launch_project_out(const void* o, const void* w_o, void* y, long rows, int L, int H,
                               int D, int d_model, hipStream_t stream)
 {
-    const LinShape s{(int)rows, d_model, H * D, L, H, D};
-    return launch<IN_HEADS, OUT_ROWS>(o, w_o, w_o, y, y, 1, s, stream);
+    const LinShape s{(int)rows, d_model, H * D, L, H, D, 0, 0, 0, 0};
+    return D == 64 ? launch<IN_HEADS, OUT_ROWS, 64>(o, w_o, w_o, y, y, 1, s, stream)
+                   : launch<IN_HEADS, OUT_ROWS, 128>(o, w_o, w_o, y, y, 1, s, stream);
 }
 
 }  // namespace lshk
