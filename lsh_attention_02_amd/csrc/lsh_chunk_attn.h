@@ -134,9 +134,29 @@ __device__ __forceinline__ int vt_swz(int d)
     return (d ^ (d >> 3)) & (C / 4 - 1);
 }
 
+// qk rows in LDS.  A 16-byte LDS access is served in four passes of 16 lanes;
+// in each half-wave, lane quads (lane / 4) of even and of odd bit parity form the
+// two passes.  The layouts below keep both the row stores (lane = piece of 4-row
+// groups) and the MFMA operand reads (lane = row r16 + 16 * piece group) free of
+// bank conflicts under that grouping:
+//   bf16, d 128: unpadded 256-byte rows, 16-byte piece p of row r stored at
+//                p ^ (r ^ ((r & 4) << 1)) mod 16;
+//   bf16, d 64:  rows padded to 160 bytes, no swizzle;
+//   f32:         rows padded by 16 bytes (4-byte operand reads).
+template <typename T, int D>
+struct KLayout {
+    static constexpr bool SWZ = sizeof(T) == 2 && D == 128;
+    static constexpr int ROW = sizeof(T) == 4 ? D + 4 : (D == 128 ? D : D + 16);
+    // element e (a multiple of the 16-byte piece or of the operand width) of row r
+    static __device__ __forceinline__ int off(int r, int e) {
+        if constexpr (SWZ) return r * ROW + 8 * ((e >> 3) ^ ((r ^ ((r & 4) << 1)) & 15)) + (e & 7);
+        else return r * ROW + e;
+    }
+};
+
 template <typename T, int D, int C, int NDW>
 struct Lds {
-    static constexpr int KROW = D + 16 / (int)sizeof(T);   // qk row, padded by 16 bytes
+    static constexpr int KROW = KLayout<T, D>::ROW;        // qk row (elements)
     static constexpr int VROWB = C * (int)sizeof(T);        // v^T row bytes (one slot's keys)
     // -log2(n_rounds - o) at byte offset 8*o, o = rounds outside (at most 16):
     // the popcount sum 8*o addresses it directly (first member: offset 0)
@@ -162,9 +182,10 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 {
     using M = Mfma16<T>;
     using S = Lds<T, D, C, NDW>;
+    using KL = KLayout<T, D>;
     constexpr int NTH = 4 * C;                         // C/16 waves of 16 queries
     constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
-    constexpr int KROW = S::KROW, VROWB = S::VROWB;
+    constexpr int VROWB = S::VROWB;
     constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
     constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
     constexpr int EB = (int)sizeof(T);
@@ -248,7 +269,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 const int rg = job / VPR, piece = job % VPR;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<u32x4*>(&sm.k[sl][(4 * rg + i) * KROW + piece * VE]) = kreg[jb][i];
+                    *reinterpret_cast<u32x4*>(&sm.k[sl][KL::off(4 * rg + i, piece * VE)]) = kreg[jb][i];
                 // transpose the 4 rows x VE elements: element x of every row gives
                 // the 4 keys 4rg..4rg+3 of v^T row d = piece*VE + x
 #pragma unroll
@@ -312,7 +333,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             typename M::Frag bq[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                bq[ks] = M::load(&sm.k[cur][qrow * KROW + ks * KSTEP + g * KPL]);
+                bq[ks] = M::load(&sm.k[cur][KL::off(qrow, ks * KSTEP + g * KPL)]);
             uint32_t q1[NW];           // query chunk ids minus one, per half
 #pragma unroll
             for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[cur][qrow * NDW + w], ones);
@@ -326,9 +347,10 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 s[t] = f32x4{};
                 if (t < CT && !has_prev) continue;
                 const int slk = t < CT ? prv : cur;
-                const T* kr = &sm.k[slk][((t % CT) * 16 + r16) * KROW + g * KPL];
+                const int krow = (t % CT) * 16 + r16;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) s[t] = M::mma(M::load(kr + ks * KSTEP), bq[ks], s[t]);
+                for (int ks = 0; ks < NKS; ++ks)
+                    s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, ks * KSTEP + g * KPL)]), bq[ks], s[t]);
             }
 
             // ---- scale and duplicate counts; self penalty on the diagonal tile;
