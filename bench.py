@@ -13,6 +13,9 @@ one (batch row, head) of the same workload on this host, scaled to the whole
 workload.
 
 Other modes:
+    --layer D_MODEL      time the attention layer instead: the shared-QK and value
+                         projections of x [B, L, D_MODEL], the four calls and the
+                         output projection (a second workload; no CPU baseline)
     --copy-calibration   run only a plain 1 GiB device copy (for scaling the
                          FETCH_SIZE / WRITE_SIZE counters)
     --pmc-summary F W CF CW   turn four rocprofv3 --pmc output folders (FETCH_SIZE
@@ -44,13 +47,17 @@ KERNEL_SOURCES = {
                        "lsh_chunk_attn_bf16_d128.hip", "lsh_chunk_attn_f32_d64.hip",
                        "lsh_chunk_attn_f32_d128.hip", "lsh_device.h"],
     "lsh_combine_rounds": ["lsh_combine.hip", "lsh_device.h"],
+    "lsh_project_in": ["lsh_linear.hip", "lsh_device.h"],
+    "lsh_project_out": ["lsh_linear.hip", "lsh_device.h"],
 }
 KERNEL_SYMBOLS = {"lsh_hash": "k_hash", "lsh_sort": "k_sort_*", "lsh_chunk_attn": "k_chunk_attn",
-                  "lsh_combine_rounds": "k_combine"}
+                  "lsh_combine_rounds": "k_combine", "lsh_project_in": "k_linear",
+                  "lsh_project_out": "k_linear"}
+LAYER_METRIC = "LSH-attention layer fwd tokens/s (projections + the four calls)"
 PMC_TRAFFIC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
-def algorithmic_work(w):
+def algorithmic_work(w, d_model=None):
     """Algorithmic FLOPs and HBM bytes per launch of each call.
 
     TR = token-head-rounds, T = token-heads, e = bytes per element.
@@ -60,12 +67,15 @@ def algorithmic_work(w):
                and v rows once and writes the o_rounds row (3*d*e), reads perm (4),
                writes lse (4), reads the cid row (2*n_r) per TR
       combine  reads n_r rows and lse values, writes one row: n_r*(d*e+4) + d*e per T
+      project_in   2*(2*H*d)*d_model FLOP per token; reads x and both weights once,
+                   writes qk and v
+      project_out  2*d_model*H*d FLOP per token; reads o and w_o, writes y
     """
     e = 2 if w.dtype == "bf16" else 4
     T = w.batch * w.heads * w.seq_len
     TR = T * w.n_rounds
     d, nb = w.d_head, w.n_buckets
-    return {
+    work = {
         "lsh_hash": {"flops": 2.0 * d * (nb // 2) * TR,
                      "bytes": T * d * e + w.n_rounds * d * (nb // 2) * e + 4.0 * TR},
         "lsh_sort": {"flops": 0.0, "bytes": 10.0 * TR},
@@ -74,16 +84,24 @@ def algorithmic_work(w):
         "lsh_combine_rounds": {"flops": 0.0,
                                "bytes": T * (w.n_rounds * (d * e + 4.0) + d * e)},
     }
+    if d_model:
+        M, hd = w.batch * w.seq_len, w.heads * d
+        work["lsh_project_in"] = {"flops": 2.0 * M * 2 * hd * d_model,
+                                  "bytes": e * (M * d_model + 2.0 * hd * d_model + 2.0 * M * hd)}
+        work["lsh_project_out"] = {"flops": 2.0 * M * d_model * hd,
+                                   "bytes": e * (M * hd + d_model * hd + 1.0 * M * d_model)}
+    return work
 
 
 def bound_of(name, w):
-    """Binding roofline of each call at the benchmark sizes: the hash is a dense
-    contraction (thousands of FLOP per byte), the other three stream memory."""
-    return "mfma" if name == "lsh_hash" else "hbm"
+    """Binding roofline of each call at the benchmark sizes: the hash and the
+    projections are dense contractions (hundreds to thousands of FLOP per byte),
+    the other three stream memory."""
+    return "mfma" if name in ("lsh_hash", "lsh_project_in", "lsh_project_out") else "hbm"
 
 
-def roofline_entry(name, w, ms):
-    work = algorithmic_work(w)[name]
+def roofline_entry(name, w, ms, d_model=None):
+    work = algorithmic_work(w, d_model)[name]
     if bound_of(name, w) == "mfma":
         ach = work["flops"] / (ms * 1e-3) / 1e12
         peak = PEAK_MFMA_TFLOPS[w.dtype]
@@ -243,6 +261,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
+                    help="time the attention layer (projections included) at this model width")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -271,18 +291,26 @@ def main():
     import torch
 
     import lsh_attention_02_amd as lsh
-    from synthetic_inputs import WORKLOADS, make_inputs
+    from synthetic_inputs import WORKLOADS, make_inputs, make_layer_inputs
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    x = make_inputs(w)
+    dm = args.layer
+    x = make_layer_inputs(w, dm) if dm else make_inputs(w)
     cfg = lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
                         w.causal, dtype=w.dtype, flags=args.flags)
     tdt = cfg.torch_dtype
-    qk = torch.from_numpy(x["qk"]).to(dev).to(tdt)
-    v = torch.from_numpy(x["v"]).to(dev).to(tdt)
-    R = torch.from_numpy(x["R"]).to(dev).to(tdt)
     B, H, L, d, nr = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
+    if dm:
+        xin = torch.from_numpy(x["x"]).to(dev).to(tdt)
+        wts = [torch.from_numpy(x[k]).to(dev).to(tdt) for k in ("w_qk", "w_v", "w_o")]
+        qk = torch.empty((B, H, L, d), dtype=tdt, device=dev)
+        v = torch.empty((B, H, L, d), dtype=tdt, device=dev)
+        y = torch.empty((B, L, dm), dtype=tdt, device=dev)
+    else:
+        qk = torch.from_numpy(x["qk"]).to(dev).to(tdt)
+        v = torch.from_numpy(x["v"]).to(dev).to(tdt)
+    R = torch.from_numpy(x["R"]).to(dev).to(tdt)
     buckets = torch.empty((B, H, nr, L), dtype=torch.int32, device=dev)
     perm = torch.empty((B, H, nr, L), dtype=torch.int32, device=dev)
     cid = torch.empty((B, H, L, nr), dtype=torch.int16, device=dev)
@@ -298,6 +326,10 @@ def main():
         lambda: lsh.lsh_chunk_attn(cfg, qk, v, perm, cid, o_r, lse, stream=stream),
         lambda: lsh.lsh_combine_rounds(cfg, o_r, lse, o, stream=stream),
     ]
+    if dm:
+        names = ["lsh_project_in"] + names + ["lsh_project_out"]
+        calls = ([lambda: lsh.lsh_project_in(cfg, dm, xin, wts[0], wts[1], qk, v, stream=stream)]
+                 + calls + [lambda: lsh.lsh_project_out(cfg, dm, o, wts[2], y, stream=stream)])
 
     def step(evs=None):
         for i, c in enumerate(calls):
@@ -325,34 +357,34 @@ def main():
     ms_per_step = total_ms / args.steps
     per_call = {n: float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
                 for i, n in enumerate(names)}
-    assert torch.isfinite(o.float()).all().item(), "non-finite output"
+    assert torch.isfinite((y if dm else o).float()).all().item(), "non-finite output"
 
     tokens = B * L
     value = tokens / (ms_per_step * 1e-3)
     dominant = max(per_call, key=per_call.get)
-    roof = roofline_entry(dominant, w, per_call[dominant])
-    work = algorithmic_work(w)[dominant]
+    roof = roofline_entry(dominant, w, per_call[dominant], dm)
+    work = algorithmic_work(w, dm)[dominant]
     # the committed counters were taken on the method without variant flags
-    roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 else None
+    roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 and not dm else None
     roof["kernel"] = KERNEL_SYMBOLS[dominant]
     roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
     kernels = {}
     for n in names:
-        e = roofline_entry(n, w, per_call[n])
+        e = roofline_entry(n, w, per_call[n], dm)
         e["ms"] = round(per_call[n], 4)
         kernels[n] = e
 
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": LAYER_METRIC if dm else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": d,
                    "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
-                   "causal": w.causal, "flags": args.flags},
+                   "causal": w.causal, "flags": args.flags, **({"d_model": dm} if dm else {})},
         "roofline": roof, "kernels": kernels,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not dm:
         result["cpu_baseline"] = cpu_baseline(w, x, flags=args.flags)
     print(json.dumps(result), flush=True)
 
