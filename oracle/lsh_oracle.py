@@ -26,6 +26,8 @@ The steps, in the pages' order:
               own chunk and the previous one, never to itself unless nothing
               else is there, optionally only to earlier positions          [AIS], [ULT], [MOD]
   4. combine  the rounds merged by logsumexp weights                      [ULT], [MOD]
+Also the gradient of steps 3-4 with respect to qk and v (attention_backward),
+by the chain rule through the steps above (the pages print no backward pass).
 
 Readings taken where the pages leave a step open (each is argued in the design
 notes):
@@ -205,25 +207,25 @@ def duplicate_counts(cid_q: np.ndarray, cid_k: np.ndarray, nchunks: int = 0,
     return inside.sum(axis=2)
 
 
-def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
-                    cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
-                    query_slots: Optional[np.ndarray] = None, dup_correct: bool = True,
-                    wrap: bool = False, bkt_bh: Optional[np.ndarray] = None, r: int = 0):
-    """One round's attention for the queries of sorted chunk k.
+def window_scores(qk_bh: np.ndarray, perm_r: np.ndarray, cid_bh: np.ndarray, k: int, chunk: int,
+                  causal: bool, scale: float, query_slots: Optional[np.ndarray] = None,
+                  dup_correct: bool = True, wrap: bool = False,
+                  bkt_bh: Optional[np.ndarray] = None, r: int = 0):
+    """One round's scores for the queries of sorted chunk k.
 
-    qk_bh, v_bh [L, d] (one batch row and head), perm_r [L] (this round's sorted
+    qk_bh [L, d] (one batch row and head), perm_r [L] (this round's sorted
     order), cid_bh [L, n_r].  For query i and key j in the window of chunk k:
         s_ij = scale * <qk_i, qk_j> - log N_ij - SELF_PENALTY * [j == i],
-    keys j > i are dropped when causal ([MOD] "LSH attention": only earlier
-    positions; the query itself is removed because shared QK makes it the most
-    similar key).  Returns (positions of the queries, o [nq, d], lse [nq]) with
-    lse = logsumexp_j s_ij and o = sum_j softmax(s)_ij v_j ([AIS] formula).
-    query_slots restricts the queries to some sorted slots of chunk k.  The
-    variants dup_correct=False (no log N_ij term) and wrap=True (chunk 0 looks
-    back to the last chunk) change the window and its scores as described in
-    window_chunks and duplicate_counts.  With bkt_bh [L, n_r] (bucket of every
-    position in every round; r is this round) the window keeps only the keys
-    in the query's bucket of round r (the same-bucket variant).
+    with s_ij = -inf for keys j > i when causal ([MOD] "LSH attention": only
+    earlier positions; the query itself is penalised because shared QK makes it
+    the most similar key).  query_slots restricts the queries to some sorted
+    slots of chunk k.  The variants dup_correct=False (no log N_ij term) and
+    wrap=True (chunk 0 looks back to the last chunk) change the window and its
+    scores as described in window_chunks and duplicate_counts.  With bkt_bh
+    [L, n_r] (bucket of every position in every round; r is this round) the
+    window keeps only the keys in the query's bucket of round r (the
+    same-bucket variant; the others get -inf).
+    Returns (query positions qi [nq], key positions kj [nk], s [nq, nk]).
     """
     nchunks = len(perm_r) // chunk
     q_slots = np.arange(k * chunk, (k + 1) * chunk) if query_slots is None else np.asarray(query_slots)
@@ -244,6 +246,20 @@ def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
     s = s - SELF_PENALTY * (qi[:, None] == kj[None, :])
     if causal:
         s = np.where(kj[None, :] > qi[:, None], -np.inf, s)
+    return qi, kj, s
+
+
+def chunk_attention(qk_bh: np.ndarray, v_bh: np.ndarray, perm_r: np.ndarray,
+                    cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
+                    query_slots: Optional[np.ndarray] = None, dup_correct: bool = True,
+                    wrap: bool = False, bkt_bh: Optional[np.ndarray] = None, r: int = 0):
+    """One round's attention for the queries of sorted chunk k, over the scores
+    of window_scores (same arguments; v_bh [L, d]).  Returns (positions of the
+    queries, o [nq, d], lse [nq]) with lse = logsumexp_j s_ij and
+    o = sum_j softmax(s)_ij v_j ([AIS] formula).
+    """
+    qi, kj, s = window_scores(qk_bh, perm_r, cid_bh, k, chunk, causal, scale, query_slots,
+                              dup_correct, wrap, bkt_bh, r)
     m = s.max(axis=1, keepdims=True)          # finite: the query itself is never dropped
     e = np.exp(s - m)
     z = e.sum(axis=1, keepdims=True)
@@ -327,6 +343,91 @@ def forward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, n_buckets: int, chunk:
     o, LSE = combine_rounds(o_r, lse)
     return {"buckets": buckets, "margins": margins, "perm": perm, "cid": cid,
             "o_rounds": o_r, "lse": lse, "o": o, "LSE": LSE}
+
+
+# --------------------------------------------------------------------------- backward
+# The gradient of the forward above with respect to qk and v, for a loss whose
+# gradient with respect to the combined output o is d_o.  The pages give no
+# backward pass; this is the chain rule through the steps as defined here.  The
+# buckets (hence perm and cid) are piecewise constant in qk and contribute no
+# gradient.  Substituting the combine into the rounds gives
+#     o_i = sum_r sum_{j in W_i^r} exp(s_ijr - LSE_i) v_j,   LSE_i = logsumexp_r lse_ir,
+# one softmax over all (round, key) pairs of query i, so with
+#     P_ijr = exp(s_ijr - LSE_i),  Delta_i = <d_o_i, o_i>,
+#     dS_ijr = P_ijr (<d_o_i, v_j> - Delta_i):
+#     dv_j  += P_ijr d_o_i
+#     dqk_i += scale dS_ijr qk_j       (query role)
+#     dqk_j += scale dS_ijr qk_i       (key role; both roles for j == i)
+# The -log N_ij, self-penalty and causal terms are constants of the scores.
+def chunk_attention_grad(qk_bh: np.ndarray, v_bh: np.ndarray, do_bh: np.ndarray,
+                         LSE_bh: np.ndarray, delta_bh: np.ndarray, perm_r: np.ndarray,
+                         cid_bh: np.ndarray, k: int, chunk: int, causal: bool, scale: float,
+                         dup_correct: bool = True, wrap: bool = False,
+                         bkt_bh: Optional[np.ndarray] = None, r: int = 0):
+    """Round r's contributions to the gradients from the queries of sorted chunk
+    k.  do_bh [L, d] is the gradient at the combined output, LSE_bh [L] the
+    combined logsumexp, delta_bh [L] = <d_o_i, o_i>.  Returns (qi, kj, dq [nq, d]
+    (query role), dk [nk, d] (key role), dv [nk, d])."""
+    qi, kj, s = window_scores(qk_bh, perm_r, cid_bh, k, chunk, causal, scale, None,
+                              dup_correct, wrap, bkt_bh, r)
+    P = np.exp(s - np.asarray(LSE_bh, dtype=np.float64)[qi][:, None])
+    do_q = np.asarray(do_bh[qi], dtype=np.float64)
+    dP = do_q @ np.asarray(v_bh[kj], dtype=np.float64).T
+    dS = P * (dP - np.asarray(delta_bh, dtype=np.float64)[qi][:, None])
+    dq = scale * (dS @ np.asarray(qk_bh[kj], dtype=np.float64))
+    dk = scale * (dS.T @ np.asarray(qk_bh[qi], dtype=np.float64))
+    dv = P.T @ do_q
+    return qi, kj, dq, dk, dv
+
+
+def attention_backward(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.ndarray,
+                       d_o: np.ndarray, chunk: int, causal: bool, scale: float,
+                       dup_correct: bool = True, wrap: bool = False,
+                       buckets: Optional[np.ndarray] = None):
+    """Gradients of steps 3-4 for fixed perm/cid (the forward is recomputed).
+
+    qk, v, d_o [B, H, L, d].  -> dict with dqk, dv [B, H, L, d] float64, the
+    per-round contributions dqk_rounds, dv_rounds [B, H, n_r, L, d] (each
+    round's share: a position's query- and key-role terms of that round), and
+    the recomputed o, LSE and Delta.
+    """
+    B, H, L, d = qk.shape
+    n_r = perm.shape[2]
+    o_r, lse = attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct,
+                                wrap=wrap, buckets=buckets)
+    o, LSE = combine_rounds(o_r, lse)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    delta = np.sum(d_o * o, axis=-1)
+    dqk_r = np.zeros((B, H, n_r, L, d))
+    dv_r = np.zeros((B, H, n_r, L, d))
+    for b in range(B):
+        for h in range(H):
+            bkt = None if buckets is None else np.asarray(buckets[b, h]).T     # [L, n_r]
+            for r in range(n_r):
+                for k in range(L // chunk):
+                    qi, kj, dq, dk, dv = chunk_attention_grad(
+                        qk[b, h], v[b, h], d_o[b, h], LSE[b, h], delta[b, h], perm[b, h, r],
+                        cid[b, h], k, chunk, causal, scale, dup_correct, wrap, bkt, r)
+                    # positions are distinct within qi and within kj
+                    dqk_r[b, h, r, qi] += dq
+                    dqk_r[b, h, r, kj] += dk
+                    dv_r[b, h, r, kj] += dv
+    return {"dqk": dqk_r.sum(axis=2), "dv": dv_r.sum(axis=2), "dqk_rounds": dqk_r,
+            "dv_rounds": dv_r, "o": o, "LSE": LSE, "delta": delta}
+
+
+def backward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, d_o: np.ndarray, n_buckets: int,
+             chunk: int, causal: bool, scale: Optional[float] = None, dup_correct: bool = True,
+             wrap: bool = False, same_bucket: bool = False):
+    """Hash and sort as in forward, then attention_backward."""
+    if scale is None:
+        scale = default_scale(qk.shape[-1])
+    buckets, _ = hash_buckets(qk, R)
+    perm, cid = sort_rounds(buckets, n_buckets, chunk)
+    out = attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale, dup_correct, wrap,
+                             buckets if same_bucket else None)
+    out.update({"buckets": buckets, "perm": perm, "cid": cid})
+    return out
 
 
 # --------------------------------------------------------------------------- the layer around it

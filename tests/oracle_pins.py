@@ -34,6 +34,10 @@ What pins what:
            a no-op;
          - same-bucket mask: union brute force and per-round brute force with
            windows restricted to the query's bucket.
+  backward - the gradients of steps 3-4 against central finite differences of
+           the oracle's own forward (fixed buckets), and against torch autograd
+           of the union closed form (independent code); sum_j dv_j = sum_i d_o_i
+           (the combined weights of each query sum to one).
   layer  - both projections against Python loops over their definitions;
          - identity weights reduce the layer to the four steps on the input's
            head slices; permuting heads consistently changes nothing.
@@ -371,6 +375,73 @@ def check_head_permutation(seed=31):
     assert np.max(np.abs(a["y"] - b["y"])) < 1e-12
 
 
+# --------------------------------------------------------------------------- backward
+def _bwd_case(L=16, d=3, n_r=2, nb=4, seed=40):
+    rng = np.random.default_rng(seed)
+    qk = rng.standard_normal((1, 1, L, d))
+    v = rng.standard_normal((1, 1, L, d))
+    d_o = rng.standard_normal((1, 1, L, d))
+    buckets = rng.integers(0, nb, size=(1, 1, n_r, L))
+    return qk, v, d_o, buckets
+
+
+def _loss(qk, v, d_o, perm, cid, chunk, causal, scale, dup_correct):
+    o_r, lse = O.attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct)
+    o, _ = O.combine_rounds(o_r, lse)
+    return float(np.sum(o * d_o))
+
+
+def check_backward_finite_differences(causal=True, n_r=2, dup_correct=True, seed=40):
+    """Central differences of sum(o * d_o) in every element of qk and v, with the
+    buckets held fixed (they are piecewise constant in qk)."""
+    L, d, nb, chunk = 16, 3, 4, 4
+    qk, v, d_o, buckets = _bwd_case(L, d, n_r, nb, seed)
+    perm, cid = O.sort_rounds(buckets, nb, chunk)
+    scale = 0.7
+    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale, dup_correct)
+    h = 1e-4
+    for name, arr, grad in (("qk", qk, g["dqk"]), ("v", v, g["dv"])):
+        fd = np.empty_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a_p = arr.copy(); a_p[idx] += h
+            a_m = arr.copy(); a_m[idx] -= h
+            args_p = (a_p, v) if name == "qk" else (qk, a_p)
+            args_m = (a_m, v) if name == "qk" else (qk, a_m)
+            fd[idx] = (_loss(*args_p, d_o, perm, cid, chunk, causal, scale, dup_correct)
+                       - _loss(*args_m, d_o, perm, cid, chunk, causal, scale, dup_correct)) / (2 * h)
+        err = np.max(np.abs(grad - fd)) / np.max(np.abs(fd))
+        assert err < 1e-6, f"d{name}: relative deviation {err:.3g} from finite differences"
+
+
+def check_backward_union_autograd(causal=False, n_r=3, seed=41):
+    """The oracle's gradients equal torch autograd of the union closed form
+    (tests/reference_forms.py), which shares no code with the oracle."""
+    import torch
+    L, d, nb, chunk = 24, 4, 4, 4
+    qk, v, d_o, buckets = _bwd_case(L, d, n_r, nb, seed)
+    perm, cid = O.sort_rounds(buckets, nb, chunk)
+    scale = 0.5
+    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale)
+    W = RF.brute_windows(buckets[0, 0], chunk, causal)
+    tq = torch.tensor(qk[0, 0], dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v[0, 0], dtype=torch.float64, requires_grad=True)
+    out = RF.union_attention_torch(tq, tv, W, scale)
+    (out * torch.tensor(d_o[0, 0])).sum().backward()
+    for name, got, want in (("qk", g["dqk"][0, 0], tq.grad.numpy()), ("v", g["dv"][0, 0], tv.grad.numpy())):
+        err = np.max(np.abs(got - want)) / np.max(np.abs(want))
+        assert err < 1e-9, f"d{name}: relative deviation {err:.3g} from autograd of the union form"
+
+
+def check_backward_dv_sum(seed=42):
+    """Each query's combined weights sum to one, so sum_j dv_j = sum_i d_o_i."""
+    L, d, nb, chunk = 32, 5, 8, 4
+    qk, v, d_o, buckets = _bwd_case(L, d, 4, nb, seed)
+    perm, cid = O.sort_rounds(buckets, nb, chunk)
+    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, True, 0.6)
+    assert np.allclose(g["dv"].sum(axis=2), d_o.sum(axis=2), rtol=0, atol=1e-10)
+    assert np.allclose(g["dqk_rounds"].sum(axis=2), g["dqk"], rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = {
     "hash_demo": check_hash_demo,
     "hash_labels": check_hash_labels,
@@ -404,4 +475,10 @@ ALL_CHECKS = {
     "projections_brute_force": check_projections_brute_force,
     "identity_layer": check_identity_layer,
     "head_permutation": check_head_permutation,
+    "backward_finite_differences": check_backward_finite_differences,
+    "backward_finite_differences_noncausal_no_correction": lambda: check_backward_finite_differences(
+        causal=False, n_r=3, dup_correct=False, seed=43),
+    "backward_union_autograd": check_backward_union_autograd,
+    "backward_union_autograd_causal": lambda: check_backward_union_autograd(causal=True, n_r=2, seed=44),
+    "backward_dv_sum": check_backward_dv_sum,
 }

@@ -122,3 +122,24 @@ def union_attention(qk: np.ndarray, v: np.ndarray, buckets: np.ndarray, chunk: i
         w /= w.sum()
         out[i] = w @ v[others]
     return out
+
+
+def union_attention_torch(qk, v, windows: list, scale: float):
+    """The union closed form above as differentiable float64 torch code (for
+    gradient checks by autograd).  qk, v: torch tensors [L, d] (requires_grad as
+    needed); windows: brute_windows(...) of one (batch row, head)."""
+    import torch
+    L = qk.shape[0]
+    rows = []
+    for i in range(L):
+        union = set()
+        for Wr in windows:
+            union |= Wr[i]
+        others = sorted(union - {i})
+        if not others:
+            rows.append(v[i])
+            continue
+        idx = torch.tensor(others, dtype=torch.long)
+        s = scale * (qk[idx] @ qk[i])
+        rows.append(torch.softmax(s, dim=0) @ v[idx])
+    return torch.stack(rows)

@@ -138,7 +138,27 @@ def _weights_read_as_in_out(x, w_qk, w_v, heads):
     return O.split_heads(qk, heads), O.split_heads(v, heads)
 
 
+_GRAD_ORIG = O.chunk_attention_grad
+
+
+def _grad_without_delta(qk, v, do, LSE, delta, *a, **k):
+    return _GRAD_ORIG(qk, v, do, LSE, np.zeros_like(delta), *a, **k)
+
+
+def _grad_part_zeroed(part):
+    def f(*a, **k):
+        out = list(_GRAD_ORIG(*a, **k))
+        out[part] = np.zeros_like(out[part])
+        return tuple(out)
+    return f
+
+
 MUTATIONS = {
+    "backward drops Delta": ("chunk_attention_grad", _grad_without_delta, "backward_finite_differences"),
+    "backward drops the key role": ("chunk_attention_grad", _grad_part_zeroed(3),
+                                    "backward_union_autograd"),
+    "backward drops the query role": ("chunk_attention_grad", _grad_part_zeroed(2),
+                                      "backward_finite_differences"),
     "hash drops the negated half": ("bucket_from_projection", _argmax_positive_half_only, "hash_antipodal"),
     "hash takes argmin": ("bucket_from_projection", _argmin_labels, "hash_labels"),
     "sort not stable": ("stable_counting_sort", _unstable_sort, "sort_library"),
