@@ -171,6 +171,36 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
                               const float* lse, void* o, void* stream);
 
 /*
+ * Backward of steps 3-4: gradients with respect to qk and v (bfloat16, chunk 64;
+ * the method as above, or with LSH_FLAG_NO_DUP_CORRECTION).  The pages print no
+ * backward pass; this is the chain rule through the forward defined above.
+ * After the combine, query i's output is one softmax over all (round, key)
+ * pairs of its windows ([MOD] "Multi-round LSH attention" merges the rounds by
+ * their logsumexp):
+ *   o_i = sum_r sum_j P_ijr v_j,   P_ijr = exp(s_ijr - LSE_i),   LSE_i = logsumexp_r lse_ir.
+ * With Delta_i = <d_o_i, o_i> and dS_ijr = P_ijr (<d_o_i, v_j> - Delta_i):
+ *   d_v[j]  = sum of P_ijr d_o_i over the (i, r) whose window holds j
+ *   d_qk[i] = scale * (sum_{r, j} dS_ijr qk_j  +  sum_{r, i'} dS_i'ir qk_i')
+ *             (i as a query, and i as a key of the queries i').
+ * The buckets are piecewise constant in qk and carry no gradient.
+ *   qk, v [B, H, L, d] and perm, cid, lse as passed to / written by steps 2-3;
+ *   o    [B, H, L, d]  the combined forward output (lsh_combine_rounds);
+ *   d_o  [B, H, L, d]  bf16 in: the loss gradient at o;
+ *   d_qk, d_v [B, H, L, d] float32 out (overwritten).
+ *   workspace  device scratch of at least lsh_backward_workspace_bytes(cfg)
+ *              bytes (combined lse and Delta, and per-round partial gradients:
+ *              about 6 * B*H*n_rounds*L*d bytes); its contents on entry do not
+ *              matter.
+ * Errors as above, and LSH_ERR_UNSUPPORTED for dtype LSH_F32, chunk other than
+ * 64, or a flag other than LSH_FLAG_NO_DUP_CORRECTION; LSH_ERR_WORKSPACE.
+ */
+size_t lsh_backward_workspace_bytes(const lsh_config* cfg);
+lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* v,
+                             const int32_t* perm, const int16_t* cid, const float* lse,
+                             const void* o, const void* d_o, float* d_qk, float* d_v,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Projections of the LSH-attention layer around steps 1-4 (bfloat16 only).
  * [MOD] "LSH attention": queries and keys share one projection; [AIS]
  * experiment set-up: d_model 1024 and 8 heads.  Weights are stored like a

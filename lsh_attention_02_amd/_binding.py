@@ -26,8 +26,8 @@ LSH_F32, LSH_BF16 = 0, 1
 LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2, 4
 
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
-            "lsh_combine_rounds", "lsh_project_in", "lsh_project_out", "lsh_status_string",
-            "lsh_last_error")
+            "lsh_combine_rounds", "lsh_backward_workspace_bytes", "lsh_attn_backward",
+            "lsh_project_in", "lsh_project_out", "lsh_status_string", "lsh_last_error")
 
 
 class LSHError(RuntimeError):
@@ -93,6 +93,9 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_sort.argtypes = [CP, P, P, P, P, ctypes.c_size_t, P]
     lib.lsh_chunk_attn.argtypes = [CP, P, P, P, P, P, P, P]
     lib.lsh_combine_rounds.argtypes = [CP, P, P, P, P]
+    lib.lsh_backward_workspace_bytes.argtypes = [CP]
+    lib.lsh_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.lsh_attn_backward.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.lsh_project_in.argtypes = [CP, I32, P, P, P, P, P, P]
     lib.lsh_project_out.argtypes = [CP, I32, P, P, P, P]
     for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_project_in",
@@ -233,6 +236,51 @@ def lsh_combine_rounds(cfg: LSHConfig, o_rounds: torch.Tensor, lse: torch.Tensor
     _check(lib.lsh_combine_rounds(ctypes.byref(c), _ptr(o_rounds), _ptr(lse), _ptr(o),
                                   _stream(dev, stream)), "lsh_combine_rounds")
     return o
+
+
+def lsh_backward_workspace_bytes(cfg: LSHConfig) -> int:
+    c = cfg.to_c()
+    return int(load_library().lsh_backward_workspace_bytes(ctypes.byref(c)))
+
+
+def backward_workspace(cfg: LSHConfig, device) -> torch.Tensor:
+    """A device buffer large enough for lsh_attn_backward (at least 16 bytes)."""
+    n = max(16, lsh_backward_workspace_bytes(cfg))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lsh_attn_backward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor,
+                      cid: torch.Tensor, lse: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor,
+                      d_qk: Optional[torch.Tensor] = None, d_v: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of steps 3-4: (d_qk, d_v), each [B, H, L, d] float32."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(qk, "qk", sh["qk"], cfg.torch_dtype)
+    dev = qk.device
+    _expect(v, "v", sh["v"], cfg.torch_dtype, dev)
+    _expect(perm, "perm", sh["perm"], torch.int32, dev)
+    _expect(cid, "cid", sh["cid"], torch.int16, dev)
+    _expect(lse, "lse", sh["lse"], torch.float32, dev)
+    _expect(o, "o", sh["o"], cfg.torch_dtype, dev)
+    _expect(d_o, "d_o", sh["o"], cfg.torch_dtype, dev)
+    if d_qk is None:
+        d_qk = torch.empty(sh["qk"], dtype=torch.float32, device=dev)
+    if d_v is None:
+        d_v = torch.empty(sh["v"], dtype=torch.float32, device=dev)
+    _expect(d_qk, "d_qk", sh["qk"], torch.float32, dev)
+    _expect(d_v, "d_v", sh["v"], torch.float32, dev)
+    if workspace is None:
+        workspace = backward_workspace(cfg, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous buffer on the same device")
+    nbytes = workspace.numel() * workspace.element_size()
+    c = cfg.to_c()
+    _check(lib.lsh_attn_backward(ctypes.byref(c), _ptr(qk), _ptr(v), _ptr(perm), _ptr(cid),
+                                 _ptr(lse), _ptr(o), _ptr(d_o), _ptr(d_qk), _ptr(d_v),
+                                 _ptr(workspace), ctypes.c_size_t(nbytes), _stream(dev, stream)),
+           "lsh_attn_backward")
+    return d_qk, d_v
 
 
 def forward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, R: torch.Tensor,

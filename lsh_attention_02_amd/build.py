@@ -26,13 +26,15 @@ CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # Packed FP32 instructions are disabled for all device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in ordinary VGPRs: the attention kernel reads its score and
-    # output accumulators with VALU instructions, and accumulation registers
-    # would add a copy per value.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# MFMA results in ordinary VGPRs: the attention kernel reads its score and
+# output accumulators with VALU instructions, and accumulation registers would
+# add a copy per value.  Not for the backward, whose live set exceeds the 256
+# ordinary VGPRs (its key-gradient accumulators live in accumulation registers).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"lsh_attn_bwd.hip"}
 
 
 def hipcc() -> str:
@@ -54,7 +56,8 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     objs = [os.path.join(BUILD_DIR, s[:-4] + ".o") for s in sources]
-    jobs = [[cc, *CXXFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    jobs = [[cc, *CXXFLAGS, *([] if s in NO_VGPR_FORM else VGPR_FORM), "-c", os.path.join(CSRC, s),
+             "-o", o] for s, o in zip(sources, objs)]
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with cf.ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(_run, jobs))

@@ -113,6 +113,44 @@ lsh_status check_layer(const lsh_config* cfg, int32_t d_model)
     return LSH_OK;
 }
 
+// counters, then (same-bucket variant) one rank per (segment, bucket)
+size_t ranks_of(const lsh_config* cfg, const lshk::SortPlan& p)
+{
+    return (cfg->flags & LSH_FLAG_SAME_BUCKET) ? (size_t)p.nseg * cfg->n_buckets : 0;
+}
+
+// Backward workspace: combined lse and Delta (float32, one per token-head), then
+// the three per-round partial tensors (bf16), each part 256-byte aligned.
+struct BwdLayout {
+    size_t lse_c, delta, dq_r, dk_r, dv_r, total;
+};
+
+BwdLayout bwd_layout(const lsh_config* cfg)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t T = (size_t)bh_of(cfg) * cfg->seq_len;
+    const size_t part = T * cfg->n_rounds * cfg->d_head * 2;
+    BwdLayout l;
+    l.lse_c = 0;
+    l.delta = up(T * 4);
+    l.dq_r = l.delta + up(T * 4);
+    l.dk_r = l.dq_r + up(part);
+    l.dv_r = l.dk_r + up(part);
+    l.total = l.dv_r + up(part);
+    return l;
+}
+
+lsh_status check_backward(const lsh_config* cfg)
+{
+    LSH_TRY(check_config(cfg));
+    if (cfg->dtype != LSH_BF16) return fail(LSH_ERR_UNSUPPORTED, "the backward supports LSH_BF16 only");
+    if (cfg->chunk != 64) return fail(LSH_ERR_UNSUPPORTED, "the backward supports chunk 64 only");
+    if (cfg->flags & ~LSH_FLAG_NO_DUP_CORRECTION)
+        return fail(LSH_ERR_UNSUPPORTED,
+                    "the backward supports the method and LSH_FLAG_NO_DUP_CORRECTION only");
+    return LSH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,12 +180,6 @@ lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_
                                         cfg->seq_len, cfg->n_rounds, cfg->n_buckets / 2,
                                         static_cast<hipStream_t>(stream)),
                       "lsh_hash");
-}
-
-// counters, then (same-bucket variant) one rank per (segment, bucket)
-size_t ranks_of(const lsh_config* cfg, const lshk::SortPlan& p)
-{
-    return (cfg->flags & LSH_FLAG_SAME_BUCKET) ? (size_t)p.nseg * cfg->n_buckets : 0;
 }
 
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg)
@@ -208,6 +240,57 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds, const
                                            cfg->seq_len, cfg->n_rounds,
                                            static_cast<hipStream_t>(stream)),
                       "lsh_combine_rounds");
+}
+
+size_t lsh_backward_workspace_bytes(const lsh_config* cfg)
+{
+    if (check_backward(cfg) != LSH_OK) return 0;
+    return bwd_layout(cfg).total;
+}
+
+lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* v,
+                             const int32_t* perm, const int16_t* cid, const float* lse,
+                             const void* o, const void* d_o, float* d_qk, float* d_v,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    LSH_TRY(check_backward(cfg));
+    LSH_TRY(check_ptr(qk, "qk"));
+    LSH_TRY(check_ptr(v, "v"));
+    LSH_TRY(check_ptr(perm, "perm"));
+    LSH_TRY(check_ptr(cid, "cid"));
+    LSH_TRY(check_ptr(lse, "lse"));
+    LSH_TRY(check_ptr(o, "o"));
+    LSH_TRY(check_ptr(d_o, "d_o"));
+    LSH_TRY(check_ptr(d_qk, "d_qk"));
+    LSH_TRY(check_ptr(d_v, "d_v"));
+    LSH_TRY(check_ptr(workspace, "workspace"));
+    const BwdLayout l = bwd_layout(cfg);
+    if (workspace_bytes < l.total)
+        return fail(LSH_ERR_WORKSPACE, "workspace smaller than lsh_backward_workspace_bytes()");
+    char* ws = static_cast<char*>(workspace);
+    lshk::BwdArgs a;
+    a.qk = qk;
+    a.v = v;
+    a.o = o;
+    a.d_o = d_o;
+    a.perm = perm;
+    a.cid = cid;
+    a.lse = lse;
+    a.lse_c = reinterpret_cast<float*>(ws + l.lse_c);
+    a.delta = reinterpret_cast<float*>(ws + l.delta);
+    a.dq_r = ws + l.dq_r;
+    a.dk_r = ws + l.dk_r;
+    a.dv_r = ws + l.dv_r;
+    a.dqk = d_qk;
+    a.dv = d_v;
+    a.bh = bh_of(cfg);
+    a.L = cfg->seq_len;
+    a.n_r = cfg->n_rounds;
+    a.causal = cfg->causal;
+    a.scale = cfg->scale;
+    a.dup = !(cfg->flags & LSH_FLAG_NO_DUP_CORRECTION);
+    return hip_status(lshk::launch_attn_backward(cfg->d_head, a, static_cast<hipStream_t>(stream)),
+                      "lsh_attn_backward");
 }
 
 lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x, const void* w_qk,

@@ -1,0 +1,547 @@
+// Backward pass of chunked LSH attention + round combine on gfx950 (bfloat16).
+//
+// The forward (ai-scholar Reformer article and Ultralytics "Reformer" glossary,
+// sections on LSH attention; modulabs-hub notes, "LSH attention" and
+// "Multi-round LSH attention") gives, after the combine, one softmax per query
+// over all (round, key) pairs of its windows:
+//     o_i = sum_r sum_j P_ijr v_j,   P_ijr = exp(s_ijr - LSE_i),
+// with LSE_i the logsumexp of the rounds' lse.  For a loss gradient d_o at the
+// combined output, with Delta_i = <d_o_i, o_i> and dS_ijr = P_ijr (<d_o_i, v_j> -
+// Delta_i), the chain rule gives
+//     dv_j += P_ijr d_o_i,  dqk_i += scale dS_ijr qk_j,  dqk_j += scale dS_ijr qk_i.
+// The buckets are piecewise constant and carry no gradient; the scores are
+// recomputed from qk (no attention matrix is kept by the forward).
+//
+// Kernels:
+//   k_bwd_prep    per token-head: LSE (from the per-round lse) and Delta.
+//   k_attn_bwd    per (b, h, round, run of chunks), like the forward: the chunk's
+//                 rows are gathered into LDS once and kept as the next chunk's
+//                 look-back.  Per query chunk c (keys: chunks c-1 and c):
+//     phase 1  wave w takes queries 16w..16w+15.  S^T = K Q^T and dP^T = V dO^T
+//              on MFMA (as the forward's scores), P and dS in registers; dQ^T =
+//              K^T dS^T (as the forward's PV product, K^T in LDS).  P and dS also
+//              go to LDS as [key][query] for phase 2.
+//     phase 2  the keys: waves 2g, 2g+1 own the chunk held in LDS slot g (32
+//              keys each) and accumulate dK^T = Q^T dS and dV^T = dO^T P over
+//              the two tiles that chunk is a key of (as the current chunk, then
+//              as the look-back of the next); a run ends with one extra tile
+//              (the next run's first queries against its last chunk), so every
+//              position's key gradient is summed in one workgroup.
+//              Results are per-round partials (bf16, original position order).
+//   k_bwd_reduce  dqk = sum_r (dq_r + dk_r), dv = sum_r dv_r in fp32.
+#include "lsh_chunk_attn.h"
+
+namespace lshk {
+namespace attn {
+namespace {
+
+constexpr int BWD_RUN = 16;                  // query chunks per workgroup
+
+// P / dS rows in LDS: one row per window key (2C rows), C queries each, in
+// 8-byte groups of 4 queries; group qg of row k is stored at qg ^ pswz(k).
+// The phase-2 operand reads (8 bytes, 32 lanes: 16 keys x 2 groups) and the
+// phase-1 stores (2 bytes, keys 4g + j of a tile, 64 queries) are then free of
+// bank conflicts (rows alternate between the 32-bank halves).
+__device__ __forceinline__ int pswz(int k) { return ((k >> 1) & 7) << 1; }
+
+template <int D, int C, int NDW>
+struct BwdLds {
+    static constexpr int KROW = KLayout<bf16_t, D>::ROW;
+    static constexpr int TROWB = C * 2;              // bytes of a transposed row (C keys)
+    static constexpr int PROWB = C * 2;              // bytes of a P / dS row (C queries)
+    static constexpr int NW = NDW > 0 ? NDW : 1;
+    float neg_log2[36];                              // as in the forward (first member)
+    bf16_t k[2][C * KROW];                           // qk rows, slot = chunk & 1
+    bf16_t v[2][C * KROW];                           // v rows
+    char kt[2][D * TROWB];                           // qk^T rows (d), keys in groups of 4
+    char dot[D * TROWB];                             // d_o^T of the query chunk
+    char p[2 * C * PROWB];                           // P[key][query] of the current tile
+    char ds[2 * C * PROWB];                          // dS[key][query]
+    int pos[2][C];
+    uint32_t cid[2][C * NW];
+    float lse2[C];                                   // combined logsumexp, log2 units
+    float delta[C];
+};
+
+template <int D, int C, int NDW>
+__global__ __launch_bounds__(4 * C)
+void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
+                const bf16_t* __restrict__ d_o, const int32_t* __restrict__ perm,
+                const int16_t* __restrict__ cid, const float* __restrict__ lse_c,
+                const float* __restrict__ delta, bf16_t* __restrict__ dq_r,
+                bf16_t* __restrict__ dk_r, bf16_t* __restrict__ dv_r, int L, int n_r,
+                int causal, float scale, float scale_log2, int nruns)
+{
+    using T = bf16_t;
+    using M = Mfma16<T>;
+    using S = BwdLds<D, C, NDW>;
+    using KL = KLayout<T, D>;
+    constexpr int NTH = 4 * C, W = C / 16;
+    constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+    constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
+    constexpr int VE = 8, VPR = D / VE;
+    constexpr int TROWB = S::TROWB, PROWB = S::PROWB;
+    constexpr int JOBS = (C / 4) * VPR;
+    constexpr int JPT = (JOBS + NTH - 1) / NTH;
+    constexpr int NW = S::NW;
+    constexpr int KSL = 2 * C / W;                   // keys per wave in phase 2
+    constexpr int KTW = KSL / 16;                    // 16-key tiles per wave in phase 2
+    static_assert(C == 64, "the P/dS layout assumes 64-query chunks");
+    __shared__ __attribute__((aligned(16))) S sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+
+    int bid = blockIdx.x;
+    const int r = bid % n_r;
+    bid /= n_r;
+    const int run = bid % nruns;
+    const long bh = bid / nruns;
+    const int nchunks = L / C;
+    const int k0 = run * BWD_RUN, k1 = min(k0 + BWD_RUN, nchunks);
+
+    const T* qb = qk + bh * (long)L * D;
+    const T* vb = v + bh * (long)L * D;
+    const T* db = d_o + bh * (long)L * D;
+    const int32_t* pr = perm + (bh * n_r + r) * (long)L;
+    const int16_t* cb = cid + bh * (long)L * n_r;
+    const float* lb = lse_c + bh * (long)L;
+    const float* deb = delta + bh * (long)L;
+    const long rbase = (bh * n_r + r) * (long)L * D;
+    const uint32_t ones = 0x00010001u;
+    const uint32_t nch2 = (uint32_t)nchunks * 0x00010001u;
+
+    if (tid < 33) sm.neg_log2[tid] = (tid % 2 == 0 && tid / 2 < n_r) ? -__log2f((float)(n_r - tid / 2)) : 0.f;
+
+    auto clamp_pos = [&](int p) { return min(max(p, 0), L - 1); };
+
+    // Gathers for the next chunk, kept raw in registers until stored (as in the
+    // forward).  Job = 4 consecutive rows x one 16-byte piece of qk, v and d_o.
+    int gpos[JPT][4];
+    int mypos = 0, qposraw = 0;
+    u32x4 kreg[JPT][4], vreg[JPT][4], dreg[JPT][4];
+    u32x4 dofrag[NKS];          // d_o fragments of this lane's query row (next chunk)
+    uint32_t craw[2 * NW];
+    float lraw = 0.f, draw = 0.f;
+    int rpos = 0;
+
+    auto fetch_positions = [&](int kk) {
+#pragma unroll
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            const int rg = (job < JOBS ? job : 0) / VPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gpos[jb][i] = pr[kk * C + 4 * rg + i];
+        }
+        mypos = pr[kk * C + tid % C];
+        qposraw = pr[kk * C + wave * 16 + r16];
+    };
+    auto fetch_rows = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            const int piece = (job < JOBS ? job : 0) % VPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const long row = (long)clamp_pos(gpos[jb][i]) * D + piece * VE;
+                kreg[jb][i] = *reinterpret_cast<const u32x4*>(qb + row);
+                vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + row);
+                dreg[jb][i] = *reinterpret_cast<const u32x4*>(db + row);
+            }
+        }
+        const long qrow = (long)clamp_pos(qposraw) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            dofrag[ks] = *reinterpret_cast<const u32x4*>(db + qrow + ks * KSTEP + g * KPL);
+        rpos = clamp_pos(mypos);
+        const int16_t* cr = cb + (long)rpos * n_r;
+        if constexpr (NDW > 0) {
+#pragma unroll
+            for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
+        }
+        lraw = lb[rpos];
+        draw = deb[rpos];
+    };
+    // transposed store of 4 rows x VE elements into a [d][row] table (the
+    // forward's v^T layout: groups of 4 rows, group rg of row d at rg ^ vt_swz(d))
+    auto store_t = [&](char* base, const u32x4 (&reg)[4], int rg, int piece) {
+#pragma unroll
+        for (int x = 0; x < VE; ++x) {
+            const int d = piece * VE + x;
+            char* dst = base + d * TROWB + 8 * (rg ^ vt_swz<C>(d));
+            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w0 = __builtin_amdgcn_perm(reg[1][x >> 1], reg[0][x >> 1], sel);
+            const uint32_t w1 = __builtin_amdgcn_perm(reg[3][x >> 1], reg[2][x >> 1], sel);
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+        }
+    };
+    auto store_rows = [&](int sl) {
+#pragma unroll
+        for (int jb = 0; jb < JPT; ++jb) {
+            const int job = tid + jb * NTH;
+            if (job < JOBS) {
+                const int rg = job / VPR, piece = job % VPR;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    *reinterpret_cast<u32x4*>(&sm.k[sl][KL::off(4 * rg + i, piece * VE)]) = kreg[jb][i];
+                    *reinterpret_cast<u32x4*>(&sm.v[sl][KL::off(4 * rg + i, piece * VE)]) = vreg[jb][i];
+                }
+                store_t(sm.kt[sl], kreg[jb], rg, piece);
+                store_t(sm.dot, dreg[jb], rg, piece);
+            }
+        }
+        if (tid < C) {
+            sm.pos[sl][tid] = rpos;
+#pragma unroll
+            for (int w = 0; w < NDW; ++w) {
+                const uint32_t lo = 2 * w < n_r ? craw[2 * w] : 0u;
+                const uint32_t hi = 2 * w + 1 < n_r ? craw[2 * w + 1] : 0u;
+                sm.cid[sl][tid * NDW + w] = lo | (hi << 16);
+            }
+            sm.lse2[tid] = lraw * LOG2E;
+            sm.delta[tid] = draw;
+        }
+    };
+
+    // Iteration it handles chunk chunk_of(it): a look-back chunk first (load
+    // only) when k0 > 0, the query chunks k0 .. k1-1, then chunk k1 when it
+    // exists (key side only: its queries against chunk k1-1).
+    const bool lookback = k0 > 0;
+    const bool extra = k1 < nchunks;
+    const int it0 = lookback ? 1 : 0;
+    const int nit = (k1 - k0) + it0 + (extra ? 1 : 0);
+    auto chunk_of = [&](int it) { return k0 - it0 + it; };
+
+    // phase-2 ownership: waves 2G, 2G+1 (G = wave / (W/2)) own the chunk in LDS
+    // slot G; wave sub-slice sw covers keys KSL*sw .. of that chunk
+    const int G = wave / (W / 2), sw = wave % (W / 2);
+    f32x4 acck[DT][KTW], accv[DT][KTW];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) { acck[dt][kt] = f32x4{}; accv[dt][kt] = f32x4{}; }
+
+    // write this wave's accumulated key gradients for the chunk in slot G
+    auto write_keys = [&]() {
+#pragma unroll
+        for (int kt = 0; kt < KTW; ++kt) {
+            const int krow = KSL * sw + 16 * kt + r16;
+            const long pos = sm.pos[G][krow];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d0 = dt * 16 + 4 * g;
+                const u32x2 wk = {pack_bf16x2(acck[dt][kt][0] * scale, acck[dt][kt][1] * scale),
+                                  pack_bf16x2(acck[dt][kt][2] * scale, acck[dt][kt][3] * scale)};
+                const u32x2 wv = {pack_bf16x2(accv[dt][kt][0], accv[dt][kt][1]),
+                                  pack_bf16x2(accv[dt][kt][2], accv[dt][kt][3])};
+                *reinterpret_cast<u32x2*>(dk_r + rbase + pos * D + d0) = wk;
+                *reinterpret_cast<u32x2*>(dv_r + rbase + pos * D + d0) = wv;
+            }
+        }
+    };
+
+    fetch_positions(chunk_of(0));
+    fetch_rows();
+    if (1 < nit) fetch_positions(chunk_of(1));
+
+    for (int it = 0; it < nit; ++it) {
+        const int c = chunk_of(it);
+        const int sl = c & 1, sp = sl ^ 1;
+        u32x4 dof[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) dof[ks] = dofrag[ks];
+        store_rows(sl);
+        __syncthreads();
+        if (it + 1 < nit) {
+            fetch_rows();
+            if (it + 2 < nit) fetch_positions(chunk_of(it + 2));
+        }
+        if (it < it0) continue;        // look-back chunk: loaded only (next barrier follows the store)
+
+        const bool is_extra = extra && c == k1;
+        const bool has_prev = c > 0;
+
+        // ---------------- phase 1: queries 16*wave + r16 of chunk c
+        {
+            const int qrow = wave * 16 + r16;
+            const int qpos = sm.pos[sl][qrow];
+            typename M::Frag bq[NKS], bd[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                bq[ks] = M::load(&sm.k[sl][KL::off(qrow, ks * KSTEP + g * KPL)]);
+                bd[ks] = *reinterpret_cast<const bf16x8*>(&dof[ks]);
+            }
+            uint32_t q1[NW];
+#pragma unroll
+            for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[sl][qrow * NDW + w], ones);
+            const float lse2 = sm.lse2[qrow], dlt = sm.delta[qrow];
+            // a query whose windows hold only itself has LSE ~ -penalty: then its
+            // self weight is exactly 1/n_r (every round has the same self score);
+            // recomputing it from fp32 numbers near 1e5 would lose 2^-7
+            const bool self_only = lse2 < -0.5f * SELF_PENALTY * LOG2E;
+            const float self_p = 1.f / (float)n_r;
+
+            f32x4 s[NKT], dp[NKT];
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                s[t] = f32x4{};
+                dp[t] = f32x4{};
+                if (t < CT ? !has_prev : is_extra) continue;
+                const int slk = t < CT ? sp : sl;
+                const int krow = (t % CT) * 16 + r16;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int e = ks * KSTEP + g * KPL;
+                    s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, e)]), bq[ks], s[t]);
+                    dp[t] = M::mma(M::load(&sm.v[slk][KL::off(krow, e)]), bd[ks], dp[t]);
+                }
+            }
+            // P and dS (in place of s and dp)
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                if (t < CT ? !has_prev : is_extra) continue;
+                const int slk = t < CT ? sp : sl;
+                const bool diag = t == CT + wave;
+                const int krow0 = (t % CT) * 16 + 4 * g;
+                const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
+                    float nlg = 0.f;
+                    if constexpr (NDW > 0) {
+                        const uint32_t outs8 = rounds_outside8<NDW, false>(
+                            q1, &sm.cid[slk][(krow0 + j) * NDW], nch2);
+                        nlg = *reinterpret_cast<const float*>(
+                            reinterpret_cast<const char*>(sm.neg_log2) + outs8);
+                    }
+                    const bool self = diag && kpos == qpos;
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[t][j], scale_log2, nlg) - lse2);
+                    if (self) p = self_only ? self_p : 0.f;
+                    if (causal && kpos > qpos) p = 0.f;
+                    s[t][j] = p;
+                    dp[t][j] = p * (dp[t][j] - dlt);
+                }
+            }
+            // P and dS to LDS, [window key][query]
+            const int qg = qrow >> 2, qo = 2 * (qrow & 3);
+#pragma unroll
+            for (int t = 0; t < NKT; ++t) {
+                if (t < CT ? !has_prev : is_extra) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int wk = t * 16 + 4 * g + j;
+                    const int off = wk * PROWB + 8 * (qg ^ pswz(wk)) + qo;
+                    *reinterpret_cast<uint16_t*>(sm.p + off) = f32_to_bf16_rne(s[t][j]);
+                    *reinterpret_cast<uint16_t*>(sm.ds + off) = f32_to_bf16_rne(dp[t][j]);
+                }
+            }
+            // dQ^T = K^T dS^T (the extra tile's queries belong to the next run)
+            if (!is_extra) {
+                f32x4 o[DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{};
+#pragma unroll
+                for (int t0 = 0; t0 < NKT; t0 += 2) {
+                    if (t0 < CT && !has_prev) continue;
+                    const int slk = t0 < CT ? sp : sl;
+                    const int kg = ((t0 % CT) * 16 + 4 * g) >> 2;
+                    bf16x8 b;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        b[x] = (__bf16)dp[t0][x];
+                        b[4 + x] = (__bf16)dp[t0 + 1][x];
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const int d = dt * 16 + r16;
+                        const char* kr = sm.kt[slk] + d * TROWB;
+                        const int swz = vt_swz<C>(d);
+                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(kr + 8 * (kg ^ swz));
+                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(kr + 8 * ((kg + 4) ^ swz));
+                        o[dt] = M::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), b, o[dt]);
+                    }
+                }
+                T* orow = dq_r + rbase + (long)qpos * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int d0 = dt * 16 + 4 * g;
+                    const u32x2 w = {pack_bf16x2(o[dt][0] * scale, o[dt][1] * scale),
+                                     pack_bf16x2(o[dt][2] * scale, o[dt][3] * scale)};
+                    *reinterpret_cast<u32x2*>(orow + d0) = w;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---------------- phase 2: keys of the chunk in slot G
+        {
+            const bool cur_role = G == sl;               // slot G holds chunk c, else c - 1
+            const bool active = cur_role ? !is_extra : (has_prev && c != k0);
+            if (cur_role && !is_extra) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int kt = 0; kt < KTW; ++kt) { acck[dt][kt] = f32x4{}; accv[dt][kt] = f32x4{}; }
+            }
+            if (active) {
+                const int wbase = cur_role ? C : 0;      // window rows of this slot's keys
+#pragma unroll
+                for (int kt = 0; kt < KTW; ++kt) {
+                    const int wk = wbase + KSL * sw + 16 * kt + r16;
+                    const char* prow = sm.p + wk * PROWB;
+                    const char* srow = sm.ds + wk * PROWB;
+                    const int psw = pswz(wk);
+#pragma unroll
+                    for (int u0 = 0; u0 < CT; u0 += 2) {
+                        const int qg = ((u0 * 16) >> 2) + g;     // queries 16 u0 + 4g + j and +16
+                        const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(prow + 8 * (qg ^ psw));
+                        const bf16x4 p1 = *reinterpret_cast<const bf16x4*>(prow + 8 * ((qg + 4) ^ psw));
+                        const bf16x4 s0 = *reinterpret_cast<const bf16x4*>(srow + 8 * (qg ^ psw));
+                        const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(srow + 8 * ((qg + 4) ^ psw));
+                        const bf16x8 bp = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 bs = __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) {
+                            const int d = dt * 16 + r16;
+                            const int swz = vt_swz<C>(d);
+                            const char* qr = sm.kt[sl] + d * TROWB;
+                            const char* dr = sm.dot + d * TROWB;
+                            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(qr + 8 * (qg ^ swz));
+                            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(qr + 8 * ((qg + 4) ^ swz));
+                            const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(dr + 8 * (qg ^ swz));
+                            const bf16x4 c1 = *reinterpret_cast<const bf16x4*>(dr + 8 * ((qg + 4) ^ swz));
+                            acck[dt][kt] = M::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                  bs, acck[dt][kt]);
+                            accv[dt][kt] = M::mma(__builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                  bp, accv[dt][kt]);
+                        }
+                    }
+                }
+                if (!cur_role) write_keys();             // chunk c - 1 is complete
+            }
+        }
+        __syncthreads();
+    }
+    // the last chunk of the round has no next tile: its keys are complete
+    if (!extra && G == ((k1 - 1) & 1)) write_keys();
+}
+
+// LSE_i = logsumexp_r lse[r, i]; Delta_i = <d_o_i, o_i>.  One thread per 16 bytes
+// of a row (TPR threads per row, reduced by shuffles within the row's lanes).
+template <int D>
+__global__ __launch_bounds__(256)
+void k_bwd_prep(const bf16_t* __restrict__ o, const bf16_t* __restrict__ d_o,
+                const float* __restrict__ lse, float* __restrict__ lse_c,
+                float* __restrict__ delta, long rows, int L, int n_r)
+{
+    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    const bool ok = row < rows;
+    const long rr = ok ? row : rows - 1;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + rr * D + part * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(d_o + rr * D + part * 8);
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        acc = fmaf(bf16_to_f32((uint16_t)(a[x] & 0xFFFFu)), bf16_to_f32((uint16_t)(b[x] & 0xFFFFu)), acc);
+        acc = fmaf(bf16_to_f32((uint16_t)(a[x] >> 16)), bf16_to_f32((uint16_t)(b[x] >> 16)), acc);
+    }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
+    if (ok && part == 0) {
+        const long bh = rr / L;
+        const int i = (int)(rr % L);
+        float m = -INFINITY;
+        for (int q = 0; q < n_r; ++q) m = fmaxf(m, lse[(bh * n_r + q) * (long)L + i]);
+        float z = 0.f;
+        for (int q = 0; q < n_r; ++q) z += __expf(lse[(bh * n_r + q) * (long)L + i] - m);
+        lse_c[rr] = m + __logf(z);
+        delta[rr] = acc;
+    }
+}
+
+// dqk = sum_r (dq_r + dk_r), dv = sum_r dv_r (fp32).  One thread per 8 elements.
+template <int D>
+__global__ __launch_bounds__(256)
+void k_bwd_reduce(const bf16_t* __restrict__ dq_r, const bf16_t* __restrict__ dk_r,
+                  const bf16_t* __restrict__ dv_r, float* __restrict__ dqk, float* __restrict__ dv,
+                  long rows, int L, int n_r)
+{
+    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    if (row >= rows) return;
+    const long bh = row / L;
+    const int i = (int)(row % L);
+    float aq[8], av[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) { aq[x] = 0.f; av[x] = 0.f; }
+    for (int q = 0; q < n_r; ++q) {
+        const long off = ((bh * n_r + q) * (long)L + i) * D + part * 8;
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dq_r + off));
+        const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dk_r + off));
+        const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dv_r + off));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            aq[2 * x] += bf16_to_f32((uint16_t)(a[x] & 0xFFFFu)) + bf16_to_f32((uint16_t)(b[x] & 0xFFFFu));
+            aq[2 * x + 1] += bf16_to_f32((uint16_t)(a[x] >> 16)) + bf16_to_f32((uint16_t)(b[x] >> 16));
+            av[2 * x] += bf16_to_f32((uint16_t)(c[x] & 0xFFFFu));
+            av[2 * x + 1] += bf16_to_f32((uint16_t)(c[x] >> 16));
+        }
+    }
+    float* oq = dqk + row * D + part * 8;
+    float* ov = dv + row * D + part * 8;
+    __builtin_nontemporal_store(f32x4{aq[0], aq[1], aq[2], aq[3]}, reinterpret_cast<f32x4*>(oq));
+    __builtin_nontemporal_store(f32x4{aq[4], aq[5], aq[6], aq[7]}, reinterpret_cast<f32x4*>(oq + 4));
+    __builtin_nontemporal_store(f32x4{av[0], av[1], av[2], av[3]}, reinterpret_cast<f32x4*>(ov));
+    __builtin_nontemporal_store(f32x4{av[4], av[5], av[6], av[7]}, reinterpret_cast<f32x4*>(ov + 4));
+}
+
+template <int D, int C, int NDW>
+hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s)
+{
+    const int nchunks = a.L / C;
+    const int nruns = (nchunks + BWD_RUN - 1) / BWD_RUN;
+    const long blocks = a.bh * nruns * a.n_r;
+    hipLaunchKernelGGL((k_attn_bwd<D, C, NDW>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
+                       static_cast<const bf16_t*>(a.qk), static_cast<const bf16_t*>(a.v),
+                       static_cast<const bf16_t*>(a.d_o), a.perm, a.cid, a.lse_c, a.delta,
+                       static_cast<bf16_t*>(a.dq_r), static_cast<bf16_t*>(a.dk_r),
+                       static_cast<bf16_t*>(a.dv_r), a.L, a.n_r, a.causal, a.scale,
+                       a.scale * LOG2E, nruns);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s)
+{
+    const long rows = a.bh * a.L;
+    constexpr int RPB = 256 / (D / 8);
+    const unsigned blocks = (unsigned)((rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(a.o), static_cast<const bf16_t*>(a.d_o), a.lse,
+                       a.lse_c, a.delta, rows, a.L, a.n_r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!a.dup) e = launch_bwd_one<D, 64, 0>(a, s);
+    else if (a.n_r <= 2) e = launch_bwd_one<D, 64, 1>(a, s);
+    else if (a.n_r <= 4) e = launch_bwd_one<D, 64, 2>(a, s);
+    else if (a.n_r <= 8) e = launch_bwd_one<D, 64, 4>(a, s);
+    else e = launch_bwd_one<D, 64, 8>(a, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_bwd_reduce<D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(a.dq_r), static_cast<const bf16_t*>(a.dk_r),
+                       static_cast<const bf16_t*>(a.dv_r), a.dqk, a.dv, rows, a.L, a.n_r);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace attn
+
+hipError_t launch_attn_backward(int d_head, const BwdArgs& a, hipStream_t stream)
+{
+    return d_head == 64 ? attn::launch_bwd_d<64>(a, stream) : attn::launch_bwd_d<128>(a, stream);
+}
+
+}  // namespace lshk

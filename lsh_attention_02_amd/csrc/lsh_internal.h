@@ -47,6 +47,29 @@ hipError_t launch_f32_d128(LSH_ATTN_LAUNCH_ARGS);
 hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
                           long bh, int L, int n_rounds, hipStream_t stream);
 
+// Backward of chunk attention + combine (bf16, chunk 64; lsh_attn_bwd.hip).
+struct BwdArgs {
+    const void* qk;
+    const void* v;
+    const void* o;               // combined forward output
+    const void* d_o;             // loss gradient at o
+    const int32_t* perm;
+    const int16_t* cid;
+    const float* lse;            // per-round lse of the forward
+    float* lse_c;                // workspace [bh * L]: combined logsumexp
+    float* delta;                // workspace [bh * L]: <d_o, o>
+    void* dq_r;                  // workspace [bh, n_r, L, d] bf16: query-role partials
+    void* dk_r;                  // workspace: key-role partials
+    void* dv_r;                  // workspace: value partials
+    float* dqk;                  // [bh, L, d] out
+    float* dv;                   // [bh, L, d] out
+    long bh;
+    int L, n_r, causal;
+    float scale;
+    bool dup;                    // duplicate-count term on
+};
+hipError_t launch_attn_backward(int d_head, const BwdArgs& a, hipStream_t stream);
+
 // Layer projections (bf16): rows = B * L; H heads of size D; d_model a multiple of 64.
 hipError_t launch_project_in(const void* x, const void* w_qk, const void* w_v, void* qk, void* v,
                              long rows, int L, int H, int D, int d_model, hipStream_t stream);

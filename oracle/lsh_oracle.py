@@ -416,6 +416,48 @@ def attention_backward(qk: np.ndarray, v: np.ndarray, perm: np.ndarray, cid: np.
             "dv_rounds": dv_r, "o": o, "LSE": LSE, "delta": delta}
 
 
+def attention_backward_one(qk_bh: np.ndarray, v_bh: np.ndarray, do_bh: np.ndarray,
+                           perm_bh: np.ndarray, cid_bh: np.ndarray, pos: int, chunk: int,
+                           causal: bool, scale: float, dup_correct: bool = True):
+    """dqk[pos] and dv[pos] of one (batch row, head) (sampled checks): the terms
+    of attention_backward that reach position pos.  In round r they come from
+    the query chunks whose window holds pos, cid[pos, r] and the one after it;
+    those queries' LSE and Delta are computed from their own rounds first."""
+    n_r, L = perm_bh.shape
+    nchunks = L // chunk
+    need = set()
+    for r in range(n_r):
+        k = int(cid_bh[pos, r])
+        for kk in (k, k + 1):
+            if kk < nchunks:
+                need.update(int(p) for p in perm_bh[r, kk * chunk:(kk + 1) * chunk])
+    LSE = np.full(L, np.nan)
+    delta = np.full(L, np.nan)
+    do_bh = np.asarray(do_bh, dtype=np.float64)
+    for q in sorted(need):
+        o_q = np.empty((n_r, qk_bh.shape[1]))
+        l_q = np.empty(n_r)
+        for r in range(n_r):
+            o_q[r], l_q[r] = attention_one(qk_bh, v_bh, perm_bh, cid_bh, r, q, chunk, causal, scale,
+                                           dup_correct=dup_correct)
+        o, lse_c = combine_rounds(o_q[:, None, :], l_q[:, None])
+        LSE[q] = lse_c[0]
+        delta[q] = float(do_bh[q] @ o[0])
+    dqk = np.zeros(qk_bh.shape[1])
+    dv = np.zeros(qk_bh.shape[1])
+    for r in range(n_r):
+        k = int(cid_bh[pos, r])
+        for kk in (k, k + 1):
+            if kk >= nchunks:
+                continue
+            qi, kj, dq, dk, dvv = chunk_attention_grad(qk_bh, v_bh, do_bh, LSE, delta, perm_bh[r],
+                                                       cid_bh, kk, chunk, causal, scale,
+                                                       dup_correct, False, None, r)
+            dqk += dq[qi == pos].sum(axis=0) + dk[kj == pos].sum(axis=0)
+            dv += dvv[kj == pos].sum(axis=0)
+    return dqk, dv
+
+
 def backward(qk: np.ndarray, v: np.ndarray, R: np.ndarray, d_o: np.ndarray, n_buckets: int,
              chunk: int, causal: bool, scale: Optional[float] = None, dup_correct: bool = True,
              wrap: bool = False, same_bucket: bool = False):

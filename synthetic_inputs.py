@@ -161,3 +161,11 @@ def make_layer_inputs(w: Workload, d_model: int, seed: int | None = None) -> Dic
     R = _normal(rng, (w.n_rounds, d, w.n_buckets // 2))
     return {k: _storage(a, w.dtype) for k, a in
             (("x", x), ("w_qk", w_qk), ("w_v", w_v), ("w_o", w_o), ("R", R))}
+
+
+def make_grad(w: Workload, seed: int | None = None) -> np.ndarray:
+    """A loss gradient at the combined output, d_o [B, H, L, d] ~ N(0, 1), drawn
+    from PCG64(seed, default the workload's seed + 2000) and rounded to
+    ``w.dtype``; float32 array."""
+    rng = np.random.Generator(np.random.PCG64((w.seed + 2000) if seed is None else seed))
+    return _storage(_normal(rng, (w.batch, w.heads, w.seq_len, w.d_head)), w.dtype)

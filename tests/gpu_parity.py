@@ -29,7 +29,7 @@ import torch
 
 import lsh_attention_02_amd as lsh
 import oracle.lsh_oracle as O
-from synthetic_inputs import Workload, make_inputs, make_layer_inputs
+from synthetic_inputs import Workload, make_grad, make_inputs, make_layer_inputs
 
 GATE = {"f32": 1e-5, "bf16": 2e-2}
 LSE_ATOL = {"f32": 2e-5, "bf16": 1e-3}
@@ -272,4 +272,76 @@ def layer_parity(w: Workload, d_model: int, flags: int = 0) -> dict:
     assert rep["y_err"] <= GATE_PROJ, rep
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[layer] {rep}")
+    return rep
+
+
+# --------------------------------------------------------------------------- backward
+# d_qk and d_v are float32 sums of bf16-rounded partial products (P and dS are
+# rounded to bf16 for the MFMA operands, each round's partial gradient is stored
+# in bf16): the error is a few 2^-9 relative, so the bf16 gate applies.
+GATE_BWD = GATE["bf16"]
+
+
+def run_backward(w: Workload, x, d_o: np.ndarray, flags: int = 0, device="cuda:0"):
+    cfg, t, g = run_gpu(w, x, flags=flags, device=device)
+    do_t = torch.from_numpy(d_o).to(device).to(cfg.torch_dtype).contiguous()
+    dqk, dv = lsh.lsh_attn_backward(cfg, t["qk"], t["v"], g["perm"], g["cid"], g["lse"], g["o"], do_t)
+    torch.cuda.synchronize()
+    return cfg, g, dqk, dv
+
+
+def backward_parity(w: Workload, flags: int = 0) -> dict:
+    """GPU d_qk, d_v against the oracle's backward fed the GPU's perm/cid (the
+    sort itself is checked bit-exact in full_parity)."""
+    t0 = time.time()
+    x = make_inputs(w)
+    d_o = make_grad(w)
+    cfg, g, dqk, dv = run_backward(w, x, d_o, flags)
+    gb = to_np(g["buckets"])
+    sp, sc_id = O.sort_rounds(gb, w.n_buckets, w.chunk)
+    assert np.array_equal(to_np(g["perm"]), sp), f"{w.name}: perm differs from the stable sort"
+    ref = O.attention_backward(x["qk"].astype(np.float64), x["v"].astype(np.float64), sp, sc_id,
+                               d_o.astype(np.float64), w.chunk, w.causal, cfg.score_scale,
+                               **variant(flags))
+    rep = {"workload": w.name, "flags": flags}
+    rep["dqk_err"] = rel_err(to_np(dqk), ref["dqk"])
+    rep["dv_err"] = rel_err(to_np(dv), ref["dv"])
+    assert rep["dqk_err"] <= GATE_BWD and rep["dv_err"] <= GATE_BWD, rep
+    assert np.isfinite(to_np(dqk)).all() and np.isfinite(to_np(dv)).all()
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[backward] {rep}")
+    return rep
+
+
+def sampled_backward(w: Workload, n_samples: int = 6, seed: int = 0) -> dict:
+    """Full-size workload: d_qk and d_v at sampled positions against the oracle's
+    single-position gradients (fed the GPU's perm/cid, which sampled_parity
+    checks against the sort's defining properties)."""
+    t0 = time.time()
+    log(f"[sampled-backward] {w.name}: generating inputs")
+    x = make_inputs(w)
+    d_o = make_grad(w)
+    cfg, g, dqk, dv = run_backward(w, x, d_o)
+    gp = to_np(g["perm"])
+    gc = to_np(g["cid"])
+    rng = np.random.default_rng(seed)
+    B, H, L = w.batch, w.heads, w.seq_len
+    sb, sh, si = rng.integers(0, B, n_samples), rng.integers(0, H, n_samples), rng.integers(0, L, n_samples)
+    got_q = to_np(dqk[torch.from_numpy(sb), torch.from_numpy(sh), torch.from_numpy(si)])
+    got_v = to_np(dv[torch.from_numpy(sb), torch.from_numpy(sh), torch.from_numpy(si)])
+    ref_q = np.empty_like(got_q, dtype=np.float64)
+    ref_v = np.empty_like(got_v, dtype=np.float64)
+    for s in range(n_samples):
+        b, h = sb[s], sh[s]
+        log(f"[sampled-backward] sample {s}: b {b} h {h} pos {si[s]} ({time.time() - t0:.1f}s)")
+        ref_q[s], ref_v[s] = O.attention_backward_one(
+            x["qk"][b, h].astype(np.float64), x["v"][b, h].astype(np.float64),
+            d_o[b, h].astype(np.float64), gp[b, h], gc[b, h], int(si[s]), w.chunk, w.causal,
+            cfg.score_scale)
+    rep = {"workload": w.name, "samples": n_samples}
+    rep["dqk_err"] = rel_err(got_q, ref_q)
+    rep["dv_err"] = rel_err(got_v, ref_v)
+    assert rep["dqk_err"] <= GATE_BWD and rep["dv_err"] <= GATE_BWD, rep
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[sampled-backward] {rep}")
     return rep

@@ -442,6 +442,21 @@ def check_backward_dv_sum(seed=42):
     assert np.allclose(g["dqk_rounds"].sum(axis=2), g["dqk"], rtol=0, atol=1e-12)
 
 
+def check_backward_one(seed=45):
+    """The single-position gradients (used by the sampled GPU checks) equal the
+    rows of the full backward."""
+    L, d, nb, chunk = 48, 4, 4, 4
+    for causal in (True, False):
+        qk, v, d_o, buckets = _bwd_case(L, d, 3, nb, seed)
+        perm, cid = O.sort_rounds(buckets, nb, chunk)
+        g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, 0.8)
+        for pos in (0, 5, 17, 47):
+            dq, dv = O.attention_backward_one(qk[0, 0], v[0, 0], d_o[0, 0], perm[0, 0], cid[0, 0],
+                                              pos, chunk, causal, 0.8)
+            assert np.allclose(dq, g["dqk"][0, 0, pos], rtol=0, atol=1e-9)
+            assert np.allclose(dv, g["dv"][0, 0, pos], rtol=0, atol=1e-9)
+
+
 ALL_CHECKS = {
     "hash_demo": check_hash_demo,
     "hash_labels": check_hash_labels,
@@ -481,4 +496,5 @@ ALL_CHECKS = {
     "backward_union_autograd": check_backward_union_autograd,
     "backward_union_autograd_causal": lambda: check_backward_union_autograd(causal=True, n_r=2, seed=44),
     "backward_dv_sum": check_backward_dv_sum,
+    "backward_one": check_backward_one,
 }

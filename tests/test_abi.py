@@ -108,11 +108,13 @@ def test_bad_config_every_call(lib, kw, status, msg):
         lambda: lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL),
         lambda: lib.lsh_chunk_attn(raw(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL),
         lambda: lib.lsh_combine_rounds(raw(c), FAKE, FAKE, FAKE, NULL),
+        lambda: lib.lsh_attn_backward(raw(c), *[FAKE] * 10, 1 << 40, NULL),
     ]
     for call in calls:
         assert call() == status
         assert msg in lib.lsh_last_error().decode()
     assert lib.lsh_sort_workspace_bytes(raw(c)) == 0
+    assert lib.lsh_backward_workspace_bytes(raw(c)) == 0
 
 
 def test_bad_dtype_and_causal(lib):
@@ -185,6 +187,35 @@ def test_projection_config_checks(lib):
     c = cfg(batch=1 << 12, seq_len=1 << 20, chunk=128)      # B * L = 2^32
     assert lib.lsh_project_in(raw(c), 512, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_INVALID_ARG
     assert "2^31" in lib.lsh_last_error().decode()
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_backward_pointer_checks(lib, which):
+    c = cfg()
+    need = lib.lsh_backward_workspace_bytes(raw(c))
+    for bad in (NULL, MISALIGNED):
+        args = [FAKE] * 10
+        args[which] = bad
+        assert lib.lsh_attn_backward(raw(c), *args, need, NULL) == B.LSH_ERR_INVALID_ARG
+
+
+def test_backward_support_and_workspace(lib):
+    for kw in (dict(dtype="f32"), dict(chunk=32), dict(chunk=128),
+               dict(flags=B.LSH_FLAG_WRAP_LOOKBACK), dict(flags=B.LSH_FLAG_SAME_BUCKET)):
+        c = cfg(**kw)
+        assert lib.lsh_backward_workspace_bytes(raw(c)) == 0, kw
+        assert lib.lsh_attn_backward(raw(c), *[FAKE] * 10, 1 << 40, NULL) == B.LSH_ERR_UNSUPPORTED, kw
+    # combined lse and Delta (float32 per token-head), then three bf16 partials
+    # [B, H, n_r, L, d], each part rounded up to 256 bytes
+    def up(x):
+        return (x + 255) // 256 * 256
+    for kw in (dict(), dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8),
+               dict(flags=B.LSH_FLAG_NO_DUP_CORRECTION, heads=3, seq_len=192)):
+        c = cfg(**kw)
+        T = c.batch * c.heads * c.seq_len
+        want = 2 * up(4 * T) + 3 * up(2 * T * c.n_rounds * c.d_head)
+        assert lib.lsh_backward_workspace_bytes(raw(c)) == want, kw
+        assert lib.lsh_attn_backward(raw(c), *[FAKE] * 10, want - 1, NULL) == B.LSH_ERR_WORKSPACE
 
 
 def test_sort_workspace(lib):

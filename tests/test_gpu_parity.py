@@ -206,3 +206,35 @@ def test_workspace_too_small_is_rejected():
     with pytest.raises(lsh.LSHError) as e:
         lsh.lsh_sort(cfg, b, workspace=ws)
     assert e.value.status == lsh.LSH_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------------- backward
+# bf16, chunk 64; several runs of 16 chunks with a ragged last run, one chunk
+# only, one round, an odd number of rounds, both head sizes, and the variant
+# without the duplicate-count term.  Causal cases include positions whose
+# windows hold only themselves.
+BWD_CASES = {
+    "b2h3_L1344_r3_d64_causal": (W("bwd_a", batch=2, heads=3, seq_len=1344, n_buckets=10,
+                                   n_rounds=3, seed=150), 0),
+    "L2048_r4_d128_noncausal": (W("bwd_b", heads=2, seq_len=2048, d_head=128, n_buckets=64,
+                                  n_rounds=4, causal=False, seed=151), 0),
+    "L64_single_chunk_r2": (W("bwd_c", heads=2, seq_len=64, n_buckets=4, seed=152), 0),
+    "L1152_r1_d128": (W("bwd_d", seq_len=1152, d_head=128, n_buckets=16, n_rounds=1, seed=153), 0),
+    "L1088_r5_d64_noncausal": (W("bwd_e", heads=2, seq_len=1088, n_buckets=16, n_rounds=5,
+                                 causal=False, seed=154), 0),
+    "L2048_r8_d128_causal": (W("bwd_f", seq_len=2048, d_head=128, n_buckets=32, n_rounds=8,
+                               seed=155), 0),
+    "no_dup_L1344_r3": (W("bwd_g", heads=2, seq_len=1344, n_buckets=10, n_rounds=3, seed=156),
+                        lsh.LSH_FLAG_NO_DUP_CORRECTION),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_CASES))
+def test_backward_parity(name):
+    w, flags = BWD_CASES[name]
+    GP.backward_parity(w, flags)
+
+
+def test_backward_sampled_paper_64k():
+    """The 64K-token, 8-head, 8-round workload at full size, sampled positions."""
+    GP.sampled_backward(WORKLOADS["paper_64k"], n_samples=4)
