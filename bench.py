@@ -16,6 +16,8 @@ Other modes:
     --layer D_MODEL      time the attention layer instead: the shared-QK and value
                          projections of x [B, L, D_MODEL], the four calls and the
                          output projection (a second workload; no CPU baseline)
+    --backward           time forward + backward (lsh_attn_backward with a synthetic
+                         loss gradient at the output; no CPU baseline)
     --copy-calibration   run only a plain 1 GiB device copy (for scaling the
                          FETCH_SIZE / WRITE_SIZE counters)
     --pmc-summary F W CF CW   turn four rocprofv3 --pmc output folders (FETCH_SIZE
@@ -47,13 +49,16 @@ KERNEL_SOURCES = {
                        "lsh_chunk_attn_bf16_d128.hip", "lsh_chunk_attn_f32_d64.hip",
                        "lsh_chunk_attn_f32_d128.hip", "lsh_device.h"],
     "lsh_combine_rounds": ["lsh_combine.hip", "lsh_device.h"],
+    "lsh_attn_backward": ["lsh_attn_bwd.hip", "lsh_chunk_attn.h", "lsh_device.h"],
     "lsh_project_in": ["lsh_linear.hip", "lsh_device.h"],
     "lsh_project_out": ["lsh_linear.hip", "lsh_device.h"],
 }
 KERNEL_SYMBOLS = {"lsh_hash": "k_hash", "lsh_sort": "k_sort_*", "lsh_chunk_attn": "k_chunk_attn",
-                  "lsh_combine_rounds": "k_combine", "lsh_project_in": "k_linear",
+                  "lsh_combine_rounds": "k_combine", "lsh_attn_backward": "k_attn_bwd",
+                  "lsh_project_in": "k_linear",
                   "lsh_project_out": "k_linear"}
 LAYER_METRIC = "LSH-attention layer fwd tokens/s (projections + the four calls)"
+BACKWARD_METRIC = "LSH-attention fwd+bwd tokens/s (the four calls + lsh_attn_backward)"
 PMC_TRAFFIC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -70,6 +75,11 @@ def algorithmic_work(w, d_model=None):
       project_in   2*(2*H*d)*d_model FLOP per token; reads x and both weights once,
                    writes qk and v
       project_out  2*d_model*H*d FLOP per token; reads o and w_o, writes y
+      backward  20*c*d FLOP per TR (scores, dP, dQ, dK, dV over the 2c-key window);
+                per TR gathers qk, v, d_o rows and writes three bf16 partial rows
+                (6*d*e), reads perm, cid, LSE and Delta (12 + 2*n_r); per T the
+                prep reads o, d_o and n_r lse values and writes LSE, Delta, and the
+                reduce reads 3*n_r partial rows and writes two float32 rows
     """
     e = 2 if w.dtype == "bf16" else 4
     T = w.batch * w.heads * w.seq_len
@@ -84,6 +94,11 @@ def algorithmic_work(w, d_model=None):
         "lsh_combine_rounds": {"flops": 0.0,
                                "bytes": T * (w.n_rounds * (d * e + 4.0) + d * e)},
     }
+    work["lsh_attn_backward"] = {
+        "flops": 20.0 * w.chunk * d * TR,
+        "bytes": TR * (6.0 * d * e + 12 + 2 * w.n_rounds)
+        + T * (2.0 * d * e + 4 * w.n_rounds + 8)
+        + T * (3.0 * w.n_rounds * d * e + 2 * d * 4)}
     if d_model:
         M, hd = w.batch * w.seq_len, w.heads * d
         work["lsh_project_in"] = {"flops": 2.0 * M * 2 * hd * d_model,
@@ -96,7 +111,8 @@ def algorithmic_work(w, d_model=None):
 def bound_of(name, w):
     """Binding roofline of each call at the benchmark sizes: the hash and the
     projections are dense contractions (hundreds to thousands of FLOP per byte),
-    the other three stream memory."""
+    the others stream memory (the backward does about 65 FLOP per byte at
+    the 64K-token workload, far below the MFMA/HBM balance)."""
     return "mfma" if name in ("lsh_hash", "lsh_project_in", "lsh_project_out") else "hbm"
 
 
@@ -261,6 +277,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (gradients of qk and v)")
     ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
                     help="time the attention layer (projections included) at this model width")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -291,7 +309,7 @@ def main():
     import torch
 
     import lsh_attention_02_amd as lsh
-    from synthetic_inputs import WORKLOADS, make_inputs, make_layer_inputs
+    from synthetic_inputs import WORKLOADS, make_grad, make_inputs, make_layer_inputs
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -326,6 +344,17 @@ def main():
         lambda: lsh.lsh_chunk_attn(cfg, qk, v, perm, cid, o_r, lse, stream=stream),
         lambda: lsh.lsh_combine_rounds(cfg, o_r, lse, o, stream=stream),
     ]
+    bwd = args.backward
+    if bwd:
+        if dm:
+            raise SystemExit("--backward and --layer are separate modes")
+        d_o = torch.from_numpy(make_grad(w)).to(dev).to(tdt)
+        d_qk = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+        d_v = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+        bws = lsh.backward_workspace(cfg, dev)
+        names = names + ["lsh_attn_backward"]
+        calls = calls + [lambda: lsh.lsh_attn_backward(cfg, qk, v, perm, cid, lse, o, d_o, d_qk, d_v,
+                                                       workspace=bws, stream=stream)]
     if dm:
         names = ["lsh_project_in"] + names + ["lsh_project_out"]
         calls = ([lambda: lsh.lsh_project_in(cfg, dm, xin, wts[0], wts[1], qk, v, stream=stream)]
@@ -358,6 +387,8 @@ def main():
     per_call = {n: float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
                 for i, n in enumerate(names)}
     assert torch.isfinite((y if dm else o).float()).all().item(), "non-finite output"
+    if bwd:
+        assert torch.isfinite(d_qk).all().item() and torch.isfinite(d_v).all().item(), "non-finite gradient"
 
     tokens = B * L
     value = tokens / (ms_per_step * 1e-3)
@@ -365,7 +396,7 @@ def main():
     roof = roofline_entry(dominant, w, per_call[dominant], dm)
     work = algorithmic_work(w, dm)[dominant]
     # the committed counters were taken on the method without variant flags
-    roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 and not dm else None
+    roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 and not dm and not bwd else None
     roof["kernel"] = KERNEL_SYMBOLS[dominant]
     roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
     kernels = {}
@@ -375,16 +406,17 @@ def main():
         kernels[n] = e
 
     result = {
-        "metric": LAYER_METRIC if dm else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": LAYER_METRIC if dm else BACKWARD_METRIC if bwd else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": d,
                    "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
-                   "causal": w.causal, "flags": args.flags, **({"d_model": dm} if dm else {})},
+                   "causal": w.causal, "flags": args.flags, **({"d_model": dm} if dm else {}),
+                   **({"backward": True} if bwd else {})},
         "roofline": roof, "kernels": kernels,
     }
-    if not args.no_cpu_baseline and not dm:
+    if not args.no_cpu_baseline and not dm and not bwd:
         result["cpu_baseline"] = cpu_baseline(w, x, flags=args.flags)
     print(json.dumps(result), flush=True)
 
