@@ -27,7 +27,9 @@ The steps, in the pages' order:
               else is there, optionally only to earlier positions          [AIS], [ULT], [MOD]
   4. combine  the rounds merged by logsumexp weights                      [ULT], [MOD]
 Also the gradient of steps 3-4 with respect to qk and v (attention_backward),
-by the chain rule through the steps above (the pages print no backward pass).
+by the chain rule through the steps above (the pages print no backward pass);
+the attention layer around the steps (projections); and the Reformer block
+built from it: reversible residual halves with a chunked feed-forward layer.
 
 Readings taken where the pages leave a step open (each is argued in the design
 notes):
@@ -511,3 +513,68 @@ def layer_forward(x: np.ndarray, w_qk: np.ndarray, w_v: np.ndarray, w_o: np.ndar
     out = forward(qk, v, R, n_buckets, chunk, causal, scale=scale, **variants)
     out.update(qk=qk, v=v, y=project_out(out["o"], w_o))
     return out
+
+
+# --------------------------------------------------------------------------- the Reformer block
+# [ULT] "Capas reversibles y división en fragmentos" and [MOD] "Reversible
+# Transformer", "Chunking": the activations are split into two halves (x1, x2);
+# attention updates one half and the feed-forward layer the other,
+#     y1 = x1 + Attention(x2),   y2 = x2 + FeedForward(y1),
+# so the inputs can be recomputed from the outputs in the backward pass,
+#     x2 = y2 - FeedForward(y1),  then  x1 = y1 - Attention(x2),
+# and only the last layer's activations are stored.  The feed-forward layer acts
+# on each position independently, so it is evaluated over chunks of positions
+# (its hidden layer is several times wider than the model: d_ff 4096 at
+# d_model 1024 in [AIS]'s set-up).  The pages do not write the feed-forward
+# out; it is read here as the transformer's position-wise form
+#     FeedForward(x) = relu(x w1^T + b1) w2^T + b2,
+# weights [out, in] like a linear layer's.  Attention(x) is the attention layer
+# above (projections, the four steps, output projection).
+def feed_forward(x: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray,
+                 b2: np.ndarray) -> np.ndarray:
+    """relu(x w1^T + b1) w2^T + b2 in float64, on the last axis of x."""
+    x = np.asarray(x, dtype=np.float64)
+    h = np.maximum(x @ np.asarray(w1, dtype=np.float64).T + np.asarray(b1, dtype=np.float64), 0.0)
+    return h @ np.asarray(w2, dtype=np.float64).T + np.asarray(b2, dtype=np.float64)
+
+
+def feed_forward_chunked(x: np.ndarray, w1, b1, w2, b2, chunk_rows: int) -> np.ndarray:
+    """feed_forward over chunks of chunk_rows positions of x [..., d_model] (rows
+    flattened), one chunk's hidden activations at a time."""
+    x = np.asarray(x, dtype=np.float64)
+    rows = x.reshape(-1, x.shape[-1])
+    out = np.empty((rows.shape[0], np.asarray(w2).shape[0]))
+    for r0 in range(0, rows.shape[0], chunk_rows):
+        out[r0:r0 + chunk_rows] = feed_forward(rows[r0:r0 + chunk_rows], w1, b1, w2, b2)
+    return out.reshape(x.shape[:-1] + (out.shape[-1],))
+
+
+def attention_block(x: np.ndarray, wa: dict, R: np.ndarray, heads: int, n_buckets: int,
+                    chunk: int, causal: bool, scale: Optional[float] = None, **variants):
+    """Attention(x): the attention layer's output y [B, L, d_model].  wa holds
+    w_qk, w_v, w_o."""
+    return layer_forward(x, wa["w_qk"], wa["w_v"], wa["w_o"], R, heads, n_buckets, chunk, causal,
+                         scale=scale, **variants)["y"]
+
+
+def block_forward(x1: np.ndarray, x2: np.ndarray, wa: dict, wf: dict, R: np.ndarray, heads: int,
+                  n_buckets: int, chunk: int, causal: bool, chunk_rows: int,
+                  scale: Optional[float] = None, **variants):
+    """(y1, y2) = (x1 + Attention(x2), x2 + FeedForward(y1)).  wf holds w1, b1, w2, b2."""
+    y1 = np.asarray(x1, dtype=np.float64) + attention_block(x2, wa, R, heads, n_buckets, chunk,
+                                                            causal, scale, **variants)
+    y2 = np.asarray(x2, dtype=np.float64) + feed_forward_chunked(y1, wf["w1"], wf["b1"], wf["w2"],
+                                                                 wf["b2"], chunk_rows)
+    return y1, y2
+
+
+def block_inverse(y1: np.ndarray, y2: np.ndarray, wa: dict, wf: dict, R: np.ndarray, heads: int,
+                  n_buckets: int, chunk: int, causal: bool, chunk_rows: int,
+                  scale: Optional[float] = None, **variants):
+    """The block's inputs recomputed from its outputs: x2 = y2 - FeedForward(y1),
+    then x1 = y1 - Attention(x2)."""
+    x2 = np.asarray(y2, dtype=np.float64) - feed_forward_chunked(y1, wf["w1"], wf["b1"], wf["w2"],
+                                                                 wf["b2"], chunk_rows)
+    x1 = np.asarray(y1, dtype=np.float64) - attention_block(x2, wa, R, heads, n_buckets, chunk,
+                                                            causal, scale, **variants)
+    return x1, x2

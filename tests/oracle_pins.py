@@ -38,6 +38,10 @@ What pins what:
            the oracle's own forward (fixed buckets), and against torch autograd
            of the union closed form (independent code); sum_j dv_j = sum_i d_o_i
            (the combined weights of each query sum to one).
+  block  - the feed-forward layer against Python loops over its definition;
+           chunking over positions (any chunk size, ragged last chunk) changes
+           nothing; the reversible block's inverse recovers its inputs (round
+           trip); zero output weights make the block the identity.
   layer  - both projections against Python loops over their definitions;
          - identity weights reduce the layer to the four steps on the input's
            head slices; permuting heads consistently changes nothing.
@@ -457,6 +461,72 @@ def check_backward_one(seed=45):
             assert np.allclose(dv, g["dv"][0, 0, pos], rtol=0, atol=1e-9)
 
 
+# --------------------------------------------------------------------------- Reformer block
+def _block_case(B=1, L=32, d_model=8, H=2, d=4, d_ff=12, seed=60):
+    rng = np.random.default_rng(seed)
+    hd = H * d
+    wa = {"w_qk": rng.standard_normal((hd, d_model)) / np.sqrt(d_model),
+          "w_v": rng.standard_normal((hd, d_model)) / np.sqrt(d_model),
+          "w_o": rng.standard_normal((d_model, hd)) / np.sqrt(hd)}
+    wf = {"w1": rng.standard_normal((d_ff, d_model)) / np.sqrt(d_model),
+          "b1": rng.standard_normal(d_ff) * 0.5,
+          "w2": rng.standard_normal((d_model, d_ff)) / np.sqrt(d_ff),
+          "b2": rng.standard_normal(d_model) * 0.5}
+    x1 = rng.standard_normal((B, L, d_model))
+    x2 = rng.standard_normal((B, L, d_model))
+    R = rng.standard_normal((2, d, 2))
+    return x1, x2, wa, wf, R
+
+
+def check_feed_forward_brute_force(seed=61):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((2, 5, 3))
+    w1, b1 = rng.standard_normal((7, 3)), rng.standard_normal(7)
+    w2, b2 = rng.standard_normal((3, 7)), rng.standard_normal(3)
+    got = O.feed_forward(x, w1, b1, w2, b2)
+    saw_negative = False
+    for b in range(2):
+        for i in range(5):
+            h = []
+            for f in range(7):
+                a = b1[f] + sum(x[b, i, k] * w1[f, k] for k in range(3))
+                saw_negative |= a < 0
+                h.append(a if a > 0 else 0.0)
+            for n in range(3):
+                want = b2[n] + sum(h[f] * w2[n, f] for f in range(7))
+                assert abs(got[b, i, n] - want) < 1e-12
+    assert saw_negative      # the ReLU is exercised
+
+
+def check_ffn_chunking(seed=62):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((2, 13, 6))
+    w1, b1 = rng.standard_normal((10, 6)), rng.standard_normal(10)
+    w2, b2 = rng.standard_normal((6, 10)), rng.standard_normal(6)
+    full = O.feed_forward(x, w1, b1, w2, b2)
+    for cr in (1, 3, 7, 26, 40):       # 26 rows in all: ragged last chunks, one chunk, larger
+        assert np.allclose(O.feed_forward_chunked(x, w1, b1, w2, b2, cr), full, rtol=0, atol=1e-12)
+
+
+def check_block_round_trip(seed=63):
+    """inverse(forward(x)) = x: the reversible block recomputes its inputs."""
+    for causal in (True, False):
+        x1, x2, wa, wf, R = _block_case(seed=seed)
+        y1, y2 = O.block_forward(x1, x2, wa, wf, R, 2, 4, 4, causal, chunk_rows=5)
+        assert np.max(np.abs(y1 - x1)) > 0.1 and np.max(np.abs(y2 - x2)) > 0.1
+        r1, r2 = O.block_inverse(y1, y2, wa, wf, R, 2, 4, 4, causal, chunk_rows=7)
+        assert np.allclose(r1, x1, rtol=0, atol=1e-10) and np.allclose(r2, x2, rtol=0, atol=1e-10)
+
+
+def check_block_zero_weights(seed=64):
+    """Zero output weights make both branches vanish: the block is the identity."""
+    x1, x2, wa, wf, R = _block_case(seed=seed)
+    wa = dict(wa, w_o=np.zeros_like(wa["w_o"]))
+    wf = dict(wf, w2=np.zeros_like(wf["w2"]), b2=np.zeros_like(wf["b2"]))
+    y1, y2 = O.block_forward(x1, x2, wa, wf, R, 2, 4, 4, True, chunk_rows=8)
+    assert np.array_equal(y1, x1) and np.array_equal(y2, x2)
+
+
 ALL_CHECKS = {
     "hash_demo": check_hash_demo,
     "hash_labels": check_hash_labels,
@@ -497,4 +567,8 @@ ALL_CHECKS = {
     "backward_union_autograd_causal": lambda: check_backward_union_autograd(causal=True, n_r=2, seed=44),
     "backward_dv_sum": check_backward_dv_sum,
     "backward_one": check_backward_one,
+    "feed_forward_brute_force": check_feed_forward_brute_force,
+    "ffn_chunking": check_ffn_chunking,
+    "block_round_trip": check_block_round_trip,
+    "block_zero_weights": check_block_zero_weights,
 }

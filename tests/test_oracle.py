@@ -153,7 +153,31 @@ def _grad_part_zeroed(part):
     return f
 
 
+def _ffn_without_relu(x, w1, b1, w2, b2):
+    x = np.asarray(x, dtype=np.float64)
+    return (x @ w1.T + b1) @ w2.T + b2
+
+
+def _chunked_drops_tail(x, w1, b1, w2, b2, chunk_rows):
+    rows = np.asarray(x, dtype=np.float64).reshape(-1, x.shape[-1])
+    out = np.zeros((rows.shape[0], w2.shape[0]))
+    for r0 in range(0, rows.shape[0] - chunk_rows + 1, chunk_rows):
+        out[r0:r0 + chunk_rows] = O.feed_forward(rows[r0:r0 + chunk_rows], w1, b1, w2, b2)
+    return out.reshape(x.shape[:-1] + (out.shape[-1],))
+
+
+def _inverse_wrong_order(y1, y2, wa, wf, R, heads, nb, chunk, causal, chunk_rows, scale=None, **v):
+    # x1 first, from the output half y2 (not yet inverted): wrong
+    x1 = y1 - O.attention_block(y2, wa, R, heads, nb, chunk, causal, scale, **v)
+    x2 = y2 - O.feed_forward_chunked(y1, wf["w1"], wf["b1"], wf["w2"], wf["b2"], chunk_rows)
+    return x1, x2
+
+
 MUTATIONS = {
+    "feed-forward without ReLU": ("feed_forward", _ffn_without_relu, "feed_forward_brute_force"),
+    "chunked feed-forward drops the ragged tail": ("feed_forward_chunked", _chunked_drops_tail,
+                                                   "ffn_chunking"),
+    "block inverse in the wrong order": ("block_inverse", _inverse_wrong_order, "block_round_trip"),
     "backward drops Delta": ("chunk_attention_grad", _grad_without_delta, "backward_finite_differences"),
     "backward drops the key role": ("chunk_attention_grad", _grad_part_zeroed(3),
                                     "backward_union_autograd"),
