@@ -221,6 +221,42 @@ lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x,
 lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o, const void* w_o,
                            void* y, void* stream);
 
+/*
+ * The Reformer block's pieces (bfloat16, fp32 accumulation, outputs rounded to
+ * nearest even).  [ULT] "Capas reversibles y división en fragmentos", [MOD]
+ * "Reversible Transformer" and "Chunking": the activations are two halves,
+ *   y1 = x1 + Attention(x2),   y2 = x2 + FeedForward(y1),
+ * and the backward pass recomputes the inputs from the outputs,
+ *   x2 = y2 - FeedForward(y1),  x1 = y1 - Attention(x2).
+ * The feed-forward layer acts on each position alone and runs over chunks of
+ * positions (its hidden layer is several times wider than the model; [AIS]:
+ * d_ff 4096 at d_model 1024).  The pages do not write it out; it is the
+ * transformer's position-wise form FeedForward(x) = relu(x w1^T + b1) w2^T + b2.
+ *
+ *   lsh_project_out_add:  y = residual + sign * (lsh_project_out's product):
+ *     the attention half of the block (sign +1), or of its inverse (sign -1).
+ *     residual, y [B, L, d_model]; y may be the same buffer as residual.
+ *   lsh_ffn:  y[m, :] = residual[m, :] + sign * FeedForward(x[m, :]) for the
+ *     rows m < rows of x, residual and y [rows, d_model] (row-major), computed
+ *     chunk_rows rows at a time: one chunk's hidden activations relu(x w1^T +
+ *     b1) are rounded to bf16 in `hidden` (at least lsh_ffn_workspace_bytes()
+ *     bytes) and multiplied by w2 before the next chunk.  w1 [d_ff, d_model],
+ *     b1 [d_ff], w2 [d_model, d_ff], b2 [d_model].  y may be the same buffer
+ *     as residual, or as x.
+ * Errors: as above for lsh_project_out_add (plus sign not finite); lsh_ffn:
+ * rows not in (0, 2^31), d_model or d_ff not a positive multiple of 64 at most
+ * 65536, chunk_rows not positive, sign not finite, a null or misaligned pointer
+ * (LSH_ERR_INVALID_ARG); hidden too small (LSH_ERR_WORKSPACE).
+ */
+lsh_status lsh_project_out_add(const lsh_config* cfg, int32_t d_model, const void* o,
+                               const void* w_o, const void* residual, float sign, void* y,
+                               void* stream);
+size_t lsh_ffn_workspace_bytes(int64_t rows, int32_t d_ff, int32_t chunk_rows);
+lsh_status lsh_ffn(int64_t rows, int32_t d_model, int32_t d_ff, int32_t chunk_rows, const void* x,
+                   const void* w1, const void* b1, const void* w2, const void* b2,
+                   const void* residual, float sign, void* y, void* hidden, size_t hidden_bytes,
+                   void* stream);
+
 /* Static description of a status code. */
 const char* lsh_status_string(lsh_status status);
 

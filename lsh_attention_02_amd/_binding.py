@@ -27,7 +27,8 @@ LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2,
 
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
             "lsh_combine_rounds", "lsh_backward_workspace_bytes", "lsh_attn_backward",
-            "lsh_project_in", "lsh_project_out", "lsh_status_string", "lsh_last_error")
+            "lsh_project_in", "lsh_project_out", "lsh_project_out_add", "lsh_ffn_workspace_bytes",
+            "lsh_ffn", "lsh_status_string", "lsh_last_error")
 
 
 class LSHError(RuntimeError):
@@ -98,8 +99,13 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_attn_backward.argtypes = [CP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.lsh_project_in.argtypes = [CP, I32, P, P, P, P, P, P]
     lib.lsh_project_out.argtypes = [CP, I32, P, P, P, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_project_in",
-              "lsh_project_out"):
+    lib.lsh_project_out_add.argtypes = [CP, I32, P, P, P, ctypes.c_float, P, P]
+    lib.lsh_ffn_workspace_bytes.argtypes = [ctypes.c_int64, I32, I32]
+    lib.lsh_ffn_workspace_bytes.restype = ctypes.c_size_t
+    lib.lsh_ffn.argtypes = [ctypes.c_int64, I32, I32, I32, P, P, P, P, P, P, ctypes.c_float, P, P,
+                            ctypes.c_size_t, P]
+    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_attn_backward",
+              "lsh_project_in", "lsh_project_out", "lsh_project_out_add", "lsh_ffn"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
     lib.lsh_status_string.restype = ctypes.c_char_p
@@ -336,6 +342,90 @@ def lsh_project_out(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torch.Te
     _check(lib.lsh_project_out(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(y),
                                _stream(dev, stream)), "lsh_project_out")
     return y
+
+
+def lsh_project_out_add(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torch.Tensor,
+                        residual: torch.Tensor, sign: float = 1.0, y: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """y = residual + sign * (lsh_project_out's product); y may be residual itself."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(o, "o", sh["o"], cfg.torch_dtype)
+    dev = o.device
+    shape = (cfg.batch, cfg.seq_len, d_model)
+    _expect(w_o, "w_o", (d_model, cfg.heads * cfg.d_head), cfg.torch_dtype, dev)
+    _expect(residual, "residual", shape, cfg.torch_dtype, dev)
+    if y is None:
+        y = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+    _expect(y, "y", shape, cfg.torch_dtype, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_project_out_add(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(residual),
+                                   ctypes.c_float(sign), _ptr(y), _stream(dev, stream)),
+           "lsh_project_out_add")
+    return y
+
+
+def lsh_ffn_workspace_bytes(rows: int, d_ff: int, chunk_rows: int) -> int:
+    return int(load_library().lsh_ffn_workspace_bytes(int(rows), int(d_ff), int(chunk_rows)))
+
+
+def lsh_ffn(x: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor,
+            residual: torch.Tensor, sign: float = 1.0, chunk_rows: int = 8192,
+            y: Optional[torch.Tensor] = None, hidden: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """y = residual + sign * (relu(x w1^T + b1) w2^T + b2) over the rows of x
+    [..., d_model] (bf16), chunk_rows rows at a time; y may be residual or x."""
+    lib = load_library()
+    d_ff, d_model = w1.shape
+    dev = x.device
+    if x.dtype != torch.bfloat16 or x.shape[-1] != d_model or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous bf16 tensor [..., {d_model}]")
+    rows = x.numel() // d_model
+    for t, name, shape in ((w1, "w1", (d_ff, d_model)), (b1, "b1", (d_ff,)), (w2, "w2", (d_model, d_ff)),
+                           (b2, "b2", (d_model,)), (residual, "residual", tuple(x.shape))):
+        _expect(t, name, shape, torch.bfloat16, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _expect(y, "y", tuple(x.shape), torch.bfloat16, dev)
+    need = lsh_ffn_workspace_bytes(rows, d_ff, chunk_rows)
+    if hidden is None:
+        hidden = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+    if hidden.device != dev or not hidden.is_contiguous():
+        raise ValueError("hidden must be a contiguous buffer on the same device")
+    _check(lib.lsh_ffn(int(rows), int(d_model), int(d_ff), int(chunk_rows), _ptr(x), _ptr(w1), _ptr(b1),
+                       _ptr(w2), _ptr(b2), _ptr(residual), ctypes.c_float(sign), _ptr(y), _ptr(hidden),
+                       ctypes.c_size_t(hidden.numel() * hidden.element_size()), _stream(dev, stream)),
+           "lsh_ffn")
+    return y
+
+
+def _attention_into(cfg: LSHConfig, x: torch.Tensor, wa: dict, R: torch.Tensor, residual: torch.Tensor,
+                    sign: float, y: torch.Tensor, workspace, stream):
+    """y = residual + sign * Attention(x), Attention the attention layer."""
+    d_model = x.shape[-1]
+    qk, v = lsh_project_in(cfg, d_model, x, wa["w_qk"], wa["w_v"], stream=stream)
+    o = forward(cfg, qk, v, R, workspace=workspace, stream=stream)
+    return lsh_project_out_add(cfg, d_model, o, wa["w_o"], residual, sign, y, stream=stream)
+
+
+def block_forward(cfg: LSHConfig, x1: torch.Tensor, x2: torch.Tensor, wa: dict, wf: dict,
+                  R: torch.Tensor, chunk_rows: int = 8192, workspace=None, stream=None):
+    """Reformer block: (y1, y2) = (x1 + Attention(x2), x2 + FeedForward(y1)).
+    wa holds w_qk, w_v, w_o; wf holds w1, b1, w2, b2 (see the header)."""
+    y1 = _attention_into(cfg, x2, wa, R, x1, 1.0, None, workspace, stream)
+    y2 = lsh_ffn(y1, wf["w1"], wf["b1"], wf["w2"], wf["b2"], x2, 1.0, chunk_rows, stream=stream)
+    return y1, y2
+
+
+def block_inverse(cfg: LSHConfig, y1: torch.Tensor, y2: torch.Tensor, wa: dict, wf: dict,
+                  R: torch.Tensor, chunk_rows: int = 8192, workspace=None, stream=None,
+                  in_place: bool = False):
+    """The block's inputs recomputed from its outputs: x2 = y2 - FeedForward(y1),
+    then x1 = y1 - Attention(x2).  in_place overwrites y2 with x2 and y1 with x1."""
+    x2 = lsh_ffn(y1, wf["w1"], wf["b1"], wf["w2"], wf["b2"], y2, -1.0, chunk_rows,
+                 y=y2 if in_place else None, stream=stream)
+    x1 = _attention_into(cfg, x2, wa, R, y1, -1.0, y1 if in_place else None, workspace, stream)
+    return x1, x2
 
 
 def layer_forward(cfg: LSHConfig, x: torch.Tensor, w_qk: torch.Tensor, w_v: torch.Tensor,

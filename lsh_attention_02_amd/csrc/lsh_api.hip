@@ -317,8 +317,57 @@ lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o
     LSH_TRY(check_ptr(y, "y"));
     return hip_status(lshk::launch_project_out(o, w_o, y, (long)cfg->batch * cfg->seq_len,
                                                cfg->seq_len, cfg->heads, cfg->d_head, d_model,
-                                               static_cast<hipStream_t>(stream)),
+                                               nullptr, 0.f, static_cast<hipStream_t>(stream)),
                       "lsh_project_out");
+}
+
+lsh_status lsh_project_out_add(const lsh_config* cfg, int32_t d_model, const void* o,
+                               const void* w_o, const void* residual, float sign, void* y,
+                               void* stream)
+{
+    LSH_TRY(check_layer(cfg, d_model));
+    if (!std::isfinite(sign)) return fail(LSH_ERR_INVALID_ARG, "sign must be finite");
+    LSH_TRY(check_ptr(o, "o"));
+    LSH_TRY(check_ptr(w_o, "w_o"));
+    LSH_TRY(check_ptr(residual, "residual"));
+    LSH_TRY(check_ptr(y, "y"));
+    return hip_status(lshk::launch_project_out(o, w_o, y, (long)cfg->batch * cfg->seq_len,
+                                               cfg->seq_len, cfg->heads, cfg->d_head, d_model,
+                                               residual, sign, static_cast<hipStream_t>(stream)),
+                      "lsh_project_out_add");
+}
+
+size_t lsh_ffn_workspace_bytes(int64_t rows, int32_t d_ff, int32_t chunk_rows)
+{
+    if (rows <= 0 || d_ff <= 0 || chunk_rows <= 0) return 0;
+    const int64_t cr = rows < chunk_rows ? rows : chunk_rows;
+    return (size_t)cr * (size_t)d_ff * 2;
+}
+
+lsh_status lsh_ffn(int64_t rows, int32_t d_model, int32_t d_ff, int32_t chunk_rows, const void* x,
+                   const void* w1, const void* b1, const void* w2, const void* b2,
+                   const void* residual, float sign, void* y, void* hidden, size_t hidden_bytes,
+                   void* stream)
+{
+    if (rows <= 0 || rows >= (1LL << 31))
+        return fail(LSH_ERR_INVALID_ARG, "rows must be positive and below 2^31");
+    if (d_model <= 0 || d_model % 64 || d_model > 65536 || d_ff <= 0 || d_ff % 64 || d_ff > 65536)
+        return fail(LSH_ERR_INVALID_ARG, "d_model and d_ff must be positive multiples of 64, at most 65536");
+    if (chunk_rows <= 0) return fail(LSH_ERR_INVALID_ARG, "chunk_rows must be positive");
+    if (!std::isfinite(sign)) return fail(LSH_ERR_INVALID_ARG, "sign must be finite");
+    LSH_TRY(check_ptr(x, "x"));
+    LSH_TRY(check_ptr(w1, "w1"));
+    LSH_TRY(check_ptr(b1, "b1"));
+    LSH_TRY(check_ptr(w2, "w2"));
+    LSH_TRY(check_ptr(b2, "b2"));
+    LSH_TRY(check_ptr(residual, "residual"));
+    LSH_TRY(check_ptr(y, "y"));
+    LSH_TRY(check_ptr(hidden, "hidden"));
+    if (hidden_bytes < lsh_ffn_workspace_bytes(rows, d_ff, chunk_rows))
+        return fail(LSH_ERR_WORKSPACE, "hidden smaller than lsh_ffn_workspace_bytes()");
+    return hip_status(lshk::launch_ffn(x, w1, b1, w2, b2, residual, sign, y, hidden, (long)rows,
+                                       d_model, d_ff, chunk_rows, static_cast<hipStream_t>(stream)),
+                      "lsh_ffn");
 }
 
 }  // extern "C"

@@ -73,7 +73,13 @@ hipError_t launch_attn_backward(int d_head, const BwdArgs& a, hipStream_t stream
 // Layer projections (bf16): rows = B * L; H heads of size D; d_model a multiple of 64.
 hipError_t launch_project_in(const void* x, const void* w_qk, const void* w_v, void* qk, void* v,
                              long rows, int L, int H, int D, int d_model, hipStream_t stream);
+// resid: null, or y = resid + sign * (the projection)
 hipError_t launch_project_out(const void* o, const void* w_o, void* y, long rows, int L, int H,
-                              int D, int d_model, hipStream_t stream);
+                              int D, int d_model, const void* resid, float sign, hipStream_t stream);
+// Position-wise feed-forward over chunks of chunk_rows rows (bf16):
+// y = resid + sign * (relu(x w1^T + b1) w2^T + b2); hidden holds chunk_rows * d_ff.
+hipError_t launch_ffn(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,
+                      const void* resid, float sign, void* y, void* hidden, long rows, int d_model,
+                      int d_ff, int chunk_rows, hipStream_t stream);
 
 }  // namespace lshk

@@ -7,12 +7,18 @@
 //   y[m, n] = sum_k x[m, k] * w[n, k]        (w row-major [N, K], as a linear
 //                                             layer's weight; fp32 accumulation)
 //
-// One bf16 GEMM kernel serves both directions through its addressing:
+// One bf16 GEMM kernel serves every projection through its addressing and its
+// epilogue:
 //   project in   x [B*L, d_model] row-major; output column n = h*d + c of row
 //                m = b*L + i goes to qk/v[b, h, i, c] (the head-major layout of
 //                the attention steps); grid.z picks (w_qk -> qk) or (w_v -> v);
 //   project out  input row m = b*L + i, column k = h*d + c is o[b, h, i, c]
-//                (the heads read in place); output y [B*L, d_model] row-major.
+//                (the heads read in place); output y [B*L, d_model] row-major;
+//   row-major    x [M, K] -> y [M, N], for the Reformer block's feed-forward
+//                layer (Ultralytics "Reformer" glossary, "Capas reversibles y
+//                división en fragmentos"; modulabs-hub notes, "Chunking").
+// Epilogue (EPI bits): + bias[n], then ReLU, then y = residual + sign * value
+// (the reversible block's half update, or its inverse with sign -1).
 //
 // Workgroup tile 128 x 128, K step 64, 4 waves of 64 x 64 (2 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16).  Both operand tiles are row-major in LDS with the
@@ -33,6 +39,7 @@ constexpr int LIN_LOADS = LIN_BM * LIN_PIECES / LIN_THREADS;     // pieces per t
 
 enum { IN_ROWS = 0, IN_HEADS = 1 };
 enum { OUT_ROWS = 0, OUT_HEADS = 1 };
+enum { EPI_BIAS = 1, EPI_RELU = 2, EPI_RESID = 4 };
 
 struct LinShape {
     int M, N, K;        // y [M, N] = x [M, K] * w[N, K]^T
@@ -87,10 +94,11 @@ __device__ __forceinline__ long out_index(const LinShape& s, int m, RowPos p, in
 // stores (8 lanes cover one row) stay conflict-free under any permutation.
 __device__ __forceinline__ int lin_swz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
-template <int IN, int OUT, int D>
+template <int IN, int OUT, int D, int EPI>
 __global__ __launch_bounds__(LIN_THREADS)
 void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
               const bf16_t* __restrict__ w1, bf16_t* __restrict__ y0, bf16_t* __restrict__ y1,
+              const bf16_t* __restrict__ bias, const bf16_t* __restrict__ resid, float sign,
               LinShape s)
 {
     __shared__ __attribute__((aligned(16))) bf16_t sa[2][LIN_BM * LIN_BK];
@@ -229,18 +237,35 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
                 const int n = n0 + 64 * wn + 32 * b + 8 * jg + 4 * kh;   // N is a multiple of 4
                 if (m < s.M && n < s.N) {
                     const f32x16& c = acc[a][b];
-                    const u32x2 v = {pack_bf16x2(c[4 * jg], c[4 * jg + 1]),
-                                     pack_bf16x2(c[4 * jg + 2], c[4 * jg + 3])};
-                    *reinterpret_cast<u32x2*>(y + out_index<OUT, D>(s, m, p, n)) = v;
+                    float e[4] = {c[4 * jg], c[4 * jg + 1], c[4 * jg + 2], c[4 * jg + 3]};
+                    const long oi = out_index<OUT, D>(s, m, p, n);
+                    if constexpr ((EPI & EPI_BIAS) != 0) {
+                        const u32x2 bb = *reinterpret_cast<const u32x2*>(bias + n);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            e[i] += bf16_to_f32((uint16_t)(bb[i >> 1] >> (16 * (i & 1))));
+                    }
+                    if constexpr ((EPI & EPI_RELU) != 0) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) e[i] = fmaxf(e[i], 0.f);
+                    }
+                    if constexpr ((EPI & EPI_RESID) != 0) {
+                        const u32x2 rr = *reinterpret_cast<const u32x2*>(resid + oi);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            e[i] = fmaf(sign, e[i], bf16_to_f32((uint16_t)(rr[i >> 1] >> (16 * (i & 1)))));
+                    }
+                    const u32x2 v = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+                    *reinterpret_cast<u32x2*>(y + oi) = v;
                 }
             }
         }
     }
 }
 
-template <int IN, int OUT, int D>
+template <int IN, int OUT, int D, int EPI>
 hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void* y1, int nmat,
-                  LinShape s, hipStream_t st)
+                  LinShape s, const void* bias, const void* resid, float sign, hipStream_t st)
 {
     s.mt = (s.M + LIN_BM - 1) / LIN_BM;
     s.nt = (s.N + LIN_BN - 1) / LIN_BN;
@@ -248,10 +273,11 @@ hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void*
     const long tiles = (long)nmat * s.mt * s.nt;
     s.per_xcd = (int)((tiles + NXCD - 1) / NXCD);
     const dim3 grid((unsigned)((long)s.per_xcd * NXCD));
-    hipLaunchKernelGGL((k_linear<IN, OUT, D>), grid, dim3(LIN_THREADS), 0, st,
+    hipLaunchKernelGGL((k_linear<IN, OUT, D, EPI>), grid, dim3(LIN_THREADS), 0, st,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w0),
                        static_cast<const bf16_t*>(w1), static_cast<bf16_t*>(y0),
-                       static_cast<bf16_t*>(y1), s);
+                       static_cast<bf16_t*>(y1), static_cast<const bf16_t*>(bias),
+                       static_cast<const bf16_t*>(resid), sign, s);
     return hipGetLastError();
 }
 
@@ -261,16 +287,42 @@ hipError_t launch_project_in(const void* x, const void* w_qk, const void* w_v, v
                              long rows, int L, int H, int D, int d_model, hipStream_t stream)
 {
     const LinShape s{(int)rows, H * D, d_model, L, H, D, 0, 0, 0, 0};
-    return D == 64 ? launch<IN_ROWS, OUT_HEADS, 64>(x, w_qk, w_v, qk, v, 2, s, stream)
-                   : launch<IN_ROWS, OUT_HEADS, 128>(x, w_qk, w_v, qk, v, 2, s, stream);
+    return D == 64 ? launch<IN_ROWS, OUT_HEADS, 64, 0>(x, w_qk, w_v, qk, v, 2, s, nullptr, nullptr, 0.f, stream)
+                   : launch<IN_ROWS, OUT_HEADS, 128, 0>(x, w_qk, w_v, qk, v, 2, s, nullptr, nullptr, 0.f, stream);
 }
 
 hipError_t launch_project_out(const void* o, const void* w_o, void* y, long rows, int L, int H,
-                              int D, int d_model, hipStream_t stream)
+                              int D, int d_model, const void* resid, float sign, hipStream_t stream)
 {
     const LinShape s{(int)rows, d_model, H * D, L, H, D, 0, 0, 0, 0};
-    return D == 64 ? launch<IN_HEADS, OUT_ROWS, 64>(o, w_o, w_o, y, y, 1, s, stream)
-                   : launch<IN_HEADS, OUT_ROWS, 128>(o, w_o, w_o, y, y, 1, s, stream);
+    if (resid)
+        return D == 64 ? launch<IN_HEADS, OUT_ROWS, 64, EPI_RESID>(o, w_o, w_o, y, y, 1, s, nullptr, resid, sign, stream)
+                       : launch<IN_HEADS, OUT_ROWS, 128, EPI_RESID>(o, w_o, w_o, y, y, 1, s, nullptr, resid, sign, stream);
+    return D == 64 ? launch<IN_HEADS, OUT_ROWS, 64, 0>(o, w_o, w_o, y, y, 1, s, nullptr, nullptr, 0.f, stream)
+                   : launch<IN_HEADS, OUT_ROWS, 128, 0>(o, w_o, w_o, y, y, 1, s, nullptr, nullptr, 0.f, stream);
+}
+
+hipError_t launch_ffn(const void* x, const void* w1, const void* b1, const void* w2, const void* b2,
+                      const void* resid, float sign, void* y, void* hidden, long rows, int d_model,
+                      int d_ff, int chunk_rows, hipStream_t stream)
+{
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* rb = static_cast<const bf16_t*>(resid);
+    bf16_t* yb = static_cast<bf16_t*>(y);
+    for (long r0 = 0; r0 < rows; r0 += chunk_rows) {
+        const int cr = (int)(rows - r0 < chunk_rows ? rows - r0 : chunk_rows);
+        // the row-major kernels take L = M: (b, i) never carries
+        const LinShape s1{cr, d_ff, d_model, cr, 1, 64, 0, 0, 0, 0};
+        hipError_t e = launch<IN_ROWS, OUT_ROWS, 64, EPI_BIAS | EPI_RELU>(
+            xb + r0 * d_model, w1, w1, hidden, hidden, 1, s1, b1, nullptr, 0.f, stream);
+        if (e != hipSuccess) return e;
+        const LinShape s2{cr, d_model, d_ff, cr, 1, 64, 0, 0, 0, 0};
+        e = launch<IN_ROWS, OUT_ROWS, 64, EPI_BIAS | EPI_RESID>(
+            hidden, w2, w2, yb + r0 * d_model, yb + r0 * d_model, 1, s2, b2, rb + r0 * d_model, sign,
+            stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace lshk

@@ -169,3 +169,25 @@ def make_grad(w: Workload, seed: int | None = None) -> np.ndarray:
     ``w.dtype``; float32 array."""
     rng = np.random.Generator(np.random.PCG64((w.seed + 2000) if seed is None else seed))
     return _storage(_normal(rng, (w.batch, w.heads, w.seq_len, w.d_head)), w.dtype)
+
+
+def make_block_inputs(w: Workload, d_model: int, d_ff: int, seed: int | None = None) -> Dict[str, np.ndarray]:
+    """Inputs of a Reformer block around workload ``w``: the halves x1, x2
+    [B, L, d_model] ~ N(0, 1); the attention weights w_qk, w_v [H*d, d_model],
+    w_o [d_model, H*d] and the feed-forward weights w1 [d_ff, d_model],
+    w2 [d_model, d_ff] ~ N(0, 1/fan_in); biases b1 [d_ff], b2 [d_model] ~
+    N(0, 0.01); R as in make_inputs.  Drawn in that order from PCG64(seed,
+    default the workload's seed + 3000), rounded to ``w.dtype``; float32 arrays."""
+    rng = np.random.Generator(np.random.PCG64((w.seed + 3000) if seed is None else seed))
+    B, H, L, d = w.batch, w.heads, w.seq_len, w.d_head
+    hd = H * d
+    out = {"x1": _normal(rng, (B, L, d_model)), "x2": _normal(rng, (B, L, d_model)),
+           "w_qk": _normal(rng, (hd, d_model)) * np.float32(1.0 / np.sqrt(d_model)),
+           "w_v": _normal(rng, (hd, d_model)) * np.float32(1.0 / np.sqrt(d_model)),
+           "w_o": _normal(rng, (d_model, hd)) * np.float32(1.0 / np.sqrt(hd)),
+           "w1": _normal(rng, (d_ff, d_model)) * np.float32(1.0 / np.sqrt(d_model)),
+           "b1": _normal(rng, (d_ff,)) * np.float32(0.1),
+           "w2": _normal(rng, (d_model, d_ff)) * np.float32(1.0 / np.sqrt(d_ff)),
+           "b2": _normal(rng, (d_model,)) * np.float32(0.1),
+           "R": _normal(rng, (w.n_rounds, d, w.n_buckets // 2))}
+    return {k: _storage(a, w.dtype) for k, a in out.items()}

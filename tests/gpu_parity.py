@@ -29,7 +29,7 @@ import torch
 
 import lsh_attention_02_amd as lsh
 import oracle.lsh_oracle as O
-from synthetic_inputs import Workload, make_grad, make_inputs, make_layer_inputs
+from synthetic_inputs import Workload, make_block_inputs, make_grad, make_inputs, make_layer_inputs
 
 GATE = {"f32": 1e-5, "bf16": 2e-2}
 LSE_ATOL = {"f32": 2e-5, "bf16": 1e-3}
@@ -344,4 +344,75 @@ def sampled_backward(w: Workload, n_samples: int = 6, seed: int = 0) -> dict:
     assert rep["dqk_err"] <= GATE_BWD and rep["dv_err"] <= GATE_BWD, rep
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[sampled-backward] {rep}")
+    return rep
+
+
+# --------------------------------------------------------------------------- Reformer block
+def ffn_parity(rows: int, d_model: int, d_ff: int, chunk_rows: int, sign: float, seed: int,
+               in_place: bool = False) -> dict:
+    """lsh_ffn against the oracle's feed-forward of the same bf16 inputs."""
+    rng = np.random.default_rng(seed)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to("cuda:0").to(torch.bfloat16).contiguous()
+    x = bf(rng.standard_normal((rows, d_model)))
+    w1 = bf(rng.standard_normal((d_ff, d_model)) / np.sqrt(d_model))
+    b1 = bf(rng.standard_normal(d_ff) * 0.1)
+    w2 = bf(rng.standard_normal((d_model, d_ff)) / np.sqrt(d_ff))
+    b2 = bf(rng.standard_normal(d_model) * 0.1)
+    res = bf(rng.standard_normal((rows, d_model)))
+    res0 = to_np(res).astype(np.float64)
+    y = lsh.lsh_ffn(x, w1, b1, w2, b2, res, sign, chunk_rows, y=res if in_place else None)
+    torch.cuda.synchronize()
+    ref = res0 + sign * O.feed_forward(to_np(x), to_np(w1), to_np(b1), to_np(w2), to_np(b2))
+    rep = {"rows": rows, "d_model": d_model, "d_ff": d_ff, "chunk_rows": chunk_rows, "sign": sign,
+           "in_place": in_place, "err": rel_err(to_np(y), ref)}
+    assert rep["err"] <= GATE_PROJ, rep
+    log(f"[ffn] {rep}")
+    return rep
+
+
+def block_parity(w: Workload, d_model: int, d_ff: int, chunk_rows: int) -> dict:
+    """Layered: the block's forward halves against the oracle fed the GPU's
+    intermediates, then the inverse likewise; the round trip x2 -> y2 -> x2 is
+    exact up to bf16 rounding (no hashing on that path)."""
+    t0 = time.time()
+    x = make_block_inputs(w, d_model, d_ff)
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous() for k, a in x.items()}
+    cfg = cfg_of(w)
+    wa = {k: t[k] for k in ("w_qk", "w_v", "w_o")}
+    wf = {k: t[k] for k in ("w1", "b1", "w2", "b2")}
+    f64 = lambda k: x[k].astype(np.float64)
+    y1, y2 = lsh.block_forward(cfg, t["x1"], t["x2"], wa, wf, t["R"], chunk_rows)
+    # the attention half: the GPU's own attention output of x2 (checked against
+    # the oracle by the layer tests), projected and added by the oracle
+    att = lsh.layer_forward(cfg, t["x2"], wa["w_qk"], wa["w_v"], wa["w_o"], t["R"], return_all=True)
+    torch.cuda.synchronize()
+    rep = {"workload": w.name, "d_model": d_model, "d_ff": d_ff, "chunk_rows": chunk_rows}
+    ref1 = f64("x1") + O.project_out(to_np(att["o"]).astype(np.float64), f64("w_o"))
+    rep["y1_err"] = rel_err(to_np(y1), ref1)
+    ref2 = f64("x2") + O.feed_forward_chunked(to_np(y1), f64("w1"), f64("b1"), f64("w2"), f64("b2"),
+                                              chunk_rows)
+    rep["y2_err"] = rel_err(to_np(y2), ref2)
+    assert rep["y1_err"] <= GATE_PROJ and rep["y2_err"] <= GATE_PROJ, rep
+    # inverse, out of place and in place
+    r1, r2 = lsh.block_inverse(cfg, y1, y2, wa, wf, t["R"], chunk_rows)
+    att2 = lsh.layer_forward(cfg, r2, wa["w_qk"], wa["w_v"], wa["w_o"], t["R"], return_all=True)
+    torch.cuda.synchronize()
+    ref_r2 = to_np(y2).astype(np.float64) - O.feed_forward(to_np(y1), f64("w1"), f64("b1"), f64("w2"),
+                                                           f64("b2"))
+    rep["x2_inverse_err"] = rel_err(to_np(r2), ref_r2)
+    ref_r1 = to_np(y1).astype(np.float64) - O.project_out(to_np(att2["o"]).astype(np.float64), f64("w_o"))
+    rep["x1_inverse_err"] = rel_err(to_np(r1), ref_r1)
+    assert rep["x2_inverse_err"] <= GATE_PROJ and rep["x1_inverse_err"] <= GATE_PROJ, rep
+    rep["x2_round_trip_err"] = rel_err(to_np(r2), f64("x2"))
+    assert rep["x2_round_trip_err"] <= GATE_PROJ, rep
+    d1 = np.abs(to_np(r1).astype(np.float64) - f64("x1"))
+    rep["x1_round_trip_median_err"] = float(np.median(d1) / np.max(np.abs(f64("x1"))))
+    ip1, ip2 = y1.clone(), y2.clone()
+    lsh.block_inverse(cfg, ip1, ip2, wa, wf, t["R"], chunk_rows, in_place=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ip2, r2), "in-place inverse differs (x2)"
+    assert torch.equal(ip1, r1), "in-place inverse differs (x1)"
+    rep["seconds"] = round(time.time() - t0, 1)
+    log(f"[block] {rep}")
     return rep

@@ -218,6 +218,42 @@ def test_backward_support_and_workspace(lib):
         assert lib.lsh_attn_backward(raw(c), *[FAKE] * 10, want - 1, NULL) == B.LSH_ERR_WORKSPACE
 
 
+def test_project_out_add_checks(lib):
+    c = cfg()
+    for which in range(4):
+        args = [FAKE] * 4
+        args[which] = NULL
+        assert lib.lsh_project_out_add(raw(c), 512, args[0], args[1], args[2], ctypes.c_float(1.0),
+                                       args[3], NULL) == B.LSH_ERR_INVALID_ARG
+    assert lib.lsh_project_out_add(raw(c), 512, FAKE, FAKE, FAKE, ctypes.c_float(float("nan")), FAKE,
+                                   NULL) == B.LSH_ERR_INVALID_ARG
+    assert "sign" in lib.lsh_last_error().decode()
+    assert lib.lsh_project_out_add(raw(c), 96, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE,
+                                   NULL) == B.LSH_ERR_INVALID_ARG
+
+
+def _ffn(lib, rows=4096, d_model=512, d_ff=2048, chunk=1024, ptrs=None, sign=1.0, hidden_bytes=1 << 40):
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    return lib.lsh_ffn(rows, d_model, d_ff, chunk, p[0], p[1], p[2], p[3], p[4], p[5],
+                       ctypes.c_float(sign), p[6], p[7], hidden_bytes, NULL)
+
+
+def test_ffn_checks(lib):
+    for kw in (dict(rows=0), dict(rows=1 << 31), dict(d_model=96), dict(d_ff=0), dict(d_ff=65600),
+               dict(chunk=0), dict(sign=float("inf"))):
+        assert _ffn(lib, **kw) == B.LSH_ERR_INVALID_ARG, kw
+    for which in range(8):
+        for bad in (NULL, MISALIGNED):
+            ptrs = [FAKE] * 8
+            ptrs[which] = bad
+            assert _ffn(lib, ptrs=ptrs) == B.LSH_ERR_INVALID_ARG
+    # one chunk's hidden activations in bf16 (fewer rows than a chunk: only those)
+    assert lib.lsh_ffn_workspace_bytes(4096, 2048, 1024) == 1024 * 2048 * 2
+    assert lib.lsh_ffn_workspace_bytes(300, 2048, 1024) == 300 * 2048 * 2
+    assert lib.lsh_ffn_workspace_bytes(0, 2048, 1024) == 0
+    assert _ffn(lib, hidden_bytes=1024 * 2048 * 2 - 1) == B.LSH_ERR_WORKSPACE
+
+
 def test_sort_workspace(lib):
     # tile = smallest power of two >= max(2048, 4 * n_buckets), at most 65536, at most L;
     # one int32 counter per (segment, tile, bucket)

@@ -238,3 +238,30 @@ def test_backward_parity(name):
 def test_backward_sampled_paper_64k():
     """The 64K-token, 8-head, 8-round workload at full size, sampled positions."""
     GP.sampled_backward(WORKLOADS["paper_64k"], n_samples=4)
+
+
+# ---------------------------------------------------------------------- Reformer block
+FFN_CASES = {
+    "rows600_dm192_dff320_chunk256": (600, 192, 320, 256, 1.0, 170, False),
+    "rows1000_dm128_dff512_chunk333_minus": (1000, 128, 512, 333, -1.0, 171, False),
+    "rows4096_dm1024_dff4096_chunk1024": (4096, 1024, 4096, 1024, 1.0, 172, False),
+    "rows700_in_place_one_chunk": (700, 256, 256, 4096, -1.0, 173, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FFN_CASES))
+def test_ffn_parity(name):
+    GP.ffn_parity(*FFN_CASES[name])
+
+
+BLOCK_CASES = {
+    "L512_dm128_dff256_h2_chunkrows200": (W("block_a", heads=2, seq_len=512, n_buckets=16, seed=180),
+                                          128, 256, 200),
+    "paper_shape_L2048_dm1024_dff4096": (W("block_b", heads=8, seq_len=2048, d_head=128,
+                                           n_buckets=64, n_rounds=2, seed=181), 1024, 4096, 512),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_CASES))
+def test_block_parity(name):
+    GP.block_parity(*BLOCK_CASES[name])
