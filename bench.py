@@ -16,6 +16,10 @@ Other modes:
     --layer D_MODEL      time the attention layer instead: the shared-QK and value
                          projections of x [B, L, D_MODEL], the four calls and the
                          output projection (a second workload; no CPU baseline)
+    --block D_MODEL      time one Reformer block forward and its input recompute
+                         (the reversible inverse) at this model width, feed-forward
+                         width --d-ff (default 4 x D_MODEL), --chunk-rows rows per
+                         feed-forward chunk (no CPU baseline)
     --backward           time forward + backward (lsh_attn_backward with a synthetic
                          loss gradient at the output; no CPU baseline)
     --copy-calibration   run only a plain 1 GiB device copy (for scaling the
@@ -52,17 +56,21 @@ KERNEL_SOURCES = {
     "lsh_attn_backward": ["lsh_attn_bwd.hip", "lsh_chunk_attn.h", "lsh_device.h"],
     "lsh_project_in": ["lsh_linear.hip", "lsh_device.h"],
     "lsh_project_out": ["lsh_linear.hip", "lsh_device.h"],
+    "lsh_project_out_add": ["lsh_linear.hip", "lsh_device.h"],
+    "lsh_ffn": ["lsh_linear.hip", "lsh_device.h"],
 }
 KERNEL_SYMBOLS = {"lsh_hash": "k_hash", "lsh_sort": "k_sort_*", "lsh_chunk_attn": "k_chunk_attn",
                   "lsh_combine_rounds": "k_combine", "lsh_attn_backward": "k_attn_bwd",
-                  "lsh_project_in": "k_linear",
+                  "lsh_project_in": "k_linear", "lsh_project_out_add": "k_linear",
+                  "lsh_ffn": "k_linear",
                   "lsh_project_out": "k_linear"}
 LAYER_METRIC = "LSH-attention layer fwd tokens/s (projections + the four calls)"
 BACKWARD_METRIC = "LSH-attention fwd+bwd tokens/s (the four calls + lsh_attn_backward)"
+BLOCK_METRIC = "Reformer block fwd + input recompute tokens/s (reversible halves, chunked FFN)"
 PMC_TRAFFIC = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
-def algorithmic_work(w, d_model=None):
+def algorithmic_work(w, d_model=None, d_ff=None):
     """Algorithmic FLOPs and HBM bytes per launch of each call.
 
     TR = token-head-rounds, T = token-heads, e = bytes per element.
@@ -75,6 +83,9 @@ def algorithmic_work(w, d_model=None):
       project_in   2*(2*H*d)*d_model FLOP per token; reads x and both weights once,
                    writes qk and v
       project_out  2*d_model*H*d FLOP per token; reads o and w_o, writes y
+                   (project_out_add also reads the residual)
+      ffn      2*2*d_model*d_ff FLOP per token; reads x, the residual and the
+               weights, writes y (the hidden chunk stays out of the count)
       backward  20*c*d FLOP per TR (scores, dP, dQ, dK, dV over the 2c-key window);
                 per TR gathers qk, v, d_o rows and writes three bf16 partial rows
                 (6*d*e), reads perm, cid, LSE and Delta (12 + 2*n_r); per T the
@@ -105,6 +116,12 @@ def algorithmic_work(w, d_model=None):
                                   "bytes": e * (M * d_model + 2.0 * hd * d_model + 2.0 * M * hd)}
         work["lsh_project_out"] = {"flops": 2.0 * M * d_model * hd,
                                    "bytes": e * (M * hd + d_model * hd + 1.0 * M * d_model)}
+        work["lsh_project_out_add"] = {"flops": 2.0 * M * d_model * hd,
+                                       "bytes": e * (M * hd + d_model * hd + 2.0 * M * d_model)}
+    if d_model and d_ff:
+        M = w.batch * w.seq_len
+        work["lsh_ffn"] = {"flops": 4.0 * M * d_model * d_ff,
+                           "bytes": e * (3.0 * M * d_model + 2.0 * d_model * d_ff + d_ff + d_model)}
     return work
 
 
@@ -113,11 +130,12 @@ def bound_of(name, w):
     projections are dense contractions (hundreds to thousands of FLOP per byte),
     the others stream memory (the backward does about 65 FLOP per byte at
     the 64K-token workload, far below the MFMA/HBM balance)."""
-    return "mfma" if name in ("lsh_hash", "lsh_project_in", "lsh_project_out") else "hbm"
+    return "mfma" if name in ("lsh_hash", "lsh_project_in", "lsh_project_out", "lsh_project_out_add",
+                             "lsh_ffn") else "hbm"
 
 
-def roofline_entry(name, w, ms, d_model=None):
-    work = algorithmic_work(w, d_model)[name]
+def roofline_entry(name, w, ms, d_model=None, d_ff=None):
+    work = algorithmic_work(w, d_model, d_ff)[name]
     if bound_of(name, w) == "mfma":
         ach = work["flops"] / (ms * 1e-3) / 1e12
         peak = PEAK_MFMA_TFLOPS[w.dtype]
@@ -277,6 +295,10 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", type=int, default=0, metavar="D_MODEL",
+                    help="time a Reformer block forward + its input recompute at this model width")
+    ap.add_argument("--d-ff", type=int, default=0, help="feed-forward width (default 4 x D_MODEL)")
+    ap.add_argument("--chunk-rows", type=int, default=8192, help="positions per feed-forward chunk")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (gradients of qk and v)")
     ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
@@ -309,17 +331,32 @@ def main():
     import torch
 
     import lsh_attention_02_amd as lsh
-    from synthetic_inputs import WORKLOADS, make_grad, make_inputs, make_layer_inputs
+    from synthetic_inputs import (WORKLOADS, make_block_inputs, make_grad, make_inputs,
+                                  make_layer_inputs)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    dm = args.layer
-    x = make_layer_inputs(w, dm) if dm else make_inputs(w)
+    blk = args.block
+    if blk and (args.layer or args.backward):
+        raise SystemExit("--block, --layer and --backward are separate modes")
+    dm = args.layer or blk
+    dff = (args.d_ff or 4 * blk) if blk else None
+    x = (make_block_inputs(w, dm, dff) if blk else make_layer_inputs(w, dm)) if dm else make_inputs(w)
     cfg = lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
                         w.causal, dtype=w.dtype, flags=args.flags)
     tdt = cfg.torch_dtype
     B, H, L, d, nr = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
-    if dm:
+    if blk:
+        bt = {k: torch.from_numpy(a).to(dev).to(tdt) for k, a in x.items()}
+        xin = bt["x2"]
+        wts = [bt["w_qk"], bt["w_v"], bt["w_o"]]
+        qk = torch.empty((B, H, L, d), dtype=tdt, device=dev)
+        v = torch.empty((B, H, L, d), dtype=tdt, device=dev)
+        y1, y2, r1, r2 = (torch.empty((B, L, dm), dtype=tdt, device=dev) for _ in range(4))
+        hidden = torch.empty(lsh.lsh_ffn_workspace_bytes(B * L, dff, args.chunk_rows), dtype=torch.uint8,
+                             device=dev)
+        y = r1
+    elif dm:
         xin = torch.from_numpy(x["x"]).to(dev).to(tdt)
         wts = [torch.from_numpy(x[k]).to(dev).to(tdt) for k in ("w_qk", "w_v", "w_o")]
         qk = torch.empty((B, H, L, d), dtype=tdt, device=dev)
@@ -355,7 +392,24 @@ def main():
         names = names + ["lsh_attn_backward"]
         calls = calls + [lambda: lsh.lsh_attn_backward(cfg, qk, v, perm, cid, lse, o, d_o, d_qk, d_v,
                                                        workspace=bws, stream=stream)]
-    if dm:
+    if blk:
+        # forward: y1 = x1 + Attention(x2), y2 = x2 + FFN(y1); then the recompute
+        # x2 = y2 - FFN(y1), x1 = y1 - Attention(x2) (into r2, r1)
+        core_names, core_calls = names, calls
+        ffn = lambda xx, res, sign, out: lsh.lsh_ffn(xx, bt["w1"], bt["b1"], bt["w2"], bt["b2"], res, sign,
+                                                     args.chunk_rows, y=out, hidden=hidden, stream=stream)
+        names = (["fwd:lsh_project_in"] + ["fwd:" + n for n in core_names]
+                 + ["fwd:lsh_project_out_add", "fwd:lsh_ffn", "inv:lsh_ffn", "inv:lsh_project_in"]
+                 + ["inv:" + n for n in core_names] + ["inv:lsh_project_out_add"])
+        calls = ([lambda: lsh.lsh_project_in(cfg, dm, bt["x2"], wts[0], wts[1], qk, v, stream=stream)]
+                 + core_calls
+                 + [lambda: lsh.lsh_project_out_add(cfg, dm, o, wts[2], bt["x1"], 1.0, y1, stream=stream),
+                    lambda: ffn(y1, bt["x2"], 1.0, y2),
+                    lambda: ffn(y1, y2, -1.0, r2),
+                    lambda: lsh.lsh_project_in(cfg, dm, r2, wts[0], wts[1], qk, v, stream=stream)]
+                 + core_calls
+                 + [lambda: lsh.lsh_project_out_add(cfg, dm, o, wts[2], y1, -1.0, r1, stream=stream)])
+    elif dm:
         names = ["lsh_project_in"] + names + ["lsh_project_out"]
         calls = ([lambda: lsh.lsh_project_in(cfg, dm, xin, wts[0], wts[1], qk, v, stream=stream)]
                  + calls + [lambda: lsh.lsh_project_out(cfg, dm, o, wts[2], y, stream=stream)])
@@ -392,27 +446,32 @@ def main():
 
     tokens = B * L
     value = tokens / (ms_per_step * 1e-3)
+    kind = lambda n: n.split(":")[-1]         # block mode: "fwd:" / "inv:" prefixes
     dominant = max(per_call, key=per_call.get)
-    roof = roofline_entry(dominant, w, per_call[dominant], dm)
-    work = algorithmic_work(w, dm)[dominant]
+    roof = roofline_entry(kind(dominant), w, per_call[dominant], dm, dff)
+    work = algorithmic_work(w, dm, dff)[kind(dominant)]
     # the committed counters were taken on the method without variant flags
     roof["traffic"] = traffic_for(dominant, w.name) if args.flags == 0 and not dm and not bwd else None
-    roof["kernel"] = KERNEL_SYMBOLS[dominant]
+    roof["kernel"] = KERNEL_SYMBOLS[kind(dominant)]
+    if blk:
+        roof["call"] = dominant
     roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
     kernels = {}
     for n in names:
-        e = roofline_entry(n, w, per_call[n], dm)
+        e = roofline_entry(kind(n), w, per_call[n], dm, dff)
         e["ms"] = round(per_call[n], 4)
         kernels[n] = e
 
     result = {
-        "metric": LAYER_METRIC if dm else BACKWARD_METRIC if bwd else METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": (BLOCK_METRIC if blk else LAYER_METRIC if dm else BACKWARD_METRIC if bwd else METRIC),
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": d,
                    "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
                    "causal": w.causal, "flags": args.flags, **({"d_model": dm} if dm else {}),
+                   **({"d_ff": dff, "chunk_rows": args.chunk_rows} if blk else {}),
                    **({"backward": True} if bwd else {})},
         "roofline": roof, "kernels": kernels,
     }
