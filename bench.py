@@ -298,7 +298,7 @@ def main():
     ap.add_argument("--block", type=int, default=0, metavar="D_MODEL",
                     help="time a Reformer block forward + its input recompute at this model width")
     ap.add_argument("--d-ff", type=int, default=0, help="feed-forward width (default 4 x D_MODEL)")
-    ap.add_argument("--chunk-rows", type=int, default=8192, help="positions per feed-forward chunk")
+    ap.add_argument("--chunk-rows", type=int, default=16384, help="positions per feed-forward chunk")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (gradients of qk and v)")
     ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",

@@ -32,9 +32,10 @@ CXXFLAGS = [
 # MFMA results in ordinary VGPRs: the attention kernel reads its score and
 # output accumulators with VALU instructions, and accumulation registers would
 # add a copy per value.  Not for the backward, whose live set exceeds the 256
-# ordinary VGPRs (its key-gradient accumulators live in accumulation registers).
+# ordinary VGPRs (its key-gradient accumulators live in accumulation registers),
+# nor for the 256 x 256 GEMM tiles (256 accumulators per lane).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-NO_VGPR_FORM = {"lsh_attn_bwd.hip"}
+NO_VGPR_FORM = {"lsh_attn_bwd.hip", "lsh_gemm256.hip"}
 
 
 def hipcc() -> str:

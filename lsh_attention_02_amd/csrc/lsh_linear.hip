@@ -28,71 +28,17 @@
 // one is multiplied (two register sets, two LDS buffers, one barrier per step).
 #include "lsh_device.h"
 #include "lsh_internal.h"
+#include "lsh_linear.h"
 
 namespace lshk {
 namespace {
+
+using namespace lin;
 
 constexpr int LIN_BM = 128, LIN_BN = 128, LIN_BK = 64;
 constexpr int LIN_THREADS = 256;
 constexpr int LIN_PIECES = LIN_BK / 8;                           // 16-byte pieces per tile row
 constexpr int LIN_LOADS = LIN_BM * LIN_PIECES / LIN_THREADS;     // pieces per thread per operand
-
-enum { IN_ROWS = 0, IN_HEADS = 1 };
-enum { OUT_ROWS = 0, OUT_HEADS = 1 };
-enum { EPI_BIAS = 1, EPI_RELU = 2, EPI_RESID = 4 };
-
-struct LinShape {
-    int M, N, K;        // y [M, N] = x [M, K] * w[N, K]^T
-    int L, H, D;        // sequence length, heads, head size (head-major addressing)
-    int mt, nt;         // tiles along M and N
-    int nmat;           // matrices (2: the qk and v projections share one launch)
-    int per_xcd;        // tiles per XCD (see the tile mapping in k_linear)
-};
-
-constexpr int NXCD = 8;
-
-// Row m = b*L + i of a tile whose first row m0 = b0*L + i0: (b, i) by carrying
-// from (b0, i0), so the division by L happens once per tile.
-struct RowPos { int b, i; };
-
-__device__ __forceinline__ RowPos row_pos(RowPos base, int r, int L)
-{
-    RowPos p{base.b, base.i + r};
-    while (p.i >= L) { p.i -= L; ++p.b; }        // at most 128 / L steps
-    return p;
-}
-
-// Address of the 8 input elements x[m, k .. k+7] (k a multiple of 8, inside one
-// head of D elements).
-template <int IN, int D>
-__device__ __forceinline__ const bf16_t* in_ptr(const bf16_t* x, const LinShape& s, int m,
-                                                RowPos p, int k)
-{
-    if constexpr (IN == IN_ROWS) {
-        return x + (long)m * s.K + k;
-    } else {
-        const int h = k / D, c = k % D;
-        return x + (((long)p.b * s.H + h) * s.L + p.i) * D + c;
-    }
-}
-
-template <int OUT, int D>
-__device__ __forceinline__ long out_index(const LinShape& s, int m, RowPos p, int n)
-{
-    if constexpr (OUT == OUT_ROWS) {
-        return (long)m * s.N + n;
-    } else {
-        const int h = n / D, c = n % D;
-        return (((long)p.b * s.H + h) * s.L + p.i) * D + c;
-    }
-}
-
-// The LDS has 64 banks of 4 bytes and serves a 16-byte read for 16 lanes per
-// clock.  An operand read takes one 16-byte piece of 16 consecutive rows: rows
-// alternate between the two 32-bank halves (a row is 128 bytes), and XOR with
-// (row / 2) % 8 gives the 8 rows of each half 8 different pieces.  The row
-// stores (8 lanes cover one row) stay conflict-free under any permutation.
-__device__ __forceinline__ int lin_swz(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
 template <int IN, int OUT, int D, int EPI>
 __global__ __launch_bounds__(LIN_THREADS)
@@ -108,7 +54,7 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
     // each XCD has its own L2.  Each XCD takes a contiguous run of tiles in
     // (matrix, row tile, column tile) order, so the column tiles that share an
     // input row tile run on one XCD and read it from its L2.
-    const int t = (blockIdx.x % NXCD) * s.per_xcd + blockIdx.x / NXCD;
+    const int t = xcd_tile(blockIdx.x, s.per_xcd);
     if (t >= s.nmat * s.mt * s.nt) return;            // padding of the last XCD's run
     const int z = t / (s.mt * s.nt), tm = (t / s.nt) % s.mt, tn = t % s.nt;
     const bf16_t* __restrict__ w = z ? w1 : w0;
@@ -237,36 +183,26 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
                 const int n = n0 + 64 * wn + 32 * b + 8 * jg + 4 * kh;   // N is a multiple of 4
                 if (m < s.M && n < s.N) {
                     const f32x16& c = acc[a][b];
-                    float e[4] = {c[4 * jg], c[4 * jg + 1], c[4 * jg + 2], c[4 * jg + 3]};
-                    const long oi = out_index<OUT, D>(s, m, p, n);
-                    if constexpr ((EPI & EPI_BIAS) != 0) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2*>(bias + n);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            e[i] += bf16_to_f32((uint16_t)(bb[i >> 1] >> (16 * (i & 1))));
-                    }
-                    if constexpr ((EPI & EPI_RELU) != 0) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) e[i] = fmaxf(e[i], 0.f);
-                    }
-                    if constexpr ((EPI & EPI_RESID) != 0) {
-                        const u32x2 rr = *reinterpret_cast<const u32x2*>(resid + oi);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            e[i] = fmaf(sign, e[i], bf16_to_f32((uint16_t)(rr[i >> 1] >> (16 * (i & 1)))));
-                    }
-                    const u32x2 v = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
-                    *reinterpret_cast<u32x2*>(y + oi) = v;
+                    store4<OUT, D, EPI>(y, s, m, p, n, c[4 * jg], c[4 * jg + 1], c[4 * jg + 2],
+                                        c[4 * jg + 3], bias, resid, sign);
                 }
             }
         }
     }
 }
 
+// Launches with at least one 256 x 256 tile per CU take the larger tiles
+// (half the LDS and L2 traffic per MFMA); smaller ones keep 128 x 128 tiles
+// to fill the chip.
+constexpr long BIG_MIN_TILES = 256;
+
 template <int IN, int OUT, int D, int EPI>
 hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void* y1, int nmat,
                   LinShape s, const void* bias, const void* resid, float sign, hipStream_t st)
 {
+    const long big = (long)nmat * ((s.M + 255) / 256) * ((s.N + 255) / 256);
+    if (big >= BIG_MIN_TILES)
+        return launch_big<IN, OUT, D, EPI>(x, w0, w1, y0, y1, nmat, s, bias, resid, sign, st);
     s.mt = (s.M + LIN_BM - 1) / LIN_BM;
     s.nt = (s.N + LIN_BN - 1) / LIN_BN;
     s.nmat = nmat;

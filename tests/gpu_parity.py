@@ -416,3 +416,67 @@ def block_parity(w: Workload, d_model: int, d_ff: int, chunk_rows: int) -> dict:
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[block] {rep}")
     return rep
+
+
+# --------------------------------------------------------------------------- large GEMM launches
+def _sample_rows(n_rows: int, n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(n_rows, size=min(n, n_rows), replace=False)
+    return np.sort(np.concatenate([rows, [0, n_rows - 1]]).astype(np.int64))
+
+
+def projections_sampled(w: Workload, d_model: int, n_samples: int = 96) -> dict:
+    """lsh_project_in / lsh_project_out / lsh_project_out_add at sizes that take the
+    256 x 256 tiles, against the oracle on sampled rows (b, i)."""
+    x = make_layer_inputs(w, d_model)
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(a).to(dev).to(torch.bfloat16).contiguous() for k, a in x.items()}
+    cfg = cfg_of(w)
+    B, H, L, d = w.batch, w.heads, w.seq_len, w.d_head
+    qk, v = lsh.lsh_project_in(cfg, d_model, t["x"], t["w_qk"], t["w_v"])
+    rng = np.random.default_rng(7)
+    o = torch.from_numpy(rng.standard_normal((B, H, L, d)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    res = torch.from_numpy(rng.standard_normal((B, L, d_model)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    y = lsh.lsh_project_out(cfg, d_model, o, t["w_o"])
+    ya = lsh.lsh_project_out_add(cfg, d_model, o, t["w_o"], res, -1.0)
+    torch.cuda.synchronize()
+    rows = _sample_rows(B * L, n_samples, 11)
+    bi, ii = rows // L, rows % L
+    xs = x["x"][bi, ii].astype(np.float64)                                 # [S, d_model]
+    ref_qk = (xs @ x["w_qk"].astype(np.float64).T).reshape(len(rows), H, d)
+    ref_v = (xs @ x["w_v"].astype(np.float64).T).reshape(len(rows), H, d)
+    got_qk = to_np(qk)[bi, :, ii]                                          # [S, H, d]
+    got_v = to_np(v)[bi, :, ii]
+    on = to_np(o)[bi, :, ii].reshape(len(rows), H * d).astype(np.float64)  # merge_heads of the rows
+    ref_y = on @ x["w_o"].astype(np.float64).T
+    ref_ya = to_np(res)[bi, ii].astype(np.float64) - ref_y
+    rep = {"workload": w.name, "d_model": d_model, "rows": B * L,
+           "qk_err": rel_err(got_qk, ref_qk), "v_err": rel_err(got_v, ref_v),
+           "y_err": rel_err(to_np(y)[bi, ii], ref_y), "y_add_err": rel_err(to_np(ya)[bi, ii], ref_ya)}
+    assert max(rep["qk_err"], rep["v_err"], rep["y_err"], rep["y_add_err"]) <= GATE_PROJ, rep
+    log(f"[projections-sampled] {rep}")
+    return rep
+
+
+def ffn_sampled(rows: int, d_model: int, d_ff: int, chunk_rows: int, seed: int,
+                n_samples: int = 96) -> dict:
+    """lsh_ffn at sizes that take the 256 x 256 tiles, against the oracle on
+    sampled rows."""
+    rng = np.random.default_rng(seed)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to("cuda:0").to(torch.bfloat16).contiguous()
+    x = bf(rng.standard_normal((rows, d_model)))
+    w1 = bf(rng.standard_normal((d_ff, d_model)) / np.sqrt(d_model))
+    b1 = bf(rng.standard_normal(d_ff) * 0.1)
+    w2 = bf(rng.standard_normal((d_model, d_ff)) / np.sqrt(d_ff))
+    b2 = bf(rng.standard_normal(d_model) * 0.1)
+    res = bf(rng.standard_normal((rows, d_model)))
+    y = lsh.lsh_ffn(x, w1, b1, w2, b2, res, 1.0, chunk_rows)
+    torch.cuda.synchronize()
+    sel = _sample_rows(rows, n_samples, seed)
+    ref = to_np(res)[sel].astype(np.float64) + O.feed_forward(to_np(x)[sel], to_np(w1), to_np(b1),
+                                                              to_np(w2), to_np(b2))
+    rep = {"rows": rows, "d_model": d_model, "d_ff": d_ff, "chunk_rows": chunk_rows,
+           "err": rel_err(to_np(y)[sel], ref)}
+    assert rep["err"] <= GATE_PROJ, rep
+    log(f"[ffn-sampled] {rep}")
+    return rep

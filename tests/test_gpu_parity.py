@@ -265,3 +265,24 @@ BLOCK_CASES = {
 @pytest.mark.parametrize("name", sorted(BLOCK_CASES))
 def test_block_parity(name):
     GP.block_parity(*BLOCK_CASES[name])
+
+
+# ---------------------------------------------------------------------- large GEMM launches
+# Sizes that take the 256 x 256 tiles (at least 256 such tiles per launch), with
+# a ragged last row tile (16448 = 64 x 257 rows), checked on sampled rows.
+def test_projections_big_tiles_sampled():
+    GP.projections_sampled(W("proj_big", heads=8, seq_len=16448, d_head=128, n_buckets=64,
+                             seed=190), 1024)
+
+
+def test_projections_big_tiles_d64_sampled():
+    GP.projections_sampled(W("proj_big64", batch=2, heads=16, seq_len=8256, d_head=64,
+                             n_buckets=64, seed=191), 1024)
+
+
+def test_ffn_big_tiles_sampled():
+    GP.ffn_sampled(16448, 1024, 4096, 16448, 192)
+
+
+def test_ffn_big_tiles_chunked_sampled():
+    GP.ffn_sampled(40000, 1024, 4096, 16384, 193)
