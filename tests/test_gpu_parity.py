@@ -240,6 +240,16 @@ def test_backward_sampled_paper_64k():
     GP.sampled_backward(WORKLOADS["paper_64k"], n_samples=4)
 
 
+def test_backward_short_4k():
+    """The 4K-token, 8-head workload (d 64, causal), every gradient."""
+    GP.backward_parity(WORKLOADS["short_4k"])
+
+
+def test_backward_sampled_clustered_16k():
+    """The clustered workload (batch 2, d 64, non-causal, 4 rounds), sampled positions."""
+    GP.sampled_backward(WORKLOADS["clustered_16k"], n_samples=4)
+
+
 # ---------------------------------------------------------------------- Reformer block
 FFN_CASES = {
     "rows600_dm192_dff320_chunk256": (600, 192, 320, 256, 1.0, 170, False),
