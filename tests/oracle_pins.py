@@ -389,20 +389,23 @@ def _bwd_case(L=16, d=3, n_r=2, nb=4, seed=40):
     return qk, v, d_o, buckets
 
 
-def _loss(qk, v, d_o, perm, cid, chunk, causal, scale, dup_correct):
-    o_r, lse = O.attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct)
+def _loss(qk, v, d_o, perm, cid, chunk, causal, scale, dup_correct, wrap=False, buckets=None):
+    o_r, lse = O.attention_rounds(qk, v, perm, cid, chunk, causal, scale, dup_correct=dup_correct,
+                                  wrap=wrap, buckets=buckets)
     o, _ = O.combine_rounds(o_r, lse)
     return float(np.sum(o * d_o))
 
 
-def check_backward_finite_differences(causal=True, n_r=2, dup_correct=True, seed=40):
+def check_backward_finite_differences(causal=True, n_r=2, dup_correct=True, seed=40, wrap=False,
+                                      same_bucket=False):
     """Central differences of sum(o * d_o) in every element of qk and v, with the
     buckets held fixed (they are piecewise constant in qk)."""
     L, d, nb, chunk = 16, 3, 4, 4
     qk, v, d_o, buckets = _bwd_case(L, d, n_r, nb, seed)
     perm, cid = O.sort_rounds(buckets, nb, chunk)
     scale = 0.7
-    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale, dup_correct)
+    bk = buckets if same_bucket else None
+    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale, dup_correct, wrap, bk)
     h = 1e-4
     for name, arr, grad in (("qk", qk, g["dqk"]), ("v", v, g["dv"])):
         fd = np.empty_like(arr)
@@ -411,13 +414,13 @@ def check_backward_finite_differences(causal=True, n_r=2, dup_correct=True, seed
             a_m = arr.copy(); a_m[idx] -= h
             args_p = (a_p, v) if name == "qk" else (qk, a_p)
             args_m = (a_m, v) if name == "qk" else (qk, a_m)
-            fd[idx] = (_loss(*args_p, d_o, perm, cid, chunk, causal, scale, dup_correct)
-                       - _loss(*args_m, d_o, perm, cid, chunk, causal, scale, dup_correct)) / (2 * h)
+            fd[idx] = (_loss(*args_p, d_o, perm, cid, chunk, causal, scale, dup_correct, wrap, bk)
+                       - _loss(*args_m, d_o, perm, cid, chunk, causal, scale, dup_correct, wrap, bk)) / (2 * h)
         err = np.max(np.abs(grad - fd)) / np.max(np.abs(fd))
         assert err < 1e-6, f"d{name}: relative deviation {err:.3g} from finite differences"
 
 
-def check_backward_union_autograd(causal=False, n_r=3, seed=41):
+def check_backward_union_autograd(causal=False, n_r=3, seed=41, wrap=False, same_bucket=False):
     """The oracle's gradients equal torch autograd of the union closed form
     (tests/reference_forms.py), which shares no code with the oracle."""
     import torch
@@ -425,8 +428,9 @@ def check_backward_union_autograd(causal=False, n_r=3, seed=41):
     qk, v, d_o, buckets = _bwd_case(L, d, n_r, nb, seed)
     perm, cid = O.sort_rounds(buckets, nb, chunk)
     scale = 0.5
-    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale)
-    W = RF.brute_windows(buckets[0, 0], chunk, causal)
+    g = O.attention_backward(qk, v, perm, cid, d_o, chunk, causal, scale, True, wrap,
+                             buckets if same_bucket else None)
+    W = RF.brute_windows(buckets[0, 0], chunk, causal, wrap, same_bucket)
     tq = torch.tensor(qk[0, 0], dtype=torch.float64, requires_grad=True)
     tv = torch.tensor(v[0, 0], dtype=torch.float64, requires_grad=True)
     out = RF.union_attention_torch(tq, tv, W, scale)
@@ -563,8 +567,16 @@ ALL_CHECKS = {
     "backward_finite_differences": check_backward_finite_differences,
     "backward_finite_differences_noncausal_no_correction": lambda: check_backward_finite_differences(
         causal=False, n_r=3, dup_correct=False, seed=43),
+    "backward_finite_differences_wrap": lambda: check_backward_finite_differences(
+        causal=False, n_r=3, seed=46, wrap=True),
+    "backward_finite_differences_same_bucket": lambda: check_backward_finite_differences(
+        causal=True, n_r=3, seed=47, same_bucket=True),
     "backward_union_autograd": check_backward_union_autograd,
     "backward_union_autograd_causal": lambda: check_backward_union_autograd(causal=True, n_r=2, seed=44),
+    "backward_union_autograd_wrap": lambda: check_backward_union_autograd(causal=True, n_r=3, seed=48,
+                                                                          wrap=True),
+    "backward_union_autograd_same_bucket": lambda: check_backward_union_autograd(
+        causal=False, n_r=3, seed=49, same_bucket=True),
     "backward_dv_sum": check_backward_dv_sum,
     "backward_one": check_backward_one,
     "feed_forward_brute_force": check_feed_forward_brute_force,
