@@ -172,7 +172,7 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
 
 /*
  * Backward of steps 3-4: gradients with respect to qk and v (bfloat16, chunk 64;
- * the method as above, or with LSH_FLAG_NO_DUP_CORRECTION).  The pages print no
+ * the method as above and every variant flag).  The pages print no
  * backward pass; this is the chain rule through the forward defined above.
  * After the combine, query i's output is one softmax over all (round, key)
  * pairs of its windows ([MOD] "Multi-round LSH attention" merges the rounds by
@@ -191,8 +191,8 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
  *              bytes (combined lse and Delta, and per-round partial gradients:
  *              about 6 * B*H*n_rounds*L*d bytes); its contents on entry do not
  *              matter.
- * Errors as above, and LSH_ERR_UNSUPPORTED for dtype LSH_F32, chunk other than
- * 64, or a flag other than LSH_FLAG_NO_DUP_CORRECTION; LSH_ERR_WORKSPACE.
+ * Errors as above, and LSH_ERR_UNSUPPORTED for dtype LSH_F32 or chunk other
+ * than 64; LSH_ERR_WORKSPACE.
  */
 size_t lsh_backward_workspace_bytes(const lsh_config* cfg);
 lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* v,

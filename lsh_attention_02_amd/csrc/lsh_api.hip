@@ -145,9 +145,6 @@ lsh_status check_backward(const lsh_config* cfg)
     LSH_TRY(check_config(cfg));
     if (cfg->dtype != LSH_BF16) return fail(LSH_ERR_UNSUPPORTED, "the backward supports LSH_BF16 only");
     if (cfg->chunk != 64) return fail(LSH_ERR_UNSUPPORTED, "the backward supports chunk 64 only");
-    if (cfg->flags & ~LSH_FLAG_NO_DUP_CORRECTION)
-        return fail(LSH_ERR_UNSUPPORTED,
-                    "the backward supports the method and LSH_FLAG_NO_DUP_CORRECTION only");
     return LSH_OK;
 }
 
@@ -289,6 +286,8 @@ lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* 
     a.causal = cfg->causal;
     a.scale = cfg->scale;
     a.dup = !(cfg->flags & LSH_FLAG_NO_DUP_CORRECTION);
+    a.wrap = (cfg->flags & LSH_FLAG_WRAP_LOOKBACK) != 0;
+    a.same_bucket = (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0;
     return hip_status(lshk::launch_attn_backward(cfg->d_head, a, static_cast<hipStream_t>(stream)),
                       "lsh_attn_backward");
 }

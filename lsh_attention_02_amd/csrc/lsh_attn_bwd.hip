@@ -25,8 +25,9 @@
 //              keys each) and accumulate dK^T = Q^T dS and dV^T = dO^T P over
 //              the two tiles that chunk is a key of (as the current chunk, then
 //              as the look-back of the next); a run ends with one extra tile
-//              (the next run's first queries against its last chunk), so every
-//              position's key gradient is summed in one workgroup.
+//              (the next run's first queries against its last chunk; with the
+//              wrap-around variant the last run's extra tile is chunk 0), so
+//              every position's key gradient is summed in one workgroup.
 //              Results are per-round partials (bf16, original position order).
 //   k_bwd_reduce  dqk = sum_r (dq_r + dk_r), dv = sum_r dv_r in fp32.
 #include "lsh_chunk_attn.h"
@@ -51,7 +52,7 @@ struct BwdLds {
     static constexpr int PROWB = C * 2;              // bytes of a P / dS row (C queries)
     static constexpr int NW = NDW > 0 ? NDW : 1;
     float neg_log2[36];                              // as in the forward (first member)
-    bf16_t k[2][C * KROW];                           // qk rows, slot = chunk & 1
+    bf16_t k[2][C * KROW];                           // qk rows, slot = iteration % 2
     bf16_t v[2][C * KROW];                           // v rows
     char kt[2][D * TROWB];                           // qk^T rows (d), keys in groups of 4
     char dot[D * TROWB];                             // d_o^T of the query chunk
@@ -59,11 +60,15 @@ struct BwdLds {
     char ds[2 * C * PROWB];                          // dS[key][query]
     int pos[2][C];
     uint32_t cid[2][C * NW];
+    int rid[2][C];                                   // same-bucket variant: window ids, this round
     float lse2[C];                                   // combined logsumexp, log2 units
     float delta[C];
 };
 
-template <int D, int C, int NDW>
+// WRAP: chunk 0 looks back to the last chunk of its round; SAME: keys outside
+// the query's bucket of this round are dropped (cid holds window ids), as in the
+// forward kernel.
+template <int D, int C, int NDW, bool WRAP, bool SAME>
 __global__ __launch_bounds__(4 * C)
 void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                 const bf16_t* __restrict__ d_o, const int32_t* __restrict__ perm,
@@ -122,6 +127,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
     u32x4 kreg[JPT][4], vreg[JPT][4], dreg[JPT][4];
     u32x4 dofrag[NKS];          // d_o fragments of this lane's query row (next chunk)
     uint32_t craw[2 * NW];
+    uint32_t ridraw = 0;
     float lraw = 0.f, draw = 0.f;
     int rpos = 0;
 
@@ -159,6 +165,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
 #pragma unroll
             for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
         }
+        if constexpr (SAME) ridraw = (uint16_t)cr[r];
         lraw = lb[rpos];
         draw = deb[rpos];
     };
@@ -198,19 +205,26 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                 const uint32_t hi = 2 * w + 1 < n_r ? craw[2 * w + 1] : 0u;
                 sm.cid[sl][tid * NDW + w] = lo | (hi << 16);
             }
+            if constexpr (SAME) sm.rid[sl][tid] = (int)ridraw;
             sm.lse2[tid] = lraw * LOG2E;
             sm.delta[tid] = draw;
         }
     };
 
-    // Iteration it handles chunk chunk_of(it): a look-back chunk first (load
-    // only) when k0 > 0, the query chunks k0 .. k1-1, then chunk k1 when it
-    // exists (key side only: its queries against chunk k1-1).
-    const bool lookback = k0 > 0;
-    const bool extra = k1 < nchunks;
+    // Iteration it handles chunk chunk_of(it) in LDS slot it % 2: a look-back
+    // chunk first (load only) when the run's first chunk has one, the query
+    // chunks k0 .. k1-1, then the chunk after k1-1 when it has k1-1 as its
+    // look-back (key side only: its queries against chunk k1-1).  With WRAP the
+    // look-back of chunk 0 is the last chunk, and the chunk after the last is 0.
+    const bool wraps = WRAP && nchunks > 1;
+    const bool lookback = k0 > 0 || wraps;
+    const bool extra = k1 < nchunks || wraps;
     const int it0 = lookback ? 1 : 0;
     const int nit = (k1 - k0) + it0 + (extra ? 1 : 0);
-    auto chunk_of = [&](int it) { return k0 - it0 + it; };
+    auto chunk_of = [&](int it) {
+        const int c = k0 - it0 + it;
+        return c < 0 ? c + nchunks : c >= nchunks ? c - nchunks : c;
+    };
 
     // phase-2 ownership: waves 2G, 2G+1 (G = wave / (W/2)) own the chunk in LDS
     // slot G; wave sub-slice sw covers keys KSL*sw .. of that chunk
@@ -246,7 +260,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
 
     for (int it = 0; it < nit; ++it) {
         const int c = chunk_of(it);
-        const int sl = c & 1, sp = sl ^ 1;
+        const int sl = it & 1, sp = sl ^ 1;
         u32x4 dof[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) dof[ks] = dofrag[ks];
@@ -258,8 +272,8 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
         }
         if (it < it0) continue;        // look-back chunk: loaded only (next barrier follows the store)
 
-        const bool is_extra = extra && c == k1;
-        const bool has_prev = c > 0;
+        const bool is_extra = extra && it == nit - 1;
+        const bool has_prev = c > 0 || wraps;
 
         // ---------------- phase 1: queries 16*wave + r16 of chunk c
         {
@@ -274,6 +288,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
             uint32_t q1[NW];
 #pragma unroll
             for (int w = 0; w < NDW; ++w) q1[w] = pk_sub_u16(sm.cid[sl][qrow * NDW + w], ones);
+            const int rq1 = SAME ? sm.rid[sl][qrow] - 1 : 0;   // query's window id minus one
             const float lse2 = sm.lse2[qrow], dlt = sm.delta[qrow];
             // a query whose windows hold only itself has LSE ~ -penalty: then its
             // self weight is exactly 1/n_r (every round has the same self score);
@@ -304,12 +319,14 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                 const bool diag = t == CT + wave;
                 const int krow0 = (t % CT) * 16 + 4 * g;
                 const int4 kp = *reinterpret_cast<const int4*>(&sm.pos[slk][krow0]);
+                int4 kr = {0, 0, 0, 0};
+                if constexpr (SAME) kr = *reinterpret_cast<const int4*>(&sm.rid[slk][krow0]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kpos = j == 0 ? kp.x : j == 1 ? kp.y : j == 2 ? kp.z : kp.w;
                     float nlg = 0.f;
                     if constexpr (NDW > 0) {
-                        const uint32_t outs8 = rounds_outside8<NDW, false>(
+                        const uint32_t outs8 = rounds_outside8<NDW, WRAP>(
                             q1, &sm.cid[slk][(krow0 + j) * NDW], nch2);
                         nlg = *reinterpret_cast<const float*>(
                             reinterpret_cast<const char*>(sm.neg_log2) + outs8);
@@ -318,6 +335,11 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     float p = __builtin_amdgcn_exp2f(fmaf(s[t][j], scale_log2, nlg) - lse2);
                     if (self) p = self_only ? self_p : 0.f;
                     if (causal && kpos > qpos) p = 0.f;
+                    if constexpr (SAME) {
+                        // another bucket: window ids differ by something other than 0 or 1
+                        const int kid = j == 0 ? kr.x : j == 1 ? kr.y : j == 2 ? kr.z : kr.w;
+                        if ((unsigned)(kid - rq1) > 1u) p = 0.f;
+                    }
                     s[t][j] = p;
                     dp[t][j] = p * (dp[t][j] - dlt);
                 }
@@ -376,7 +398,8 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
         // ---------------- phase 2: keys of the chunk in slot G
         {
             const bool cur_role = G == sl;               // slot G holds chunk c, else c - 1
-            const bool active = cur_role ? !is_extra : (has_prev && c != k0);
+            // the run's first query tile has a look-back that another run owns
+            const bool active = cur_role ? !is_extra : (has_prev && it > it0);
             if (cur_role && !is_extra) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
@@ -422,8 +445,8 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
         }
         __syncthreads();
     }
-    // the last chunk of the round has no next tile: its keys are complete
-    if (!extra && G == ((k1 - 1) & 1)) write_keys();
+    // the run's last chunk is nobody's look-back: its keys are complete
+    if (!extra && G == ((nit - 1) & 1)) write_keys();
 }
 
 // LSE_i = logsumexp_r lse[r, i]; Delta_i = <d_o_i, o_i>.  One thread per 16 bytes
@@ -498,19 +521,29 @@ void k_bwd_reduce(const bf16_t* __restrict__ dq_r, const bf16_t* __restrict__ dk
     __builtin_nontemporal_store(f32x4{av[4], av[5], av[6], av[7]}, reinterpret_cast<f32x4*>(ov + 4));
 }
 
-template <int D, int C, int NDW>
+template <int D, int C, int NDW, bool WRAP, bool SAME>
 hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s)
 {
     const int nchunks = a.L / C;
     const int nruns = (nchunks + BWD_RUN - 1) / BWD_RUN;
     const long blocks = a.bh * nruns * a.n_r;
-    hipLaunchKernelGGL((k_attn_bwd<D, C, NDW>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
+    hipLaunchKernelGGL((k_attn_bwd<D, C, NDW, WRAP, SAME>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const bf16_t*>(a.qk), static_cast<const bf16_t*>(a.v),
                        static_cast<const bf16_t*>(a.d_o), a.perm, a.cid, a.lse_c, a.delta,
                        static_cast<bf16_t*>(a.dq_r), static_cast<bf16_t*>(a.dk_r),
                        static_cast<bf16_t*>(a.dv_r), a.L, a.n_r, a.causal, a.scale,
                        a.scale * LOG2E, nruns);
     return hipGetLastError();
+}
+
+template <int D, bool WRAP, bool SAME>
+hipError_t launch_bwd_ndw(const BwdArgs& a, hipStream_t s)
+{
+    if (!a.dup) return launch_bwd_one<D, 64, 0, WRAP, SAME>(a, s);
+    if (a.n_r <= 2) return launch_bwd_one<D, 64, 1, WRAP, SAME>(a, s);
+    if (a.n_r <= 4) return launch_bwd_one<D, 64, 2, WRAP, SAME>(a, s);
+    if (a.n_r <= 8) return launch_bwd_one<D, 64, 4, WRAP, SAME>(a, s);
+    return launch_bwd_one<D, 64, 8, WRAP, SAME>(a, s);
 }
 
 template <int D>
@@ -524,11 +557,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s)
                        a.lse_c, a.delta, rows, a.L, a.n_r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!a.dup) e = launch_bwd_one<D, 64, 0>(a, s);
-    else if (a.n_r <= 2) e = launch_bwd_one<D, 64, 1>(a, s);
-    else if (a.n_r <= 4) e = launch_bwd_one<D, 64, 2>(a, s);
-    else if (a.n_r <= 8) e = launch_bwd_one<D, 64, 4>(a, s);
-    else e = launch_bwd_one<D, 64, 8>(a, s);
+    if (a.same_bucket) e = launch_bwd_ndw<D, false, true>(a, s);
+    else if (a.wrap) e = launch_bwd_ndw<D, true, false>(a, s);
+    else e = launch_bwd_ndw<D, false, false>(a, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_bwd_reduce<D>), dim3(blocks), dim3(256), 0, s,
                        static_cast<const bf16_t*>(a.dq_r), static_cast<const bf16_t*>(a.dk_r),

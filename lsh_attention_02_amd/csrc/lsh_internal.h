@@ -67,6 +67,8 @@ struct BwdArgs {
     int L, n_r, causal;
     float scale;
     bool dup;                    // duplicate-count term on
+    bool wrap;                   // LSH_FLAG_WRAP_LOOKBACK
+    bool same_bucket;            // LSH_FLAG_SAME_BUCKET
 };
 hipError_t launch_attn_backward(int d_head, const BwdArgs& a, hipStream_t stream);
 

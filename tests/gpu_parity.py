@@ -302,7 +302,7 @@ def backward_parity(w: Workload, flags: int = 0) -> dict:
     assert np.array_equal(to_np(g["perm"]), sp), f"{w.name}: perm differs from the stable sort"
     ref = O.attention_backward(x["qk"].astype(np.float64), x["v"].astype(np.float64), sp, sc_id,
                                d_o.astype(np.float64), w.chunk, w.causal, cfg.score_scale,
-                               **variant(flags))
+                               **variant(flags), buckets=gb if same_bucket(flags) else None)
     rep = {"workload": w.name, "flags": flags}
     rep["dqk_err"] = rel_err(to_np(dqk), ref["dqk"])
     rep["dv_err"] = rel_err(to_np(dv), ref["dv"])

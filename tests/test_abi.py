@@ -200,8 +200,7 @@ def test_backward_pointer_checks(lib, which):
 
 
 def test_backward_support_and_workspace(lib):
-    for kw in (dict(dtype="f32"), dict(chunk=32), dict(chunk=128),
-               dict(flags=B.LSH_FLAG_WRAP_LOOKBACK), dict(flags=B.LSH_FLAG_SAME_BUCKET)):
+    for kw in (dict(dtype="f32"), dict(chunk=32), dict(chunk=128)):
         c = cfg(**kw)
         assert lib.lsh_backward_workspace_bytes(raw(c)) == 0, kw
         assert lib.lsh_attn_backward(raw(c), *[FAKE] * 10, 1 << 40, NULL) == B.LSH_ERR_UNSUPPORTED, kw
@@ -210,7 +209,8 @@ def test_backward_support_and_workspace(lib):
     def up(x):
         return (x + 255) // 256 * 256
     for kw in (dict(), dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8),
-               dict(flags=B.LSH_FLAG_NO_DUP_CORRECTION, heads=3, seq_len=192)):
+               dict(flags=B.LSH_FLAG_NO_DUP_CORRECTION, heads=3, seq_len=192),
+               dict(flags=B.LSH_FLAG_WRAP_LOOKBACK), dict(flags=B.LSH_FLAG_SAME_BUCKET)):
         c = cfg(**kw)
         T = c.batch * c.heads * c.seq_len
         want = 2 * up(4 * T) + 3 * up(2 * T * c.n_rounds * c.d_head)

@@ -226,6 +226,22 @@ BWD_CASES = {
                                seed=155), 0),
     "no_dup_L1344_r3": (W("bwd_g", heads=2, seq_len=1344, n_buckets=10, n_rounds=3, seed=156),
                         lsh.LSH_FLAG_NO_DUP_CORRECTION),
+    # wrap-around look-back: 21 chunks (odd: chunk 0 and its look-back share a
+    # parity) over two runs; two chunks; one chunk
+    "wrap_L1344_r3_causal": (W("bwd_h", heads=2, seq_len=1344, n_buckets=10, n_rounds=3, seed=157),
+                             lsh.LSH_FLAG_WRAP_LOOKBACK),
+    "wrap_L2048_r4_d128_noncausal": (W("bwd_i", seq_len=2048, d_head=128, n_buckets=32, n_rounds=4,
+                                       causal=False, seed=158), lsh.LSH_FLAG_WRAP_LOOKBACK),
+    "wrap_no_dup_L128_two_chunks": (W("bwd_j", heads=2, seq_len=128, n_buckets=4, n_rounds=3,
+                                      causal=False, seed=159),
+                                    lsh.LSH_FLAG_WRAP_LOOKBACK | lsh.LSH_FLAG_NO_DUP_CORRECTION),
+    "wrap_L64_one_chunk": (W("bwd_k", heads=2, seq_len=64, n_buckets=4, seed=160),
+                           lsh.LSH_FLAG_WRAP_LOOKBACK),
+    "same_bucket_L1344_r3": (W("bwd_l", batch=2, heads=2, seq_len=1344, n_buckets=10, n_rounds=3,
+                               seed=161), lsh.LSH_FLAG_SAME_BUCKET),
+    "same_bucket_no_dup_L2048_d128": (W("bwd_m", seq_len=2048, d_head=128, n_buckets=16, n_rounds=4,
+                                        causal=False, seed=162),
+                                      lsh.LSH_FLAG_SAME_BUCKET | lsh.LSH_FLAG_NO_DUP_CORRECTION),
 }
 
 
