@@ -344,18 +344,30 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     dp[t][j] = p * (dp[t][j] - dlt);
                 }
             }
-            // P and dS to LDS, [window key][query]
-            const int qg = qrow >> 2, qo = 2 * (qrow & 3);
+            // P and dS to LDS, [window key][query], two queries per 4-byte store:
+            // lanes 2i and 2i+1 (queries qe, qe+1) swap halves with one DPP move;
+            // the even lane stores keys 4g+0 and 4g+2 of the pair, the odd lane
+            // keys 4g+1 and 4g+3 (rows of both parities in each store: no bank
+            // conflicts).
+            const bool odd = (r16 & 1) != 0;
+            const int qe = qrow & ~1;
+            const int qge = qe >> 2, qoe = 2 * (qe & 3);
+            auto store_pair = [&](char* base, int t, const f32x4& x) {
+                const uint32_t p02 = pack_bf16x2(x[0], x[2]), p13 = pack_bf16x2(x[1], x[3]);
+                const uint32_t send = odd ? p02 : p13, own = odd ? p13 : p02;
+                const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+                const uint32_t lo = odd ? recv : own, hi = odd ? own : recv;   // (query qe, qe + 1)
+                const uint32_t wa = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                const uint32_t wb = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+                const int ka = t * 16 + 4 * g + (odd ? 1 : 0), kb = ka + 2;
+                *reinterpret_cast<uint32_t*>(base + ka * PROWB + 8 * (qge ^ pswz(ka)) + qoe) = wa;
+                *reinterpret_cast<uint32_t*>(base + kb * PROWB + 8 * (qge ^ pswz(kb)) + qoe) = wb;
+            };
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 if (t < CT ? !has_prev : is_extra) continue;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int wk = t * 16 + 4 * g + j;
-                    const int off = wk * PROWB + 8 * (qg ^ pswz(wk)) + qo;
-                    *reinterpret_cast<uint16_t*>(sm.p + off) = f32_to_bf16_rne(s[t][j]);
-                    *reinterpret_cast<uint16_t*>(sm.ds + off) = f32_to_bf16_rne(dp[t][j]);
-                }
+                store_pair(sm.p, t, s[t]);
+                store_pair(sm.ds, t, dp[t]);
             }
             // dQ^T = K^T dS^T (the extra tile's queries belong to the next run)
             if (!is_extra) {
