@@ -420,35 +420,41 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
             }
             if (active) {
                 const int wbase = cur_role ? C : 0;      // window rows of this slot's keys
+                // queries 16 u0 + 4g + j and 16 (u0 + 1) + 4g + j: the Q^T and dO^T
+                // fragments serve both key tiles of this wave
 #pragma unroll
-                for (int kt = 0; kt < KTW; ++kt) {
-                    const int wk = wbase + KSL * sw + 16 * kt + r16;
-                    const char* prow = sm.p + wk * PROWB;
-                    const char* srow = sm.ds + wk * PROWB;
-                    const int psw = pswz(wk);
+                for (int u0 = 0; u0 < CT; u0 += 2) {
+                    const int qg = ((u0 * 16) >> 2) + g;
+                    bf16x8 bp[KTW], bs[KTW];
 #pragma unroll
-                    for (int u0 = 0; u0 < CT; u0 += 2) {
-                        const int qg = ((u0 * 16) >> 2) + g;     // queries 16 u0 + 4g + j and +16
+                    for (int kt = 0; kt < KTW; ++kt) {
+                        const int wk = wbase + KSL * sw + 16 * kt + r16;
+                        const char* prow = sm.p + wk * PROWB;
+                        const char* srow = sm.ds + wk * PROWB;
+                        const int psw = pswz(wk);
                         const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(prow + 8 * (qg ^ psw));
                         const bf16x4 p1 = *reinterpret_cast<const bf16x4*>(prow + 8 * ((qg + 4) ^ psw));
                         const bf16x4 s0 = *reinterpret_cast<const bf16x4*>(srow + 8 * (qg ^ psw));
                         const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(srow + 8 * ((qg + 4) ^ psw));
-                        const bf16x8 bp = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const bf16x8 bs = __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        bp[kt] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        bs[kt] = __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
 #pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) {
-                            const int d = dt * 16 + r16;
-                            const int swz = vt_swz<C>(d);
-                            const char* qr = sm.kt[sl] + d * TROWB;
-                            const char* dr = sm.dot + d * TROWB;
-                            const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(qr + 8 * (qg ^ swz));
-                            const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(qr + 8 * ((qg + 4) ^ swz));
-                            const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(dr + 8 * (qg ^ swz));
-                            const bf16x4 c1 = *reinterpret_cast<const bf16x4*>(dr + 8 * ((qg + 4) ^ swz));
-                            acck[dt][kt] = M::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                  bs, acck[dt][kt]);
-                            accv[dt][kt] = M::mma(__builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                  bp, accv[dt][kt]);
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const int d = dt * 16 + r16;
+                        const int swz = vt_swz<C>(d);
+                        const char* qr = sm.kt[sl] + d * TROWB;
+                        const char* dr = sm.dot + d * TROWB;
+                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(qr + 8 * (qg ^ swz));
+                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(qr + 8 * ((qg + 4) ^ swz));
+                        const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(dr + 8 * (qg ^ swz));
+                        const bf16x4 c1 = *reinterpret_cast<const bf16x4*>(dr + 8 * ((qg + 4) ^ swz));
+                        const bf16x8 aq = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const bf16x8 ad = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int kt = 0; kt < KTW; ++kt) {
+                            acck[dt][kt] = M::mma(aq, bs[kt], acck[dt][kt]);
+                            accv[dt][kt] = M::mma(ad, bp[kt], accv[dt][kt]);
                         }
                     }
                 }
