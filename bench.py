@@ -20,6 +20,8 @@ Other modes:
                          (the reversible inverse) at this model width, feed-forward
                          width --d-ff (default 4 x D_MODEL), --chunk-rows rows per
                          feed-forward chunk (no CPU baseline)
+    --graph              also time the step captured into one HIP graph and replayed
+                         (launch overhead removed; `value` is then the replay rate)
     --backward           time forward + backward (lsh_attn_backward with a synthetic
                          loss gradient at the output; no CPU baseline)
     --copy-calibration   run only a plain 1 GiB device copy (for scaling the
@@ -295,6 +297,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one captured HIP graph (replayed); per-call times stay eager")
     ap.add_argument("--block", type=int, default=0, metavar="D_MODEL",
                     help="time a Reformer block forward + its input recompute at this model width")
     ap.add_argument("--d-ff", type=int, default=0, help="feed-forward width (default 4 x D_MODEL)")
@@ -438,6 +442,25 @@ def main():
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    eager_ms_per_step = ms_per_step
+    if args.graph:
+        # the same step captured into one HIP graph; every call is asynchronous
+        # on `stream` and allocates nothing, so the capture records the kernels
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.Event(enable_timing=True)
+        ge = torch.cuda.Event(enable_timing=True)
+        gs.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                graph.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = gs.elapsed_time(ge) / args.steps
     per_call = {n: float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
                 for i, n in enumerate(names)}
     assert torch.isfinite((y if dm else o).float()).all().item(), "non-finite output"
@@ -472,6 +495,8 @@ def main():
                    "n_buckets": w.n_buckets, "n_rounds": nr, "chunk": w.chunk,
                    "causal": w.causal, "flags": args.flags, **({"d_model": dm} if dm else {}),
                    **({"d_ff": dff, "chunk_rows": args.chunk_rows} if blk else {}),
+                   **({"graph": True, "eager_ms_per_step": round(eager_ms_per_step, 4)}
+                      if args.graph else {}),
                    **({"backward": True} if bwd else {})},
         "roofline": roof, "kernels": kernels,
     }

@@ -36,7 +36,6 @@ namespace lshk {
 namespace attn {
 namespace {
 
-constexpr int BWD_RUN = 16;                  // query chunks per workgroup
 
 // P / dS rows in LDS: one row per window key (2C rows), C queries each, in
 // 8-byte groups of 4 queries; group qg of row k is stored at qg ^ pswz(k).
@@ -75,7 +74,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                 const int16_t* __restrict__ cid, const float* __restrict__ lse_c,
                 const float* __restrict__ delta, bf16_t* __restrict__ dq_r,
                 bf16_t* __restrict__ dk_r, bf16_t* __restrict__ dv_r, int L, int n_r,
-                int causal, float scale, float scale_log2, int nruns)
+                int causal, float scale, float scale_log2, int nruns, int run_len)
 {
     using T = bf16_t;
     using M = Mfma16<T>;
@@ -103,7 +102,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
     const int run = bid % nruns;
     const long bh = bid / nruns;
     const int nchunks = L / C;
-    const int k0 = run * BWD_RUN, k1 = min(k0 + BWD_RUN, nchunks);
+    const int k0 = run * run_len, k1 = min(k0 + run_len, nchunks);
 
     const T* qb = qk + bh * (long)L * D;
     const T* vb = v + bh * (long)L * D;
@@ -543,14 +542,15 @@ template <int D, int C, int NDW, bool WRAP, bool SAME>
 hipError_t launch_bwd_one(const BwdArgs& a, hipStream_t s)
 {
     const int nchunks = a.L / C;
-    const int nruns = (nchunks + BWD_RUN - 1) / BWD_RUN;
+    const int run_len = run_length(nchunks, a.bh * a.n_r);     // as the forward's runs
+    const int nruns = (nchunks + run_len - 1) / run_len;
     const long blocks = a.bh * nruns * a.n_r;
     hipLaunchKernelGGL((k_attn_bwd<D, C, NDW, WRAP, SAME>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const bf16_t*>(a.qk), static_cast<const bf16_t*>(a.v),
                        static_cast<const bf16_t*>(a.d_o), a.perm, a.cid, a.lse_c, a.delta,
                        static_cast<bf16_t*>(a.dq_r), static_cast<bf16_t*>(a.dk_r),
                        static_cast<bf16_t*>(a.dv_r), a.L, a.n_r, a.causal, a.scale,
-                       a.scale * LOG2E, nruns);
+                       a.scale * LOG2E, nruns, run_len);
     return hipGetLastError();
 }
 

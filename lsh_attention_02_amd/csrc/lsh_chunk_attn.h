@@ -44,7 +44,18 @@ namespace attn {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float SELF_PENALTY = 1.0e5f;               // score units
-constexpr int RUN = 16;                              // chunks per workgroup
+// Chunks per workgroup: a run of consecutive chunks shares each look-back
+// load.  Runs are RUN chunks long unless the problem is small: then shorter
+// runs spread it over about RUN_TARGET_WGS workgroups (a run of one chunk
+// loads its look-back itself), so a few segments do not serialise on a few CUs.
+constexpr int RUN = 16;
+constexpr long RUN_TARGET_WGS = 1024;
+
+inline int run_length(int nchunks, long segments)
+{
+    const long len = ((long)nchunks * segments + RUN_TARGET_WGS - 1) / RUN_TARGET_WGS;
+    return (int)(len < 1 ? 1 : len > RUN ? RUN : len);
+}
 
 __device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
 {
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(4 * C)
 void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                   const int32_t* __restrict__ perm, const int16_t* __restrict__ cid,
                   T* __restrict__ o_rounds, float* __restrict__ lse, int L, int n_r, int causal,
-                  float scale_log2, int nruns)
+                  float scale_log2, int nruns, int run_len)
 {
     using M = Mfma16<T>;
     using S = Lds<T, D, C, NDW>;
@@ -203,7 +214,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     const int run = bid % nruns;
     const long bh = bid / nruns;
     const int nchunks = L / C;
-    const int k0 = run * RUN, k1 = min(k0 + RUN, nchunks);
+    const int k0 = run * run_len, k1 = min(k0 + run_len, nchunks);
 
     const T* qb = qk + bh * (long)L * D;
     const T* vb = v + bh * (long)L * D;
@@ -486,11 +497,12 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
                       hipStream_t s)
 {
     const int nchunks = L / C;
-    const int nruns = (nchunks + RUN - 1) / RUN;
+    const int run_len = run_length(nchunks, bh * n_r);
+    const int nruns = (nchunks + run_len - 1) / run_len;
     const long blocks = bh * nruns * n_r;
     hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW, WRAP, SAME>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
                        static_cast<const T*>(qk), static_cast<const T*>(v), perm, cid,
-                       static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns);
+                       static_cast<T*>(o_rounds), lse, L, n_r, causal, scale * LOG2E, nruns, run_len);
     return hipGetLastError();
 }
 

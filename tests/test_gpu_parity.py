@@ -25,6 +25,12 @@ def W(name, **kw) -> Workload:
 # and ragged tails (L not a multiple of the hash workgroup's 512 tokens, chunk
 # counts not a multiple of the attention run of 16 chunks, partial column tiles).
 SMALL = {
+    # runs of several chunks (the run length adapts to the problem size: these
+    # have 2 and 3 chunks per run, with a ragged last run)
+    "runs2_b2h8_L1344_r4": W("runs2", batch=2, heads=8, seq_len=1344, n_buckets=10, n_rounds=4,
+                             seed=107),
+    "runs3_b2h8_L4096_r3_d128": W("runs3", batch=2, heads=8, seq_len=4096, d_head=128,
+                                  n_buckets=32, n_rounds=3, causal=False, seed=108),
     "tiny_f32": WORKLOADS["tiny_f32"],
     "short_4k": WORKLOADS["short_4k"],
     "ragged_b2h3_L1344_nb10_r3": W("ragged", batch=2, heads=3, seq_len=1344, n_buckets=10,
@@ -237,6 +243,13 @@ BWD_CASES = {
                                     lsh.LSH_FLAG_WRAP_LOOKBACK | lsh.LSH_FLAG_NO_DUP_CORRECTION),
     "wrap_L64_one_chunk": (W("bwd_k", heads=2, seq_len=64, n_buckets=4, seed=160),
                            lsh.LSH_FLAG_WRAP_LOOKBACK),
+    # runs of 2 and 3 chunks (ragged last run): key gradients carried across tiles
+    "runs2_b2h8_L1344_r4": (W("bwd_n", batch=2, heads=8, seq_len=1344, n_buckets=10, n_rounds=4,
+                              seed=163), 0),
+    "runs3_b2h8_L4096_r3_d128": (W("bwd_o", batch=2, heads=8, seq_len=4096, d_head=128,
+                                   n_buckets=32, n_rounds=3, causal=False, seed=164), 0),
+    "runs2_wrap_b2h8_L1344_r4": (W("bwd_p", batch=2, heads=8, seq_len=1344, n_buckets=10,
+                                   n_rounds=4, seed=165), lsh.LSH_FLAG_WRAP_LOOKBACK),
     "same_bucket_L1344_r3": (W("bwd_l", batch=2, heads=2, seq_len=1344, n_buckets=10, n_rounds=3,
                                seed=161), lsh.LSH_FLAG_SAME_BUCKET),
     "same_bucket_no_dup_L2048_d128": (W("bwd_m", seq_len=2048, d_head=128, n_buckets=16, n_rounds=4,
@@ -312,3 +325,43 @@ def test_ffn_big_tiles_sampled():
 
 def test_ffn_big_tiles_chunked_sampled():
     GP.ffn_sampled(40000, 1024, 4096, 16384, 193)
+
+
+# ---------------------------------------------------------------------- HIP graph replay
+def test_forward_graph_replay():
+    """The four calls captured into one HIP graph (torch.cuda.CUDAGraph), replayed
+    three times with eager work in between: every replay equals the eager
+    result bit for bit (the kernels are deterministic and allocate nothing)."""
+    w = WORKLOADS["short_4k"]
+    x = make_inputs(w)
+    cfg = GP.cfg_of(w)
+    dev = "cuda:0"
+    t = GP.upload(w, x, dev)
+    eager = lsh.forward(cfg, t["qk"], t["v"], t["R"], return_all=True)
+    torch.cuda.synchronize()
+    B, H, L, d, nr = w.batch, w.heads, w.seq_len, w.d_head, w.n_rounds
+    out = {k: torch.empty_like(eager[k]) for k in ("buckets", "perm", "cid", "o_rounds", "lse", "o")}
+    ws = lsh.sort_workspace(cfg, dev)
+    s = torch.cuda.Stream(device=dev)
+
+    def step():
+        lsh.lsh_hash(cfg, t["qk"], t["R"], out["buckets"], stream=s)
+        lsh.lsh_sort(cfg, out["buckets"], out["perm"], out["cid"], ws, stream=s)
+        lsh.lsh_chunk_attn(cfg, t["qk"], t["v"], out["perm"], out["cid"], out["o_rounds"], out["lse"],
+                           stream=s)
+        lsh.lsh_combine_rounds(cfg, out["o_rounds"], out["lse"], out["o"], stream=s)
+
+    with torch.cuda.stream(s):
+        step()                                   # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        for k in out:                            # eager work between replays
+            out[k].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out:
+            assert torch.equal(out[k], eager[k]), (rep, k)
