@@ -35,6 +35,8 @@
 // one byte permute per two words gathers the flags and v_bcnt counts them.
 #pragma once
 
+#include <type_traits>
+
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
@@ -200,6 +202,9 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
     constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
     constexpr int EB = (int)sizeof(T);
+    // score tiles per scheduling region: two accumulation chains at a time where
+    // the registers allow it
+    constexpr int SGRP = sizeof(T) == 2 && C <= 64 ? 2 : 1;
     // gather jobs: 4 consecutive rows x one 16-byte piece (of qk and of v)
     constexpr int JOBS = (C / 4) * VPR;
     constexpr int JPT = (JOBS + NTH - 1) / NTH;        // jobs per thread
@@ -228,29 +233,41 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 
     if (tid < 33) sm.neg_log2[tid] = (tid % 2 == 0 && tid / 2 < n_r) ? -__log2f((float)(n_r - tid / 2)) : 0.f;
 
-    // Loaded values are kept raw until the iteration that uses them (positions
-    // are clamped, chunk ids masked and packed there): processing a value right
-    // after its load would make the wave wait for every earlier load as well,
-    // including the gathers meant to overlap the current chunk's math.
+    // Loaded values are kept raw until the iteration that stores them
+    // (positions are clamped, chunk ids masked and packed there): processing a
+    // value right after its load would make the wave wait for every earlier
+    // load as well, the gathers meant to overlap the math included.  Every
+    // iteration issues the same loads (past the run's end they repeat its last
+    // chunk and are never stored), so the compiler's wait counts are the same
+    // in every iteration.
     // Positions come from the caller's perm: every gather stays inside the row.
     auto clamp_pos = [&](int p) { return min(max(p, 0), L - 1); };
 
-    int gpos[JPT][4];      // raw perm entries of this thread's gather rows, next chunk to load
-    int mypos = 0;         // raw perm entry of row tid (tid < C), next chunk to load
+    // Per-row jobs: job m < C * NW loads word m % NW (rounds 2w and 2w+1) of
+    // the packed chunk ids of row m / NW and, for m % NW == 0, the row's
+    // position (and its window id in the same-bucket variant).
+    constexpr int MJOBS = C * NW;
+    constexpr int MJPT = (MJOBS + NTH - 1) / NTH;
+    int gpos[JPT][4];          // raw perm entries of this thread's gather rows, next chunk to load
+    int mpos[MJPT];            // raw perm entries of this thread's per-row jobs, next chunk to load
     u32x4 kreg[JPT][4], vreg[JPT][4];
-    uint32_t craw[2 * NW];    // chunk ids of row tid per round (raw), chunk held in registers
-    uint32_t ridraw = 0;       // same-bucket variant: row tid's window id in this round
-    int rpos = 0;          // position of row tid for the chunk held in registers
+    int rpos[MJPT];            // clamped positions of the per-row jobs' rows, chunk in registers
+    uint32_t clo[MJPT], chi[MJPT];   // raw chunk ids of rounds 2w and 2w+1, chunk in registers
+    uint32_t ridraw[MJPT];     // same-bucket variant: the row's window id in this round
 
     auto fetch_positions = [&](int kk) {
 #pragma unroll
         for (int jb = 0; jb < JPT; ++jb) {
             const int job = tid + jb * NTH;
             const int rg = (job < JOBS ? job : 0) / VPR;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gpos[jb][i] = pr[kk * C + 4 * rg + i];
+            const int4 p4 = *reinterpret_cast<const int4*>(pr + kk * C + 4 * rg);
+            gpos[jb][0] = p4.x; gpos[jb][1] = p4.y; gpos[jb][2] = p4.z; gpos[jb][3] = p4.w;
         }
-        mypos = pr[kk * C + tid % C];          // rows past C repeat (loads without branches)
+#pragma unroll
+        for (int mj = 0; mj < MJPT; ++mj) {
+            const int m = (tid + mj * NTH) % MJOBS;     // jobs past the end repeat (no branches)
+            mpos[mj] = pr[kk * C + m / NW];
+        }
     };
     auto fetch_rows = [&]() {
 #pragma unroll
@@ -264,13 +281,18 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + row);
             }
         }
-        rpos = clamp_pos(mypos);
-        const int16_t* cr = cb + (long)rpos * n_r;
-        if constexpr (NDW > 0) {
 #pragma unroll
-            for (int h = 0; h < 2 * NDW; ++h) craw[h] = (uint16_t)cr[min(h, n_r - 1)];
+        for (int mj = 0; mj < MJPT; ++mj) {
+            const int m = (tid + mj * NTH) % MJOBS;
+            rpos[mj] = clamp_pos(mpos[mj]);
+            const int16_t* cr = cb + (long)rpos[mj] * n_r;
+            if constexpr (NDW > 0) {
+                const int w = m % NW;
+                clo[mj] = (uint16_t)cr[min(2 * w, n_r - 1)];
+                chi[mj] = (uint16_t)cr[min(2 * w + 1, n_r - 1)];
+            }
+            if constexpr (SAME) ridraw[mj] = (uint16_t)cr[r];
         }
-        if constexpr (SAME) ridraw = (uint16_t)cr[r];
     };
     auto store_rows = [&](int sl) {
 #pragma unroll
@@ -299,15 +321,21 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 }
             }
         }
-        if (tid < C) {
-            sm.pos[sl][tid] = rpos;
-            if constexpr (SAME) sm.rid[sl][tid] = (int)ridraw;
-            // rounds past n_r hold 0 for keys and queries alike (always inside)
 #pragma unroll
-            for (int w = 0; w < NDW; ++w) {   // nothing when NDW = 0
-                const uint32_t lo = 2 * w < n_r ? craw[2 * w] : 0u;
-                const uint32_t hi = 2 * w + 1 < n_r ? craw[2 * w + 1] : 0u;
-                sm.cid[sl][tid * NDW + w] = lo | (hi << 16);
+        for (int mj = 0; mj < MJPT; ++mj) {
+            const int m = tid + mj * NTH;
+            if (m < MJOBS) {
+                const int row = m / NW, w = m % NW;
+                if (w == 0) {
+                    sm.pos[sl][row] = rpos[mj];
+                    if constexpr (SAME) sm.rid[sl][row] = (int)ridraw[mj];
+                }
+                // rounds past n_r hold 0 for keys and queries alike (always inside)
+                if constexpr (NDW > 0) {
+                    const uint32_t lo = 2 * w < n_r ? clo[mj] : 0u;
+                    const uint32_t hi = 2 * w + 1 < n_r ? chi[mj] : 0u;
+                    sm.cid[sl][row * NDW + w] = lo | (hi << 16);
+                }
             }
         }
     };
@@ -319,24 +347,13 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     const int it0 = lookback ? 1 : 0;
     const int nit = (k1 - k0) + it0;
     auto chunk_of = [&](int it) {
-        const int c = k0 - it0 + it;
+        const int c = k0 - it0 + min(it, nit - 1);     // past the end: the last chunk again
         return c < 0 ? c + nchunks : c;
     };
 
-    fetch_positions(chunk_of(0));
-    fetch_rows();
-    if (1 < nit) fetch_positions(chunk_of(1));
-
-
-    for (int it = 0; it < nit; ++it) {
-        const int cur = it & 1, prv = cur ^ 1;
-        store_rows(cur);               // slot of iteration it-2, released by the last barrier
-        __syncthreads();
-        if (it + 1 < nit) {
-            fetch_rows();              // iteration it+1 (positions fetched an iteration ago)
-            if (it + 2 < nit) fetch_positions(chunk_of(it + 2));
-        }
-        if (it >= it0) {
+    // Chunk it in slot cur = it % 2 (its look-back in the other slot) against
+    // the 16 queries of this wave.
+    auto compute = [&](int it, int cur, int prv) __attribute__((always_inline)) {
             const bool has_prev = it > 0;
             const int qrow = wave * 16 + r16;
             const int qpos = sm.pos[cur][qrow];
@@ -362,6 +379,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, ks * KSTEP + g * KPL)]), bq[ks], s[t]);
+                if (t % SGRP == SGRP - 1) __builtin_amdgcn_sched_barrier(0);
             }
 
             // ---- scale and duplicate counts; self penalty on the diagonal tile;
@@ -401,6 +419,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     s[t][j] = sc;
                     mx = fmaxf(mx, sc);
                 }
+                if (t % SGRP == SGRP - 1) __builtin_amdgcn_sched_barrier(0);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -448,6 +467,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                         const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                         o[dt] = M::mma(a, b, o[dt]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
                 // one instruction per key column j: lane group g holds key 4g+j
@@ -486,8 +506,28 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 }
             }
             if (g == 0) lb[qpos] = (mx + __log2f(sum)) * LN2;
-        }
+    };
+
+    // One iteration: store chunk it into slot it % 2 (a compile-time slot: the
+    // loop is unrolled by two), load the rows of chunk it+1 and the positions
+    // of chunk it+2, compute chunk it.  The scheduling barriers in compute keep
+    // the compiler from hoisting a whole phase's LDS reads at once, which would
+    // raise the registers past two waves per SIMD.
+    auto step = [&](int it, auto slot) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot)::value;
+        store_rows(SL);                // slot of iteration it-2, released by the last barrier
         __syncthreads();
+        fetch_rows();                  // chunk it+1 (positions fetched an iteration ago)
+        fetch_positions(chunk_of(it + 2));
+        if (it >= it0) compute(it, SL, 1 - SL);
+        __syncthreads();
+    };
+    fetch_positions(chunk_of(0));
+    fetch_rows();
+    fetch_positions(chunk_of(1));
+    for (int it = 0; it < nit; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
 }
 
