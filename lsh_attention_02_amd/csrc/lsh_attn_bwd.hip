@@ -309,6 +309,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, e)]), bq[ks], s[t]);
                     dp[t] = M::mma(M::load(&sm.v[slk][KL::off(krow, e)]), bd[ks], dp[t]);
                 }
+                if (t & 1) __builtin_amdgcn_sched_barrier(0);
             }
             // P and dS (in place of s and dp)
 #pragma unroll
@@ -342,6 +343,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     s[t][j] = p;
                     dp[t][j] = p * (dp[t][j] - dlt);
                 }
+                if (t & 1) __builtin_amdgcn_sched_barrier(0);
             }
             // P and dS to LDS, [window key][query], two queries per 4-byte store:
             // lanes 2i and 2i+1 (queries qe, qe+1) swap halves with one DPP move;
@@ -393,6 +395,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                         const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(kr + 8 * ((kg + 4) ^ swz));
                         o[dt] = M::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), b, o[dt]);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 T* orow = dq_r + rbase + (long)qpos * D;
 #pragma unroll
@@ -455,6 +458,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                             acck[dt][kt] = M::mma(aq, bs[kt], acck[dt][kt]);
                             accv[dt][kt] = M::mma(ad, bp[kt], accv[dt][kt]);
                         }
+                        if (dt & 1) __builtin_amdgcn_sched_barrier(0);
                     }
                 }
                 if (!cur_role) write_keys();             // chunk c - 1 is complete

@@ -9,14 +9,17 @@
 // scan followed by one cross-half exchange.  The token operands stay in
 // registers for every round.
 //
-// R streams through LDS in groups of GROUP_COLS columns, transposed to
-// [column][d] so that each MFMA A-operand read is 16 contiguous bytes; the
-// transpose happens in registers (VE x VE blocks) and the 16-byte pieces are
-// XOR-swizzled within each row so that stores and reads are free of LDS bank
-// conflicts.  The
-// groups of all rounds form one sequence; the next group is loaded from global
-// memory into registers while the current one feeds the MFMAs (two LDS
-// buffers, one barrier per group).
+// R streams through LDS in groups of columns; the groups of all rounds form
+// one sequence, and the next group is loaded while the current one feeds the
+// MFMAs (two LDS buffers, one barrier per group).  Two kernels:
+//   k_hash_tr (bf16, rows of R 16-byte aligned): the group is copied from
+//     global memory straight into LDS in R's own [d][column] layout, and the
+//     MFMA operands are read with the transposing LDS load;
+//   k_hash (fp32, or unaligned rows): the group is loaded into registers,
+//     transposed there to [column][d] and stored, so that each operand read
+//     is contiguous.
+// Both LDS layouts XOR-swizzle 16-byte pieces so that stores and operand reads
+// are free of bank conflicts.
 //
 // argmax over [p, -p] is the argmax of |p| with the sign selecting the half:
 // entry k of p and entry k of -p have the same magnitude.  The scan keeps the
@@ -273,11 +276,214 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     }
 }
 
+
+// ---- bf16 with 16-byte aligned R rows: R staged straight from global memory
+// into LDS in its own [d][column] layout (one 16-byte global-to-LDS load per
+// lane and piece, no registers, no transpose instructions), and the MFMA A
+// operand read with the transposing LDS load: ds_read_b64_tr_b16 gives lane i
+// of each 16-lane group element i % 4 of the 4 elements that lanes 4k + i / 4
+// (k = 0..3) address.  When lane 4k + q addresses row d0 + k, columns
+// cb + 4q .. +3, lane i receives column cb + i of rows d0 .. d0 + 3: four
+// consecutive k of its A row.  Two such reads (rows d0 and d0 + 4) give the 8
+// elements of one 32x32x16 operand.
+constexpr int TR_COLS = 128;                     // R columns staged per step
+constexpr int TR_TILES = TR_COLS / 32;
+constexpr int TR_ROWB = TR_COLS * 2;             // bytes per staged row
+
+// Piece p (8 columns, 16 bytes) of staged row d sits at p ^ 4 (d % 4): the 32
+// lanes of one read pass (4 consecutive rows x 8 half-pieces) then touch all 64
+// banks once.
+__device__ __forceinline__ int tr_piece(int p, int d) { return p ^ (4 * (d & 3)); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 tr_read(const char* p)
+{
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)p);
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Group (r, c0) of R into buf: piece P = i * HASH_THREADS + tid is staged row
+// P / 16, LDS slot P % 16 (global piece slot ^ 4 (row % 4)), so one wave
+// instruction fills 1 KiB of consecutive LDS.  Pieces past ncol load a valid
+// piece instead and are zeroed by tr_zero_tail once the loads have landed.
+template <int D>
+__device__ __forceinline__ void tr_stage(const bf16_t* __restrict__ Rr, int c0, int ncol, char* buf)
+{
+    constexpr int ITERS = D * 16 / HASH_THREADS;
+    const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+        const int P = i * HASH_THREADS + tid;
+        const int d = P >> 4;
+        const int col = min(c0 + 8 * tr_piece(P & 15, d), ncol - 8);
+        __builtin_amdgcn_global_load_lds(Rr + (long)d * ncol + col,
+                                         (__attribute__((address_space(3))) void*)(buf + 16 * (i * HASH_THREADS + wave * 64)),
+                                         16, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void tr_zero_tail(int c0, int ncol, char* buf)
+{
+#pragma unroll
+    for (int i = 0; i < D * 16 / HASH_THREADS; ++i) {
+        const int P = i * HASH_THREADS + threadIdx.x;
+        if (c0 + 8 * tr_piece(P & 15, P >> 4) >= ncol)
+            *reinterpret_cast<u32x4*>(buf + 16 * P) = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(HASH_THREADS)
+void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int32_t* __restrict__ buckets,
+               int L, int n_r, int ncol, int tiles_per_bh)
+{
+    using M = Mfma<bf16_t>;
+    constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+    // two buffers as separate arrays, so that the compiler can tell the staged
+    // loads into one from the operand reads of the other
+    __shared__ __attribute__((aligned(1024))) char rt0[D * TR_ROWB];
+    __shared__ __attribute__((aligned(1024))) char rt1[D * TR_ROWB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const long bh = blockIdx.x / tiles_per_bh;
+    const int tok0 = (blockIdx.x % tiles_per_bh) * HASH_TOK_WG + wave * HASH_NT * 32;
+    const bf16_t* q = qk + bh * (long)L * D;
+
+    typename M::Frag bq[HASH_NT][NKS];
+#pragma unroll
+    for (int u = 0; u < HASH_NT; ++u) {
+        const int tok = tok0 + 32 * u + n;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            bq[u][ks] = tok < L ? M::load(q + (long)tok * D + ks * KSTEP + hh * KPL) : M::zero();
+    }
+
+    const int groups_per_round = (ncol + TR_COLS - 1) / TR_COLS;
+    const int ngroups = n_r * groups_per_round;
+
+    // this lane's transposing-read offsets, per column tile: group G = lane / 16
+    // (column half G % 2, k half G / 2), lane 4k + q of it addresses row
+    // 8 (G / 2) + k and columns 32 ct + 16 (G % 2) + 4q
+    int toff[TR_TILES];
+    {
+        const int G = lane >> 4, j = lane & 15, k = j >> 2, qq = j & 3;
+#pragma unroll
+        for (int ct = 0; ct < TR_TILES; ++ct)
+            toff[ct] = (8 * (G >> 1) + k) * TR_ROWB
+                     + 16 * tr_piece(4 * ct + 2 * (G & 1) + (qq >> 1), k) + 8 * (qq & 1);
+    }
+
+    float bmag[HASH_NT];
+    int btile[HASH_NT];
+    f32x16 keep[HASH_NT];
+
+    auto group_rc = [&](int g, int& r, int& c0) {
+        r = g / groups_per_round;
+        c0 = (g % groups_per_round) * TR_COLS;
+    };
+    {
+        tr_stage<D>(R, 0, ncol, rt0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (TR_COLS > ncol) tr_zero_tail<D>(0, ncol, rt0);
+        __syncthreads();
+    }
+
+    // one group: the next group's R goes into the other buffer while this one
+    // feeds the MFMAs
+    auto group = [&](int g, const char* buf, char* nbuf) __attribute__((always_inline)) {
+        int r, c0;
+        group_rc(g, r, c0);
+        if (c0 == 0) {
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u) { bmag[u] = 0.f; btile[u] = -1; keep[u] = f32x16{}; }
+        }
+        int r1, c1;
+        group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
+        tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
+        // staged columns past ncol hold zeros, so their projections are exactly
+        // 0 and can never beat a record: no column test is needed
+        const int tiles = min(TR_TILES, (ncol - c0 + 31) >> 5);
+#pragma unroll
+        for (int ct = 0; ct < TR_TILES; ++ct) {
+            if (ct < tiles) {
+                f32x16 acc[HASH_NT];
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) acc[u] = f32x16{};
+                typename M::Frag a[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const char* p = buf + toff[ct] + 16 * ks * TR_ROWB;
+                    a[ks] = __builtin_shufflevector(tr_read(p), tr_read(p + 4 * TR_ROWB),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                    for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a[ks], bq[u][ks], acc[u]);
+                }
+                const int tile = (c0 >> 5) + ct;
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) {
+                    float m = fabsf(acc[u][0]);
+#pragma unroll
+                    for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(acc[u][j]));
+                    const bool up = m > bmag[u];
+                    bmag[u] = up ? m : bmag[u];
+                    btile[u] = up ? tile : btile[u];
+                    keep[u] = up ? acc[u] : keep[u];
+                }
+            }
+        }
+        if (c0 + TR_COLS >= ncol) {                  // last group of round r
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u) {
+                int jj = 0;
+                float bv = 0.f;
+#pragma unroll
+                for (int j = 15; j >= 0; --j) {
+                    const bool hit = fabsf(keep[u][j]) == bmag[u];
+                    jj = hit ? j : jj;
+                    bv = hit ? keep[u][j] : bv;
+                }
+                int bi = btile[u] < 0 ? INT_MAX : 32 * btile[u] + 4 * hh + 8 * (jj >> 2) + (jj & 3);
+                if (btile[u] < 0) bv = 0.f;
+                const float ov = __shfl_xor(bv, 32);
+                const int oi = __shfl_xor(bi, 32);
+                if (fabsf(ov) > fabsf(bv) || (fabsf(ov) == fabsf(bv) && oi < bi)) { bv = ov; bi = oi; }
+                if (bi == INT_MAX) bi = 0;
+                const int tok = tok0 + 32 * u + n;
+                if (hh == 0 && tok < L)
+                    buckets[((long)bh * n_r + r) * L + tok] = bi + (bv < 0.f ? ncol : 0);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next group has landed
+        if (g + 1 < ngroups && c1 + TR_COLS > ncol) tr_zero_tail<D>(c1, ncol, nbuf);
+        __syncthreads();
+    };
+    for (int g = 0; g < ngroups; g += 2) {
+        group(g, rt0, rt1);
+        if (g + 1 < ngroups) group(g + 1, rt1, rt0);
+    }
+}
+
 template <typename T, int D>
 hipError_t launch(const void* qk, const void* R, int32_t* buckets, long bh, int L, int n_r,
                   int ncol, hipStream_t s)
 {
     const int tiles = (L + HASH_TOK_WG - 1) / HASH_TOK_WG;
+    if constexpr (sizeof(T) == 2) {
+        if (ncol % 8 == 0) {                // 16-byte aligned rows of R
+            hipLaunchKernelGGL((k_hash_tr<D>), dim3((unsigned)(bh * tiles)), dim3(HASH_THREADS), 0, s,
+                               static_cast<const bf16_t*>(qk), static_cast<const bf16_t*>(R), buckets,
+                               L, n_r, ncol, tiles);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((k_hash<T, D>), dim3((unsigned)(bh * tiles)), dim3(HASH_THREADS), 0, s,
                        static_cast<const T*>(qk), static_cast<const T*>(R), buckets, L, n_r, ncol,
                        tiles);
