@@ -169,13 +169,14 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
         draw = deb[rpos];
     };
     // transposed store of 4 rows x VE elements into a [d][row] table (the
-    // forward's v^T layout: groups of 4 rows, group rg of row d at rg ^ vt_swz(d))
+    // forward's 16-bit v^T layout: groups of 4 rows, paired as (rg, rg + 4))
     auto store_t = [&](char* base, const u32x4 (&reg)[4], int rg, int piece) {
 #pragma unroll
         for (int x = 0; x < VE; ++x) {
-            const int d = piece * VE + x;
-            char* dst = base + d * TROWB + 8 * (rg ^ vt_swz<C>(d));
-            const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+            const int xe = x ^ (piece & 1);            // element order x ^ 1 on odd pieces
+            const int d = piece * VE + xe;
+            char* dst = base + d * TROWB + vt_group_off<C>(rg, d);
+            const uint32_t sel = 0x05040100u + 0x02020202u * (uint32_t)(xe & 1);
             const uint32_t w0 = __builtin_amdgcn_perm(reg[1][x >> 1], reg[0][x >> 1], sel);
             const uint32_t w1 = __builtin_amdgcn_perm(reg[3][x >> 1], reg[2][x >> 1], sel);
             *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
@@ -390,10 +391,8 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     for (int dt = 0; dt < DT; ++dt) {
                         const int d = dt * 16 + r16;
                         const char* kr = sm.kt[slk] + d * TROWB;
-                        const int swz = vt_swz<C>(d);
-                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(kr + 8 * (kg ^ swz));
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(kr + 8 * ((kg + 4) ^ swz));
-                        o[dt] = M::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), b, o[dt]);
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + vt_group_off<C>(kg, d));
+                        o[dt] = M::mma(a, b, o[dt]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -444,15 +443,9 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         const int d = dt * 16 + r16;
-                        const int swz = vt_swz<C>(d);
-                        const char* qr = sm.kt[sl] + d * TROWB;
-                        const char* dr = sm.dot + d * TROWB;
-                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(qr + 8 * (qg ^ swz));
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(qr + 8 * ((qg + 4) ^ swz));
-                        const bf16x4 c0 = *reinterpret_cast<const bf16x4*>(dr + 8 * (qg ^ swz));
-                        const bf16x4 c1 = *reinterpret_cast<const bf16x4*>(dr + 8 * ((qg + 4) ^ swz));
-                        const bf16x8 aq = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const bf16x8 ad = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const int go = vt_group_off<C>(qg, d);   // groups qg and qg + 4: one pair
+                        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.kt[sl] + d * TROWB + go);
+                        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(sm.dot + d * TROWB + go);
 #pragma unroll
                         for (int kt = 0; kt < KTW; ++kt) {
                             acck[dt][kt] = M::mma(aq, bs[kt], acck[dt][kt]);

@@ -137,14 +137,37 @@ __device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], c
     }
 }
 
-// V^T rows hold a slot's keys in groups of 4 consecutive keys.  Group kg of row
-// d is stored at position kg ^ vt_swz(d).  The PV operand reads (16 rows d of
-// one 16-row tile, one group each) and the transposed stores (rows 8p + x for
-// 16 pieces p, one group each) then touch distinct bank groups.
+// V^T rows hold a slot's keys in groups of 4 consecutive keys.
+// 32-bit elements: group kg of row d is the 16 bytes at kg ^ vt_swz(d).
+// 16-bit elements: groups kg and kg + 4 (kg with bit 2 clear) form one 16-byte
+// pair: the two groups that one PV operand combines (keys 4g.. of tiles t0 and
+// t0 + 1), so the operand is a single 16-byte read.  Pair p of row d sits at
+// p ^ vt_pair_swz(d) = p ^ f(d % 16) ^ 2 (d / 16), f(r) = r (r / 2 at chunk 32).
+// Each read pass (16 lanes: the lane-quad groups of a 16-byte access) of rows
+// 16 dt + r16 then covers the 64 banks once, and the transposed 8-byte stores,
+// where lanes of odd pieces store their rows' elements in the order x ^ 1 (so
+// that both row parities occur in every store instruction), hit each bank at
+// most twice (four times at chunk 32), as the previous single-group layout did
+// (both checked exhaustively against the hardware's pass groups).
 template <int C>
 __device__ __forceinline__ int vt_swz(int d)
 {
     return (d ^ (d >> 3)) & (C / 4 - 1);
+}
+
+template <int C>
+__device__ __forceinline__ int vt_pair_swz(int d)
+{
+    const int r16 = d & 15;
+    return ((C == 32 ? r16 >> 1 : r16) ^ (2 * (d >> 4))) & (C / 8 - 1);
+}
+
+// byte offset of 4-key group kg within a 16-bit V^T row d
+template <int C>
+__device__ __forceinline__ int vt_group_off(int kg, int d)
+{
+    const int pair = (kg & 3) | ((kg >> 3) << 2);
+    return 16 * (pair ^ vt_pair_swz<C>(d)) + 8 * ((kg >> 2) & 1);
 }
 
 // qk rows in LDS.  A 16-byte LDS access is served in four passes of 16 lanes;
@@ -209,6 +232,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     constexpr int JOBS = (C / 4) * VPR;
     constexpr int JPT = (JOBS + NTH - 1) / NTH;        // jobs per thread
     __shared__ __attribute__((aligned(16))) S sm;
+    static_assert(offsetof(S, vt) % 16 == 0, "16-byte V^T reads");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;          // MFMA 16x16 lane coordinates
@@ -307,14 +331,17 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 // the 4 keys 4rg..4rg+3 of v^T row d = piece*VE + x
 #pragma unroll
                 for (int x = 0; x < VE; ++x) {
-                    const int d = piece * VE + x;
-                    char* dst = sm.vt[sl] + d * VROWB + 4 * EB * (rg ^ vt_swz<C>(d));
                     if constexpr (sizeof(T) == 2) {
-                        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+                        const int xe = x ^ (piece & 1);        // element order x ^ 1 on odd pieces
+                        const int d = piece * VE + xe;
+                        char* dst = sm.vt[sl] + d * VROWB + vt_group_off<C>(rg, d);
+                        const uint32_t sel = 0x05040100u + 0x02020202u * (uint32_t)(xe & 1);
                         const uint32_t w0 = __builtin_amdgcn_perm(vreg[jb][1][x >> 1], vreg[jb][0][x >> 1], sel);
                         const uint32_t w1 = __builtin_amdgcn_perm(vreg[jb][3][x >> 1], vreg[jb][2][x >> 1], sel);
                         *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
                     } else {
+                        const int d = piece * VE + x;
+                        char* dst = sm.vt[sl] + d * VROWB + 16 * (rg ^ vt_swz<C>(d));
                         const u32x4 w4 = {vreg[jb][0][x], vreg[jb][1][x], vreg[jb][2][x], vreg[jb][3][x]};
                         *reinterpret_cast<u32x4*>(dst) = w4;
                     }
@@ -372,12 +399,12 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             f32x4 s[NKT];
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
-                s[t] = f32x4{};
-                if (t < CT && !has_prev) continue;
+                if (t < CT && !has_prev) { s[t] = f32x4{}; continue; }
                 const int slk = t < CT ? prv : cur;
                 const int krow = (t % CT) * 16 + r16;
+                s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, g * KPL)]), bq[0], f32x4{});
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
+                for (int ks = 1; ks < NKS; ++ks)
                     s[t] = M::mma(M::load(&sm.k[slk][KL::off(krow, ks * KSTEP + g * KPL)]), bq[ks], s[t]);
                 if (t % SGRP == SGRP - 1) __builtin_amdgcn_sched_barrier(0);
             }
@@ -459,12 +486,9 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         const int d = dt * 16 + r16;
-                        const char* vr = sm.vt[slk] + d * VROWB;
-                        const int sw = vt_swz<C>(d);
-                        const int kg = key0 >> 2;          // groups kg (tile t0) and kg + 4 (t0 + 1)
-                        const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(vr + 8 * (kg ^ sw));
-                        const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(vr + 8 * ((kg + 4) ^ sw));
-                        const bf16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        // groups kg (tile t0) and kg + 4 (tile t0 + 1): one pair
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            sm.vt[slk] + d * VROWB + vt_group_off<C>(key0 >> 2, d));
                         o[dt] = M::mma(a, b, o[dt]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
