@@ -142,13 +142,13 @@ __device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], c
 // 16-bit elements: groups kg and kg + 4 (kg with bit 2 clear) form one 16-byte
 // pair: the two groups that one PV operand combines (keys 4g.. of tiles t0 and
 // t0 + 1), so the operand is a single 16-byte read.  Pair p of row d sits at
-// p ^ vt_pair_swz(d) = p ^ f(d % 16) ^ 2 (d / 16), f(r) = r (r / 2 at chunk 32).
-// Each read pass (16 lanes: the lane-quad groups of a 16-byte access) of rows
-// 16 dt + r16 then covers the 64 banks once, and the transposed 8-byte stores,
-// where lanes of odd pieces store their rows' elements in the order x ^ 1 (so
-// that both row parities occur in every store instruction), hit each bank at
-// most twice (four times at chunk 32), as the previous single-group layout did
-// (both checked exhaustively against the hardware's pass groups).
+// p ^ vt_pair_swz(d) = p ^ f(d % 16) ^ 5 (d / 16), f(r) = r (r / 2 at chunk 32).
+// A 16-byte read is served in passes of 16 lanes (the lane quads of even, then
+// odd, bit parity in each half-wave); each pass of the operand reads of rows
+// 16 dt + r16 covers the 64 banks once (checked exhaustively, and measured:
+// no conflict cycles).  The transposed 8-byte stores (lanes of odd pieces store
+// their rows' elements in the order x ^ 1) measured 4 conflict cycles per store
+// instruction, 8 instructions per chunk: negligible next to the reads.
 template <int C>
 __device__ __forceinline__ int vt_swz(int d)
 {
@@ -159,7 +159,7 @@ template <int C>
 __device__ __forceinline__ int vt_pair_swz(int d)
 {
     const int r16 = d & 15;
-    return ((C == 32 ? r16 >> 1 : r16) ^ (2 * (d >> 4))) & (C / 8 - 1);
+    return ((C == 32 ? r16 >> 1 : r16) ^ (5 * (d >> 4))) & (C / 8 - 1);
 }
 
 // byte offset of 4-key group kg within a 16-bit V^T row d
