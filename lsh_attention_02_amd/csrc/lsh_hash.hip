@@ -286,6 +286,10 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
 // cb + 4q .. +3, lane i receives column cb + i of rows d0 .. d0 + 3: four
 // consecutive k of its A row.  Two such reads (rows d0 and d0 + 4) give the 8
 // elements of one 32x32x16 operand.
+// Workgroups of 8 waves at d 128 (one per CU: the registers allow two waves
+// per SIMD), of 4 waves at d 64, where three waves per SIMD fit: three
+// independent workgroups per CU, whose barriers do not hold each other up.
+template <int D> constexpr int tr_waves() { return D == 64 ? 4 : 8; }
 constexpr int TR_COLS = 128;                     // R columns staged per step
 constexpr int TR_TILES = TR_COLS / 32;
 constexpr int TR_ROWB = TR_COLS * 2;             // bytes per staged row
@@ -304,22 +308,23 @@ __device__ __forceinline__ bf16x4 tr_read(const char* p)
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// Group (r, c0) of R into buf: piece P = i * HASH_THREADS + tid is staged row
+// Group (r, c0) of R into buf: piece P = i * NTH + tid (NTH threads) is staged row
 // P / 16, LDS slot P % 16 (global piece slot ^ 4 (row % 4)), so one wave
 // instruction fills 1 KiB of consecutive LDS.  Pieces past ncol load a valid
 // piece instead and are zeroed by tr_zero_tail once the loads have landed.
 template <int D>
 __device__ __forceinline__ void tr_stage(const bf16_t* __restrict__ Rr, int c0, int ncol, char* buf)
 {
-    constexpr int ITERS = D * 16 / HASH_THREADS;
+    constexpr int NTH = tr_waves<D>() * 64;
+    constexpr int ITERS = D * 16 / NTH;
     const int tid = threadIdx.x, wave = tid >> 6;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
-        const int P = i * HASH_THREADS + tid;
+        const int P = i * NTH + tid;
         const int d = P >> 4;
         const int col = min(c0 + 8 * tr_piece(P & 15, d), ncol - 8);
         __builtin_amdgcn_global_load_lds(Rr + (long)d * ncol + col,
-                                         (__attribute__((address_space(3))) void*)(buf + 16 * (i * HASH_THREADS + wave * 64)),
+                                         (__attribute__((address_space(3))) void*)(buf + 16 * (i * NTH + wave * 64)),
                                          16, 0, 0);
     }
 }
@@ -327,16 +332,17 @@ __device__ __forceinline__ void tr_stage(const bf16_t* __restrict__ Rr, int c0, 
 template <int D>
 __device__ __forceinline__ void tr_zero_tail(int c0, int ncol, char* buf)
 {
+    constexpr int NTH = tr_waves<D>() * 64;
 #pragma unroll
-    for (int i = 0; i < D * 16 / HASH_THREADS; ++i) {
-        const int P = i * HASH_THREADS + threadIdx.x;
+    for (int i = 0; i < D * 16 / NTH; ++i) {
+        const int P = i * NTH + threadIdx.x;
         if (c0 + 8 * tr_piece(P & 15, P >> 4) >= ncol)
             *reinterpret_cast<u32x4*>(buf + 16 * P) = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(HASH_THREADS)
+__global__ __launch_bounds__(tr_waves<D>() * 64)
 void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int32_t* __restrict__ buckets,
                int L, int n_r, int ncol, int tiles_per_bh)
 {
@@ -350,7 +356,7 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const long bh = blockIdx.x / tiles_per_bh;
-    const int tok0 = (blockIdx.x % tiles_per_bh) * HASH_TOK_WG + wave * HASH_NT * 32;
+    const int tok0 = (blockIdx.x % tiles_per_bh) * (tr_waves<D>() * HASH_NT * 32) + wave * HASH_NT * 32;
     const bf16_t* q = qk + bh * (long)L * D;
 
     typename M::Frag bq[HASH_NT][NKS];
@@ -478,9 +484,11 @@ hipError_t launch(const void* qk, const void* R, int32_t* buckets, long bh, int 
     const int tiles = (L + HASH_TOK_WG - 1) / HASH_TOK_WG;
     if constexpr (sizeof(T) == 2) {
         if (ncol % 8 == 0) {                // 16-byte aligned rows of R
-            hipLaunchKernelGGL((k_hash_tr<D>), dim3((unsigned)(bh * tiles)), dim3(HASH_THREADS), 0, s,
+            constexpr int TOK = tr_waves<D>() * HASH_NT * 32;
+            const int trt = (L + TOK - 1) / TOK;
+            hipLaunchKernelGGL((k_hash_tr<D>), dim3((unsigned)(bh * trt)), dim3(tr_waves<D>() * 64), 0, s,
                                static_cast<const bf16_t*>(qk), static_cast<const bf16_t*>(R), buckets,
-                               L, n_r, ncol, tiles);
+                               L, n_r, ncol, trt);
             return hipGetLastError();
         }
     }
