@@ -46,6 +46,12 @@ SMALL = {
     "clustered_b2h2_L4096": W("clu", batch=2, heads=2, seq_len=4096, n_buckets=256, n_rounds=4,
                               causal=False, clustered=True, seed=107),
     "rounds16_buckets1000": W("r16", seq_len=2048, n_buckets=1000, n_rounds=16, seed=108),
+    # hash: 200 columns per round, one full and one partial group of 128 staged
+    # columns (the bf16 path copies R into LDS and zeroes the columns past 200)
+    "groups_d128_nb400_r3": W("grp128", heads=2, seq_len=2048, d_head=128, n_buckets=400,
+                              n_rounds=3, seed=111),
+    "groups_d64_nb400_r2": W("grp64", heads=2, seq_len=1536, n_buckets=400, n_rounds=2,
+                             causal=False, seed=112),
     "one_chunk": W("one", seq_len=64, n_buckets=6, n_rounds=3, seed=109),
     "two_chunks_nb2": W("two", seq_len=128, n_buckets=2, n_rounds=1, seed=110),
 }
