@@ -2,8 +2,8 @@
 // p = qk_i · R_r  (Ultralytics glossary "Reformer", section on LSH attention;
 // modulabs-hub Reformer notes, "Locality sensitive hashing").
 //
-// One workgroup = HASH_WAVES waves; each wave owns HASH_NT tiles of 32 tokens
-// of one (batch row, head).  The tokens are the MFMA column (lane) axis and the
+// One workgroup = 8 waves (4 for k_hash_tr at d 64); each wave owns HASH_NT
+// tiles of 32 tokens of one (batch row, head).  The tokens are the MFMA column (lane) axis and the
 // projection columns are the row (register) axis, so a token's projections
 // land in two lanes (l, l+32) as registers and the argmax is an in-register
 // scan followed by one cross-half exchange.  The token operands stay in
