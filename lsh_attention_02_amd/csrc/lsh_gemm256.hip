@@ -13,12 +13,19 @@
 // consecutive output columns of a row: one 8-byte store each.
 //
 // K steps of 64: the operand tiles (2 x 32 KiB, swizzled as lin_swz) are double
-// buffered in LDS (128 KiB, one workgroup per CU).  Step kt+1 is held in
-// registers while step kt is multiplied, stored into the other buffer after it,
-// and step kt+2 is loaded right after the barrier; loads past the last step
-// repeat it and rows past M or N repeat the last row (never stored), so the
-// loop has no branches.  (Deeper software pipelining across the barrier, and a
-// second register set for two steps in flight, measured no faster.)
+// buffered in LDS (128 KiB, one workgroup per CU) and copied straight from
+// global memory with global_load_lds_dwordx4: each lane copies one 16-byte
+// piece, chosen so that the 1 KiB a wave instruction writes is 8 swizzled rows;
+// no registers, LDS store instructions or waits on them sit between the MFMAs.
+// Step kt is multiplied from one buffer while step kt+1 is copied into the
+// other; the barrier after step kt (every wave done with its buffer, step kt+1
+// landed) starts the copy of step kt+2 into the buffer just freed.  Copies
+// past the last step repeat it and rows past M or N repeat the last row (never
+// stored), so the loop has no branches.  The source rows are 32-bit byte
+// offsets from a per-step base (operands under 4 GiB, checked by the caller).
+// (Unrolling the loop by two, so that each buffer is a compile-time symbol,
+// made the compiler hoist enough addresses to spill; copying through registers
+// instead, as an earlier version did, measured 12-17% slower.)
 #include "lsh_device.h"
 #include "lsh_internal.h"
 #include "lsh_linear.h"
@@ -39,8 +46,12 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
                   const bf16_t* __restrict__ bias, const bf16_t* __restrict__ resid, float sign,
                   LinShape s)
 {
-    __shared__ __attribute__((aligned(16))) bf16_t sa[2][BIG_BM * BIG_BK];
-    __shared__ __attribute__((aligned(16))) bf16_t sw[2][BIG_BN * BIG_BK];
+    // two buffers per operand as separate arrays, so that the compiler can tell
+    // the copy into one from the operand reads of the other
+    __shared__ __attribute__((aligned(1024))) bf16_t sa0[BIG_BM * BIG_BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t sa1[BIG_BM * BIG_BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t sw0[BIG_BN * BIG_BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t sw1[BIG_BN * BIG_BK];
 
     const int t = xcd_tile(blockIdx.x, s.per_xcd);
     if (t >= s.nmat * s.mt * s.nt) return;             // padding of the last XCD's run
@@ -51,9 +62,10 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
     const int m0 = tm * BIG_BM, n0 = tn * BIG_BN;
     const RowPos base{m0 / s.L, m0 % s.L};
 
-    // piece tid + 256 i: row 32 i + tid / 8, piece tid % 8
-    const int piece = tid % BIG_PIECES;
-    u32x4 ra[BIG_LOADS], rw[BIG_LOADS];
+    // LDS piece P = 256 i + tid of a step: row 32 i + tid / 8, slot tid % 8, which
+    // holds the row's k piece (tid % 8) ^ swz (lin_swz is an involution); one
+    // wave instruction copies 1 KiB of consecutive LDS (8 rows)
+    const int piece = (tid % BIG_PIECES) ^ (((tid / BIG_PIECES) >> 1) & 7);
     const int nk = s.K / BIG_BK;
     RowPos lrow[BIG_LOADS];
     int lm[BIG_LOADS], ln[BIG_LOADS];
@@ -64,21 +76,30 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
         ln[i] = min(n0 + row, s.N - 1);
         lrow[i] = row_pos(base, lm[i] - m0, s.L);
     }
-    auto load = [&](int kt) {
-        const int k = min(kt, nk - 1) * BIG_BK + 8 * piece;
+    // this thread's source rows as byte offsets (32-bit: operands under 4 GiB)
+    // from a per-step base that only the step moves
+    uint32_t aoff[BIG_LOADS], woff[BIG_LOADS];
+#pragma unroll
+    for (int i = 0; i < BIG_LOADS; ++i) {
+        if constexpr (IN == IN_ROWS) aoff[i] = (uint32_t)((long)lm[i] * s.K * 2) + 16 * piece;
+        else aoff[i] = (uint32_t)(((long)lrow[i].b * s.H * s.L + lrow[i].i) * D * 2) + 16 * piece;
+        woff[i] = (uint32_t)((long)ln[i] * s.K * 2) + 16 * piece;
+    }
+    // global -> LDS copy of step kt (past the last step: the last again, never read)
+    auto copy = [&](int kt, bf16_t* da, bf16_t* dw) __attribute__((always_inline)) {
+        const int k0 = min(kt, nk - 1) * BIG_BK;
+        long ka;
+        if constexpr (IN == IN_ROWS) ka = k0;
+        else ka = (long)(k0 / D) * s.L * D + k0 % D;
+        const char* xa = reinterpret_cast<const char*>(x + ka);
+        const char* xw = reinterpret_cast<const char*>(w + k0);
 #pragma unroll
         for (int i = 0; i < BIG_LOADS; ++i) {
-            ra[i] = *reinterpret_cast<const u32x4*>(in_ptr<IN, D>(x, s, lm[i], lrow[i], k));
-            rw[i] = *reinterpret_cast<const u32x4*>(w + (long)ln[i] * s.K + k);
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < BIG_LOADS; ++i) {
-            const int row = 32 * i + tid / BIG_PIECES;
-            const int off = row * BIG_BK + 8 * lin_swz(row, piece);
-            *reinterpret_cast<u32x4*>(&sa[buf][off]) = ra[i];
-            *reinterpret_cast<u32x4*>(&sw[buf][off]) = rw[i];
+            const int off = (i * BIG_THREADS + wave * 64) * 8;      // elements
+            __builtin_amdgcn_global_load_lds(xa + aoff[i],
+                                             (__attribute__((address_space(3))) void*)(da + off), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(xw + woff[i],
+                                             (__attribute__((address_space(3))) void*)(dw + off), 16, 0, 0);
         }
     };
 
@@ -90,24 +111,27 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-    auto read_frags = [&](int buf, int ks, bf16x8 (&ra_)[4], bf16x8 (&rw_)[4]) {
-        const int pc = 2 * ks + kh;                    // k = 16 ks + 8 kh .. +8
+    // operand reads: rows 128 wm + 32 u + r32 (128 wn + ..), piece 2 ks + kh at
+    // slot (2 ks + kh) ^ ((r32 / 2) % 8), as 32 u rows do not change the swizzle:
+    // a per-lane offset per ks plus a constant per u
+    int roff[BIG_BK / 16];
+#pragma unroll
+    for (int ks = 0; ks < BIG_BK / 16; ++ks) roff[ks] = r32 * BIG_BK + 8 * lin_swz(r32, 2 * ks + kh);
+    auto read_frags = [&](const bf16_t* ba, const bf16_t* bw, int ks, bf16x8 (&ra_)[4], bf16x8 (&rw_)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int ar = 128 * wm + 32 * u + r32, wr = 128 * wn + 32 * u + r32;
-            ra_[u] = *reinterpret_cast<const bf16x8*>(&sa[buf][ar * BIG_BK + 8 * lin_swz(ar, pc)]);
-            rw_[u] = *reinterpret_cast<const bf16x8*>(&sw[buf][wr * BIG_BK + 8 * lin_swz(wr, pc)]);
+            ra_[u] = *reinterpret_cast<const bf16x8*>(&ba[(128 * wm + 32 * u) * BIG_BK + roff[ks]]);
+            rw_[u] = *reinterpret_cast<const bf16x8*>(&bw[(128 * wn + 32 * u) * BIG_BK + roff[ks]]);
         }
     };
     // One LDS read after each MFMA: the fragments of sub-step ks+1 arrive while
-    // sub-step ks multiplies (left alone, the compiler waits for each sub-step's
-    // reads before its first MFMA).
-    auto multiply = [&](int buf) {
+    // sub-step ks multiplies.
+    auto multiply = [&](const bf16_t* ba, const bf16_t* bw) __attribute__((always_inline)) {
         bf16x8 fa[2][4], fw[2][4];
-        read_frags(buf, 0, fa[0], fw[0]);
+        read_frags(ba, bw, 0, fa[0], fw[0]);
 #pragma unroll
         for (int ks = 0; ks < BIG_BK / 16; ++ks) {
-            if (ks + 1 < BIG_BK / 16) read_frags(buf, ks + 1, fa[(ks + 1) & 1], fw[(ks + 1) & 1]);
+            if (ks + 1 < BIG_BK / 16) read_frags(ba, bw, ks + 1, fa[(ks + 1) & 1], fw[(ks + 1) & 1]);
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -128,17 +152,23 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     };
 
-    load(0);
-    store(0);
+    // Step kt is multiplied from buffer kt % 2 while step kt + 1 is being copied
+    // into the other; after the barrier that ends step kt (every wave done with
+    // its buffer, step kt + 1 landed) the copy of step kt + 2 starts there.
+    copy(0, sa0, sw0);
+    copy(1, sa1, sw1);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * BIG_LOADS) : "memory");   // step 0 landed
     __syncthreads();
-    load(1);
     for (int kt = 0; kt < nk; ++kt) {
-        multiply(kt & 1);
-        store((kt + 1) & 1);           // step kt+1 (a repeat past the end, never read)
+        bf16_t* ba = (kt & 1) ? sa1 : sa0;
+        bf16_t* bw = (kt & 1) ? sw1 : sw0;
+        multiply(ba, bw);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                  // step kt + 1 landed
         __syncthreads();
-        load(kt + 2);
+        copy(kt + 2, ba, bw);
         __builtin_amdgcn_sched_barrier(0);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the workgroup
 
     // D element j of tile (a, b): column n = 32b + 8(j/4) + 4 kh + (j%4), row m = 32a + r32
 #pragma unroll

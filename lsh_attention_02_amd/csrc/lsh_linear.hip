@@ -193,15 +193,17 @@ void k_linear(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
 
 // Launches with at least one 256 x 256 tile per CU take the larger tiles
 // (half the LDS and L2 traffic per MFMA); smaller ones keep 128 x 128 tiles
-// to fill the chip.
+// to fill the chip.  The larger tiles address their operands with 32-bit byte
+// offsets, so x and w must each stay under 4 GiB there.
 constexpr long BIG_MIN_TILES = 256;
+constexpr long BIG_MAX_BYTES = 1L << 32;
 
 template <int IN, int OUT, int D, int EPI>
 hipError_t launch(const void* x, const void* w0, const void* w1, void* y0, void* y1, int nmat,
                   LinShape s, const void* bias, const void* resid, float sign, hipStream_t st)
 {
     const long big = (long)nmat * ((s.M + 255) / 256) * ((s.N + 255) / 256);
-    if (big >= BIG_MIN_TILES)
+    if (big >= BIG_MIN_TILES && (long)s.M * s.K * 2 < BIG_MAX_BYTES && (long)s.N * s.K * 2 < BIG_MAX_BYTES)
         return launch_big<IN, OUT, D, EPI>(x, w0, w1, y0, y1, nmat, s, bias, resid, sign, st);
     s.mt = (s.M + LIN_BM - 1) / LIN_BM;
     s.nt = (s.N + LIN_BN - 1) / LIN_BN;
