@@ -224,7 +224,6 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     constexpr int VROWB = S::VROWB;
     constexpr int CT = C / 16, NKT = 2 * CT, DT = D / 16;
     constexpr int VE = 16 / (int)sizeof(T), VPR = D / VE;
-    constexpr int EB = (int)sizeof(T);
     // score tiles per scheduling region: two accumulation chains at a time where
     // the registers allow it
     constexpr int SGRP = sizeof(T) == 2 && C <= 64 ? 2 : 1;
