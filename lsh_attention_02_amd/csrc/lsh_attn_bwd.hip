@@ -175,7 +175,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
         for (int x = 0; x < VE; ++x) {
             const int xe = x ^ (piece & 1);            // element order x ^ 1 on odd pieces
             const int d = piece * VE + xe;
-            char* dst = base + d * TROWB + vt_group_off<C>(rg, d);
+            char* dst = base + d * TROWB + vt_group_off<C, D>(rg, d);
             const uint32_t sel = 0x05040100u + 0x02020202u * (uint32_t)(xe & 1);
             const uint32_t w0 = __builtin_amdgcn_perm(reg[1][x >> 1], reg[0][x >> 1], sel);
             const uint32_t w1 = __builtin_amdgcn_perm(reg[3][x >> 1], reg[2][x >> 1], sel);
@@ -391,7 +391,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                     for (int dt = 0; dt < DT; ++dt) {
                         const int d = dt * 16 + r16;
                         const char* kr = sm.kt[slk] + d * TROWB;
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + vt_group_off<C>(kg, d));
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + vt_group_off<C, D>(kg, d));
                         o[dt] = M::mma(a, b, o[dt]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -443,7 +443,7 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         const int d = dt * 16 + r16;
-                        const int go = vt_group_off<C>(qg, d);   // groups qg and qg + 4: one pair
+                        const int go = vt_group_off<C, D>(qg, d);   // groups qg and qg + 4: one pair
                         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sm.kt[sl] + d * TROWB + go);
                         const bf16x8 ad = *reinterpret_cast<const bf16x8*>(sm.dot + d * TROWB + go);
 #pragma unroll

@@ -142,7 +142,9 @@ __device__ __forceinline__ uint32_t rounds_outside8(const uint32_t (&q1)[NDW], c
 // 16-bit elements: groups kg and kg + 4 (kg with bit 2 clear) form one 16-byte
 // pair: the two groups that one PV operand combines (keys 4g.. of tiles t0 and
 // t0 + 1), so the operand is a single 16-byte read.  Pair p of row d sits at
-// p ^ vt_pair_swz(d) = p ^ f(d % 16) ^ 5 (d / 16), f(r) = r (r / 2 at chunk 32).
+// p ^ vt_pair_swz(d) = p ^ f(d % 16) ^ 5 (d / 16), f(r) = r (r / 2 at chunk 32;
+// no d / 16 term at chunk 128 with d 128, where its per-dt addresses made the
+// compiler spill).
 // A 16-byte read is served in passes of 16 lanes (the lane quads of even, then
 // odd, bit parity in each half-wave); each pass of the operand reads of rows
 // 16 dt + r16 covers the 64 banks once (checked exhaustively, and measured:
@@ -155,19 +157,20 @@ __device__ __forceinline__ int vt_swz(int d)
     return (d ^ (d >> 3)) & (C / 4 - 1);
 }
 
-template <int C>
+template <int C, int D>
 __device__ __forceinline__ int vt_pair_swz(int d)
 {
     const int r16 = d & 15;
-    return ((C == 32 ? r16 >> 1 : r16) ^ (5 * (d >> 4))) & (C / 8 - 1);
+    constexpr bool MIX = !(C == 128 && D == 128);
+    return ((C == 32 ? r16 >> 1 : r16) ^ (MIX ? 5 * (d >> 4) : 0)) & (C / 8 - 1);
 }
 
 // byte offset of 4-key group kg within a 16-bit V^T row d
-template <int C>
+template <int C, int D>
 __device__ __forceinline__ int vt_group_off(int kg, int d)
 {
     const int pair = (kg & 3) | ((kg >> 3) << 2);
-    return 16 * (pair ^ vt_pair_swz<C>(d)) + 8 * ((kg >> 2) & 1);
+    return 16 * (pair ^ vt_pair_swz<C, D>(d)) + 8 * ((kg >> 2) & 1);
 }
 
 // qk rows in LDS.  A 16-byte LDS access is served in four passes of 16 lanes;
@@ -189,6 +192,15 @@ struct KLayout {
         else return r * ROW + e;
     }
 };
+
+// Register sets for the gathered rows: with two, the rows of the next two
+// chunks are in flight while one is computed (measured 1-2% faster at d 128,
+// chunk 64).  Elsewhere the second set would cost a wave per SIMD.
+template <typename T, int D, int C, int NDW, bool SAME>
+constexpr int gather_sets()
+{
+    return sizeof(T) == 2 && D == 128 && C == 64 && NDW <= 4 && !SAME ? 2 : 1;
+}
 
 template <typename T, int D, int C, int NDW>
 struct Lds {
@@ -271,53 +283,57 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     // position (and its window id in the same-bucket variant).
     constexpr int MJOBS = C * NW;
     constexpr int MJPT = (MJOBS + NTH - 1) / NTH;
-    int gpos[JPT][4];          // raw perm entries of this thread's gather rows, next chunk to load
-    int mpos[MJPT];            // raw perm entries of this thread's per-row jobs, next chunk to load
-    u32x4 kreg[JPT][4], vreg[JPT][4];
-    int rpos[MJPT];            // clamped positions of the per-row jobs' rows, chunk in registers
-    uint32_t clo[MJPT], chi[MJPT];   // raw chunk ids of rounds 2w and 2w+1, chunk in registers
-    uint32_t ridraw[MJPT];     // same-bucket variant: the row's window id in this round
+    constexpr int NSET = gather_sets<T, D, C, NDW, SAME>();
+    int gpos[NSET][JPT][4];    // raw perm entries of this thread's gather rows, per register set
+    int mpos[NSET][MJPT];      // raw perm entries of this thread's per-row jobs
+    u32x4 kreg[NSET][JPT][4], vreg[NSET][JPT][4];
+    int rpos[NSET][MJPT];      // clamped positions of the per-row jobs' rows
+    uint32_t clo[NSET][MJPT], chi[NSET][MJPT];   // raw chunk ids of rounds 2w and 2w+1
+    uint32_t ridraw[NSET][MJPT];   // same-bucket variant: the row's window id in this round
 
-    auto fetch_positions = [&](int kk) {
+    auto fetch_positions = [&](int kk, auto set) __attribute__((always_inline)) {
+        constexpr int P = decltype(set)::value;
 #pragma unroll
         for (int jb = 0; jb < JPT; ++jb) {
             const int job = tid + jb * NTH;
             const int rg = (job < JOBS ? job : 0) / VPR;
             const int4 p4 = *reinterpret_cast<const int4*>(pr + kk * C + 4 * rg);
-            gpos[jb][0] = p4.x; gpos[jb][1] = p4.y; gpos[jb][2] = p4.z; gpos[jb][3] = p4.w;
+            gpos[P][jb][0] = p4.x; gpos[P][jb][1] = p4.y; gpos[P][jb][2] = p4.z; gpos[P][jb][3] = p4.w;
         }
 #pragma unroll
         for (int mj = 0; mj < MJPT; ++mj) {
             const int m = (tid + mj * NTH) % MJOBS;     // jobs past the end repeat (no branches)
-            mpos[mj] = pr[kk * C + m / NW];
+            mpos[P][mj] = pr[kk * C + m / NW];
         }
     };
-    auto fetch_rows = [&]() {
+    auto fetch_rows = [&](auto set) __attribute__((always_inline)) {
+        constexpr int P = decltype(set)::value;
 #pragma unroll
         for (int jb = 0; jb < JPT; ++jb) {
             const int job = tid + jb * NTH;
             const int piece = (job < JOBS ? job : 0) % VPR;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const long row = (long)clamp_pos(gpos[jb][i]) * D + piece * VE;
-                kreg[jb][i] = *reinterpret_cast<const u32x4*>(qb + row);
-                vreg[jb][i] = *reinterpret_cast<const u32x4*>(vb + row);
+                const long row = (long)clamp_pos(gpos[P][jb][i]) * D + piece * VE;
+                kreg[P][jb][i] = *reinterpret_cast<const u32x4*>(qb + row);
+                vreg[P][jb][i] = *reinterpret_cast<const u32x4*>(vb + row);
             }
         }
 #pragma unroll
         for (int mj = 0; mj < MJPT; ++mj) {
             const int m = (tid + mj * NTH) % MJOBS;
-            rpos[mj] = clamp_pos(mpos[mj]);
-            const int16_t* cr = cb + (long)rpos[mj] * n_r;
+            rpos[P][mj] = clamp_pos(mpos[P][mj]);
+            const int16_t* cr = cb + (long)rpos[P][mj] * n_r;
             if constexpr (NDW > 0) {
                 const int w = m % NW;
-                clo[mj] = (uint16_t)cr[min(2 * w, n_r - 1)];
-                chi[mj] = (uint16_t)cr[min(2 * w + 1, n_r - 1)];
+                clo[P][mj] = (uint16_t)cr[min(2 * w, n_r - 1)];
+                chi[P][mj] = (uint16_t)cr[min(2 * w + 1, n_r - 1)];
             }
-            if constexpr (SAME) ridraw[mj] = (uint16_t)cr[r];
+            if constexpr (SAME) ridraw[P][mj] = (uint16_t)cr[r];
         }
     };
-    auto store_rows = [&](int sl) {
+    auto store_rows = [&](int sl, auto set) __attribute__((always_inline)) {
+        constexpr int P = decltype(set)::value;
 #pragma unroll
         for (int jb = 0; jb < JPT; ++jb) {
             const int job = tid + jb * NTH;
@@ -325,7 +341,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 const int rg = job / VPR, piece = job % VPR;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<u32x4*>(&sm.k[sl][KL::off(4 * rg + i, piece * VE)]) = kreg[jb][i];
+                    *reinterpret_cast<u32x4*>(&sm.k[sl][KL::off(4 * rg + i, piece * VE)]) = kreg[P][jb][i];
                 // transpose the 4 rows x VE elements: element x of every row gives
                 // the 4 keys 4rg..4rg+3 of v^T row d = piece*VE + x
 #pragma unroll
@@ -333,15 +349,15 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                     if constexpr (sizeof(T) == 2) {
                         const int xe = x ^ (piece & 1);        // element order x ^ 1 on odd pieces
                         const int d = piece * VE + xe;
-                        char* dst = sm.vt[sl] + d * VROWB + vt_group_off<C>(rg, d);
+                        char* dst = sm.vt[sl] + d * VROWB + vt_group_off<C, D>(rg, d);
                         const uint32_t sel = 0x05040100u + 0x02020202u * (uint32_t)(xe & 1);
-                        const uint32_t w0 = __builtin_amdgcn_perm(vreg[jb][1][x >> 1], vreg[jb][0][x >> 1], sel);
-                        const uint32_t w1 = __builtin_amdgcn_perm(vreg[jb][3][x >> 1], vreg[jb][2][x >> 1], sel);
+                        const uint32_t w0 = __builtin_amdgcn_perm(vreg[P][jb][1][x >> 1], vreg[P][jb][0][x >> 1], sel);
+                        const uint32_t w1 = __builtin_amdgcn_perm(vreg[P][jb][3][x >> 1], vreg[P][jb][2][x >> 1], sel);
                         *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
                     } else {
                         const int d = piece * VE + x;
                         char* dst = sm.vt[sl] + d * VROWB + 16 * (rg ^ vt_swz<C>(d));
-                        const u32x4 w4 = {vreg[jb][0][x], vreg[jb][1][x], vreg[jb][2][x], vreg[jb][3][x]};
+                        const u32x4 w4 = {vreg[P][jb][0][x], vreg[P][jb][1][x], vreg[P][jb][2][x], vreg[P][jb][3][x]};
                         *reinterpret_cast<u32x4*>(dst) = w4;
                     }
                 }
@@ -353,13 +369,13 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             if (m < MJOBS) {
                 const int row = m / NW, w = m % NW;
                 if (w == 0) {
-                    sm.pos[sl][row] = rpos[mj];
-                    if constexpr (SAME) sm.rid[sl][row] = (int)ridraw[mj];
+                    sm.pos[sl][row] = rpos[P][mj];
+                    if constexpr (SAME) sm.rid[sl][row] = (int)ridraw[P][mj];
                 }
                 // rounds past n_r hold 0 for keys and queries alike (always inside)
                 if constexpr (NDW > 0) {
-                    const uint32_t lo = 2 * w < n_r ? clo[mj] : 0u;
-                    const uint32_t hi = 2 * w + 1 < n_r ? chi[mj] : 0u;
+                    const uint32_t lo = 2 * w < n_r ? clo[P][mj] : 0u;
+                    const uint32_t hi = 2 * w + 1 < n_r ? chi[P][mj] : 0u;
                     sm.cid[sl][row * NDW + w] = lo | (hi << 16);
                 }
             }
@@ -487,7 +503,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                         const int d = dt * 16 + r16;
                         // groups kg (tile t0) and kg + 4 (tile t0 + 1): one pair
                         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            sm.vt[slk] + d * VROWB + vt_group_off<C>(key0 >> 2, d));
+                            sm.vt[slk] + d * VROWB + vt_group_off<C, D>(key0 >> 2, d));
                         o[dt] = M::mma(a, b, o[dt]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -536,18 +552,37 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     // of chunk it+2, compute chunk it.  The scheduling barriers in compute keep
     // the compiler from hoisting a whole phase's LDS reads at once, which would
     // raise the registers past two waves per SIMD.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, NSET - 1>;
     auto step = [&](int it, auto slot) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot)::value;
-        store_rows(SL);                // slot of iteration it-2, released by the last barrier
+        using PS = std::integral_constant<int, NSET == 2 ? SL : 0>;
+        using QS = std::integral_constant<int, NSET == 2 ? 1 - SL : 0>;
+        store_rows(SL, PS{});          // slot of iteration it-2, released by the last barrier
         __syncthreads();
-        fetch_rows();                  // chunk it+1 (positions fetched an iteration ago)
-        fetch_positions(chunk_of(it + 2));
+        if constexpr (NSET == 2) {
+            // positions of chunk it+3 before the rows of chunk it+2, so that
+            // waiting for them never waits for those rows
+            fetch_positions(chunk_of(it + 3), QS{});
+            fetch_rows(PS{});
+        } else {
+            fetch_rows(PS{});          // chunk it+1 (positions fetched an iteration ago)
+            fetch_positions(chunk_of(it + 2), PS{});
+        }
         if (it >= it0) compute(it, SL, 1 - SL);
         __syncthreads();
     };
-    fetch_positions(chunk_of(0));
-    fetch_rows();
-    fetch_positions(chunk_of(1));
+    if constexpr (NSET == 2) {
+        fetch_positions(chunk_of(0), S0{});
+        fetch_positions(chunk_of(1), S1{});
+        fetch_rows(S0{});
+        fetch_positions(chunk_of(2), S0{});
+        fetch_rows(S1{});
+    } else {
+        fetch_positions(chunk_of(0), S0{});
+        fetch_rows(S0{});
+        fetch_positions(chunk_of(1), S0{});
+    }
     for (int it = 0; it < nit; it += 2) {
         step(it, std::integral_constant<int, 0>{});
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});

@@ -37,6 +37,8 @@ SMALL = {
                                    n_rounds=3, seed=101),
     "d128_L2048_r4": W("d128", heads=2, seq_len=2048, d_head=128, n_buckets=64, n_rounds=4, seed=102),
     "chunk128_L2560": W("c128", heads=2, seq_len=2560, n_buckets=40, chunk=128, seed=103),
+    "chunk128_d128_L2048_r3": W("c128d128", heads=2, seq_len=2048, d_head=128, n_buckets=32,
+                                n_rounds=3, chunk=128, seed=113),
     "chunk32_noncausal_r5": W("c32", heads=2, seq_len=1056, n_buckets=16, n_rounds=5, chunk=32,
                               causal=False, seed=104),
     "f32_d128_r2_scale1": W("f32d128", seq_len=576, d_head=128, dtype="f32", n_buckets=16,
