@@ -14,8 +14,9 @@
 // Workgroup = C/16 waves; it walks a run of consecutive chunks of one
 // (b, h, r).  Each chunk's qk rows (row-major) and v rows (transposed) are
 // gathered once into LDS and kept for the next chunk, whose look-back window
-// they form.  The rows of chunk k+1 are loaded into registers while chunk k is
-// computed (positions two chunks ahead), so the gathers overlap the math.
+// they form.  The rows of chunk k+1 (and k+2 where a second register set
+// fits) are loaded into registers while chunk k is computed, so the gathers
+// overlap the math.
 // Wave w takes the 16 queries in rows 16w.. of the chunk (16x16 MFMA tiles,
 // so that four waves share one chunk's LDS tiles and each SIMD holds two waves):
 //   S^T[key, q] = K[key, :] · Q[q, :]     (A = key rows, B = query rows)
