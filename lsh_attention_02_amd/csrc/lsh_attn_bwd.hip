@@ -44,6 +44,8 @@ namespace {
 // bank conflicts (rows alternate between the 32-bank halves).
 __device__ __forceinline__ int pswz(int k) { return ((k >> 1) & 7) << 1; }
 
+constexpr int PREP_RPT = 4;                         // rows per thread in k_bwd_prep
+
 template <int D, int C, int NDW>
 struct BwdLds {
     static constexpr int KROW = KLayout<bf16_t, D>::ROW;
@@ -471,30 +473,46 @@ void k_bwd_prep(const bf16_t* __restrict__ o, const bf16_t* __restrict__ d_o,
                 const float* __restrict__ lse, float* __restrict__ lse_c,
                 float* __restrict__ delta, long rows, int L, int n_r)
 {
+    // TPR threads per row, 16 bytes of o and d_o each; PREP_RPT rows per thread
+    // (strided by the block's RPB rows), their loads all issued first
     constexpr int TPR = D / 8, RPB = 256 / TPR;
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
     const int part = threadIdx.x % TPR;
-    const bool ok = row < rows;
-    const long rr = ok ? row : rows - 1;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + rr * D + part * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(d_o + rr * D + part * 8);
-    float acc = 0.f;
+    const long row0 = (long)blockIdx.x * RPB * PREP_RPT + threadIdx.x / TPR;
+    u32x4 a[PREP_RPT], b[PREP_RPT];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        acc = fmaf(bf16_to_f32((uint16_t)(a[x] & 0xFFFFu)), bf16_to_f32((uint16_t)(b[x] & 0xFFFFu)), acc);
-        acc = fmaf(bf16_to_f32((uint16_t)(a[x] >> 16)), bf16_to_f32((uint16_t)(b[x] >> 16)), acc);
+    for (int k = 0; k < PREP_RPT; ++k) {
+        const long rr = min(row0 + (long)k * RPB, rows - 1);
+        a[k] = *reinterpret_cast<const u32x4*>(o + rr * D + part * 8);
+        b[k] = *reinterpret_cast<const u32x4*>(d_o + rr * D + part * 8);
     }
 #pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
-    if (ok && part == 0) {
+    for (int k = 0; k < PREP_RPT; ++k) {
+        const long row = row0 + (long)k * RPB;
+        const long rr = min(row, rows - 1);
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            acc = fmaf(bf16_to_f32((uint16_t)(a[k][x] & 0xFFFFu)), bf16_to_f32((uint16_t)(b[k][x] & 0xFFFFu)), acc);
+            acc = fmaf(bf16_to_f32((uint16_t)(a[k][x] >> 16)), bf16_to_f32((uint16_t)(b[k][x] >> 16)), acc);
+        }
+        // LSE over the rounds: the row's lanes take rounds part, part + TPR, ..
         const long bh = rr / L;
         const int i = (int)(rr % L);
         float m = -INFINITY;
-        for (int q = 0; q < n_r; ++q) m = fmaxf(m, lse[(bh * n_r + q) * (long)L + i]);
+        for (int q = part; q < n_r; q += TPR) m = fmaxf(m, lse[(bh * n_r + q) * (long)L + i]);
+#pragma unroll
+        for (int s = 1; s < TPR; s <<= 1) {
+            acc += __shfl_xor(acc, s);
+            m = fmaxf(m, __shfl_xor(m, s));
+        }
         float z = 0.f;
-        for (int q = 0; q < n_r; ++q) z += __expf(lse[(bh * n_r + q) * (long)L + i] - m);
-        lse_c[rr] = m + __logf(z);
-        delta[rr] = acc;
+        for (int q = part; q < n_r; q += TPR) z += __expf(lse[(bh * n_r + q) * (long)L + i] - m);
+#pragma unroll
+        for (int s = 1; s < TPR; s <<= 1) z += __shfl_xor(z, s);
+        if (row < rows && part == 0) {
+            lse_c[row] = m + __logf(z);
+            delta[row] = acc;
+        }
     }
 }
 
@@ -565,9 +583,10 @@ template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s)
 {
     const long rows = a.bh * a.L;
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (D / 8);               // rows per 256-thread block
     const unsigned blocks = (unsigned)((rows + RPB - 1) / RPB);
-    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(blocks), dim3(256), 0, s,
+    const unsigned pblocks = (unsigned)((rows + RPB * PREP_RPT - 1) / (RPB * PREP_RPT));
+    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(pblocks), dim3(256), 0, s,
                        static_cast<const bf16_t*>(a.o), static_cast<const bf16_t*>(a.d_o), a.lse,
                        a.lse_c, a.delta, rows, a.L, a.n_r);
     hipError_t e = hipGetLastError();
