@@ -11,7 +11,9 @@
 //
 // R streams through LDS in groups of columns; the groups of all rounds form
 // one sequence, and the next group is loaded while the current one feeds the
-// MFMAs (two LDS buffers, one barrier per group).  Two kernels:
+// MFMAs (two LDS buffers, one barrier per group).  At d 128 the column tiles
+// are software-pipelined: each tile's argmax scan runs under the next tile's
+// MFMAs.  Two kernels:
 //   k_hash_tr (bf16, rows of R 16-byte aligned): the group is copied from
 //     global memory straight into LDS in R's own [d][column] layout, and the
 //     MFMA operands are read with the transposing LDS load;
@@ -28,6 +30,7 @@
 #include "lsh_internal.h"
 
 #include <climits>
+
 
 namespace lshk {
 namespace {
@@ -290,7 +293,9 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
 // per SIMD), of 4 waves at d 64, where three waves per SIMD fit: three
 // independent workgroups per CU, whose barriers do not hold each other up.
 template <int D> constexpr int tr_waves() { return D == 64 ? 4 : 8; }
+template <int D> constexpr bool hash_pipe() { return D == 128; }
 constexpr int TR_COLS = 128;                     // R columns staged per step
+constexpr int TR_PPR = TR_COLS / 8;              // 16-byte pieces per staged row
 constexpr int TR_TILES = TR_COLS / 32;
 constexpr int TR_ROWB = TR_COLS * 2;             // bytes per staged row
 
@@ -316,13 +321,13 @@ template <int D>
 __device__ __forceinline__ void tr_stage(const bf16_t* __restrict__ Rr, int c0, int ncol, char* buf)
 {
     constexpr int NTH = tr_waves<D>() * 64;
-    constexpr int ITERS = D * 16 / NTH;
+    constexpr int ITERS = D * TR_PPR / NTH;
     const int tid = threadIdx.x, wave = tid >> 6;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) {
         const int P = i * NTH + tid;
-        const int d = P >> 4;
-        const int col = min(c0 + 8 * tr_piece(P & 15, d), ncol - 8);
+        const int d = P / TR_PPR;
+        const int col = min(c0 + 8 * tr_piece(P % TR_PPR, d), ncol - 8);
         __builtin_amdgcn_global_load_lds(Rr + (long)d * ncol + col,
                                          (__attribute__((address_space(3))) void*)(buf + 16 * (i * NTH + wave * 64)),
                                          16, 0, 0);
@@ -334,9 +339,9 @@ __device__ __forceinline__ void tr_zero_tail(int c0, int ncol, char* buf)
 {
     constexpr int NTH = tr_waves<D>() * 64;
 #pragma unroll
-    for (int i = 0; i < D * 16 / NTH; ++i) {
+    for (int i = 0; i < D * TR_PPR / NTH; ++i) {
         const int P = i * NTH + threadIdx.x;
-        if (c0 + 8 * tr_piece(P & 15, P >> 4) >= ncol)
+        if (c0 + 8 * tr_piece(P % TR_PPR, P / TR_PPR) >= ncol)
             *reinterpret_cast<u32x4*>(buf + 16 * P) = u32x4{0u, 0u, 0u, 0u};
     }
 }
@@ -398,74 +403,141 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         __syncthreads();
     }
 
-    // one group: the next group's R goes into the other buffer while this one
-    // feeds the MFMAs
+    auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) { bmag[u] = 0.f; btile[u] = -1; keep[u] = f32x16{}; }
+    };
+    // one column tile's projections (16 per lane and token tile) against the
+    // round's record: the largest |p| so far, its tile, and that tile's values
+    auto scan = [&](const f32x16 (&ac)[HASH_NT], int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) {
+            float m = fabsf(ac[u][0]);
+#pragma unroll
+            for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(ac[u][j]));
+            const bool up = m > bmag[u];
+            bmag[u] = up ? m : bmag[u];
+            btile[u] = up ? tile : btile[u];
+            keep[u] = up ? ac[u] : keep[u];
+        }
+    };
+    // end of round r: first kept entry with the record magnitude (one always
+    // matches), then the better of the two lanes that hold the token
+    auto resolve = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) {
+            int jj = 0;
+            float bv = 0.f;
+#pragma unroll
+            for (int j = 15; j >= 0; --j) {
+                const bool hit = fabsf(keep[u][j]) == bmag[u];
+                jj = hit ? j : jj;
+                bv = hit ? keep[u][j] : bv;
+            }
+            int bi = btile[u] < 0 ? INT_MAX : 32 * btile[u] + 4 * hh + 8 * (jj >> 2) + (jj & 3);
+            if (btile[u] < 0) bv = 0.f;
+            const float ov = __shfl_xor(bv, 32);
+            const int oi = __shfl_xor(bi, 32);
+            if (fabsf(ov) > fabsf(bv) || (fabsf(ov) == fabsf(bv) && oi < bi)) { bv = ov; bi = oi; }
+            if (bi == INT_MAX) bi = 0;
+            const int tok = tok0 + 32 * u + n;
+            if (hh == 0 && tok < L)
+                buckets[((long)bh * n_r + r) * L + tok] = bi + (bv < 0.f ? ncol : 0);
+        }
+    };
+
+    // PIPE (d 128): software pipeline over column tiles.  The MFMAs of tile t
+    // go into accumulator set t % 2 while the scan of tile t - 1 reads the
+    // other set, about three VALU instructions per MFMA, and the operands of
+    // tile t + 1 are read into the operand registers that each MFMA pair
+    // frees.  A wave's own scan and LDS reads thus run under its matrix
+    // instructions instead of waiting for the other wave of its SIMD (the
+    // group barriers keep the two in phase).  The last tile of a group is
+    // scanned under the first tile of the next group, and a round is resolved
+    // after the scan of its last tile.  All four tiles of a group are
+    // computed: staged columns past ncol hold zeros, whose projections are
+    // exactly 0 and never beat a record.  At d 64 the second accumulator set
+    // would cost the third wave per SIMD, so each tile is scanned right after
+    // its own MFMAs.
+    constexpr bool PIPE = hash_pipe<D>();
+    f32x16 acc[PIPE ? 2 : 1][HASH_NT];
+    if constexpr (PIPE) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) acc[1][u] = f32x16{};
+    }
+    reset();
+    int ptile = 0, pr = 0;                 // previous group's last tile and round (PIPE)
+    bool pend = false;                     // previous group ended its round (PIPE)
+
     auto group = [&](int g, const char* buf, char* nbuf) __attribute__((always_inline)) {
         int r, c0;
         group_rc(g, r, c0);
-        if (c0 == 0) {
-#pragma unroll
-            for (int u = 0; u < HASH_NT; ++u) { bmag[u] = 0.f; btile[u] = -1; keep[u] = f32x16{}; }
-        }
         int r1, c1;
         group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
         tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
-        // staged columns past ncol hold zeros, so their projections are exactly
-        // 0 and can never beat a record: no column test is needed
-        const int tiles = min(TR_TILES, (ncol - c0 + 31) >> 5);
+        const int tbase = c0 >> 5;
+        if constexpr (!PIPE) {
+            if (c0 == 0) reset();
+        }
+        const int tiles = PIPE ? TR_TILES : min(TR_TILES, (ncol - c0 + 31) >> 5);
+        typename M::Frag a[NKS];
+        auto read_tile = [&](int ct, int ks) __attribute__((always_inline)) {
+            const char* p = buf + toff[ct] + 16 * ks * TR_ROWB;
+            a[ks] = __builtin_shufflevector(tr_read(p), tr_read(p + 4 * TR_ROWB),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+        };
 #pragma unroll
         for (int ct = 0; ct < TR_TILES; ++ct) {
             if (ct < tiles) {
-                f32x16 acc[HASH_NT];
+                // operands: all at once, or (PIPE) for tile 0 only, the
+                // others being read under the previous tile's MFMAs
+                if (!PIPE || ct == 0) {
 #pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) acc[u] = f32x16{};
-                typename M::Frag a[NKS];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const char* p = buf + toff[ct] + 16 * ks * TR_ROWB;
-                    a[ks] = __builtin_shufflevector(tr_read(p), tr_read(p + 4 * TR_ROWB),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
+                    for (int ks = 0; ks < NKS; ++ks) read_tile(ct, ks);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                f32x16 (&ac)[HASH_NT] = acc[PIPE ? ct & 1 : 0];
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) ac[u] = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-                    for (int u = 0; u < HASH_NT; ++u) acc[u] = M::mma(a[ks], bq[u][ks], acc[u]);
+                    for (int u = 0; u < HASH_NT; ++u) ac[u] = M::mma(a[ks], bq[u][ks], ac[u]);
+                    if (PIPE && ct + 1 < TR_TILES) read_tile(ct + 1, ks);   // into a[ks], now free
                 }
-                const int tile = (c0 >> 5) + ct;
+                if constexpr (PIPE) {
+                    scan(acc[(ct + 1) & 1], ct == 0 ? ptile : tbase + ct - 1);
+                    // an IR-level scheduler would otherwise sink the scans of
+                    // a group below all of its MFMAs
 #pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) {
-                    float m = fabsf(acc[u][0]);
+                    for (int u = 0; u < HASH_NT; ++u)
+                        asm volatile("" :: "v"(bmag[u]), "v"(btile[u]), "v"(keep[u]));
 #pragma unroll
-                    for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(acc[u][j]));
-                    const bool up = m > bmag[u];
-                    bmag[u] = up ? m : bmag[u];
-                    btile[u] = up ? tile : btile[u];
-                    keep[u] = up ? acc[u] : keep[u];
+                    for (int i = 0; i < NKS; ++i) {
+#pragma unroll
+                        for (int u = 0; u < HASH_NT; ++u) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU
+                        }
+                        if (ct + 1 < TR_TILES)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (ct == 0) {
+                        if (pend) resolve(pr);
+                        if (c0 == 0) reset();
+                    }
+                } else {
+                    scan(ac, tbase + ct);
                 }
             }
         }
-        if (c0 + TR_COLS >= ncol) {                  // last group of round r
-#pragma unroll
-            for (int u = 0; u < HASH_NT; ++u) {
-                int jj = 0;
-                float bv = 0.f;
-#pragma unroll
-                for (int j = 15; j >= 0; --j) {
-                    const bool hit = fabsf(keep[u][j]) == bmag[u];
-                    jj = hit ? j : jj;
-                    bv = hit ? keep[u][j] : bv;
-                }
-                int bi = btile[u] < 0 ? INT_MAX : 32 * btile[u] + 4 * hh + 8 * (jj >> 2) + (jj & 3);
-                if (btile[u] < 0) bv = 0.f;
-                const float ov = __shfl_xor(bv, 32);
-                const int oi = __shfl_xor(bi, 32);
-                if (fabsf(ov) > fabsf(bv) || (fabsf(ov) == fabsf(bv) && oi < bi)) { bv = ov; bi = oi; }
-                if (bi == INT_MAX) bi = 0;
-                const int tok = tok0 + 32 * u + n;
-                if (hh == 0 && tok < L)
-                    buckets[((long)bh * n_r + r) * L + tok] = bi + (bv < 0.f ? ncol : 0);
-            }
+        if constexpr (PIPE) {
+            ptile = tbase + TR_TILES - 1;
+            pr = r;
+            pend = c0 + TR_COLS >= ncol;
+        } else {
+            if (c0 + TR_COLS >= ncol) resolve(r);    // last group of round r
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next group has landed
         if (g + 1 < ngroups && c1 + TR_COLS > ncol) tr_zero_tail<D>(c1, ncol, nbuf);
@@ -474,6 +546,10 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
     for (int g = 0; g < ngroups; g += 2) {
         group(g, rt0, rt1);
         if (g + 1 < ngroups) group(g + 1, rt1, rt0);
+    }
+    if constexpr (PIPE) {
+        scan(acc[1], ptile);
+        resolve(pr);
     }
 }
 
