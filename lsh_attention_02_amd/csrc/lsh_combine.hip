@@ -14,7 +14,10 @@ namespace {
 constexpr int COMB_THREADS = 256;
 constexpr int MAX_ROUNDS = 16;
 
-template <typename T, int D>
+// NR: n_r rounded up to a power of two; rounds n_r .. NR-1 repeat round n_r - 1
+// (a valid address) and are not used, so that every load of the thread is
+// issued before the first one is waited for.
+template <typename T, int D, int NR>
 __global__ __launch_bounds__(COMB_THREADS)
 void k_combine(const T* __restrict__ o_rounds, const float* __restrict__ lse, T* __restrict__ o,
                long rows, int L, int n_r)
@@ -27,28 +30,29 @@ void k_combine(const T* __restrict__ o_rounds, const float* __restrict__ lse, T*
     if (row >= rows) return;
     const long bh = row / L;
     const int i = (int)(row % L);
-
-    float l[MAX_ROUNDS];
+    float l[NR];
+    u32x4 raw[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const long rr = bh * n_r + min(r, n_r - 1);
+        l[r] = lse[rr * L + i];
+        raw[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(o_rounds + (rr * L + i) * D + part * VE));
+    }
     float m = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < MAX_ROUNDS; ++r) {
-        if (r < n_r) {
-            l[r] = lse[(bh * n_r + r) * (long)L + i];
-            m = fmaxf(m, l[r]);
-        }
-    }
+    for (int r = 0; r < NR; ++r)
+        if (r < n_r) m = fmaxf(m, l[r]);
     float acc[VE];
 #pragma unroll
     for (int x = 0; x < VE; ++x) acc[x] = 0.f;
     float wsum = 0.f;
 #pragma unroll
-    for (int r = 0; r < MAX_ROUNDS; ++r) {
+    for (int r = 0; r < NR; ++r) {
         if (r < n_r) {
             const float w = __expf(l[r] - m);
             wsum += w;
-            const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                o_rounds + ((bh * n_r + r) * (long)L + i) * D + part * VE));
-            const T* e = reinterpret_cast<const T*>(&raw);
+            const T* e = reinterpret_cast<const T*>(&raw[r]);
 #pragma unroll
             for (int x = 0; x < VE; ++x) acc[x] += w * to_f32(e[x]);
         }
@@ -61,16 +65,27 @@ void k_combine(const T* __restrict__ o_rounds, const float* __restrict__ lse, T*
     __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(o + row * D + part * VE));
 }
 
-template <typename T, int D>
-hipError_t launch(const void* o_rounds, const float* lse, void* o, long bh, int L, int n_r,
-                  hipStream_t s)
+template <typename T, int D, int NR>
+hipError_t launch_nr(const void* o_rounds, const float* lse, void* o, long bh, int L, int n_r,
+                     hipStream_t s)
 {
     constexpr int RPB = COMB_THREADS / (D / (16 / (int)sizeof(T)));
     const long rows = bh * L;
     const long blocks = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((k_combine<T, D>), dim3((unsigned)blocks), dim3(COMB_THREADS), 0, s,
+    hipLaunchKernelGGL((k_combine<T, D, NR>), dim3((unsigned)blocks), dim3(COMB_THREADS), 0, s,
                        static_cast<const T*>(o_rounds), lse, static_cast<T*>(o), rows, L, n_r);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch(const void* o_rounds, const float* lse, void* o, long bh, int L, int n_r,
+                  hipStream_t s)
+{
+    if (n_r <= 1) return launch_nr<T, D, 1>(o_rounds, lse, o, bh, L, n_r, s);
+    if (n_r <= 2) return launch_nr<T, D, 2>(o_rounds, lse, o, bh, L, n_r, s);
+    if (n_r <= 4) return launch_nr<T, D, 4>(o_rounds, lse, o, bh, L, n_r, s);
+    if (n_r <= 8) return launch_nr<T, D, 8>(o_rounds, lse, o, bh, L, n_r, s);
+    return launch_nr<T, D, MAX_ROUNDS>(o_rounds, lse, o, bh, L, n_r, s);
 }
 
 }  // namespace
