@@ -11,6 +11,9 @@ What pins what:
          - bucket labels on axis-aligned inputs (x along column k of R lands in
            bucket k, -x in bucket k + n_buckets/2; exact ties go to the first
            index of [p, -p]);
+         - the near-tie margin (top-1 minus top-2 of [p, -p]) on hand-built
+           projections with known gaps: runner-up in either half, winner in
+           the negated half, exact ties (margin 0), one column;
          - antipodal identity h(-x) = (h(x) + n_buckets/2) mod n_buckets;
          - scale invariance h(2^k x) = h(x);
          - with 2 buckets, the collision rate over random R is 1 - angle/pi
@@ -75,33 +78,51 @@ def small_case(L=48, d=8, nb=6, n_r=3, chunk=8, causal=False, seed=11, dtype="f3
 
 
 # --------------------------------------------------------------------------- hash
-def check_hash_demo():
+def _draw_recipe(rc):
+    """The named draws of a fixture recipe, in order, from torch's CPU generator
+    (seeded 0): each is a standard-normal tensor of the listed shape, optionally
+    scaled and added to an earlier draw.  Shapes name the recipe's sizes; "x/2"
+    is half of size x."""
     import torch  # only to reproduce the page's random draws (CPU generator)
+
+    def dim(s):
+        name, _, div = s.partition("/")
+        return rc["sizes"][name] // int(div or 1)
+
+    out = {}
+    state = torch.random.get_rng_state()
+    try:
+        torch.manual_seed(0)
+        for dr in rc["draws"]:
+            z = torch.randn(*[dim(s) for s in dr["shape"]]).numpy().astype(np.float64)
+            if "scaled_by" in dr:
+                # float32 arithmetic, as the draws themselves
+                z = (np.float32(dr["scaled_by"]) * z.astype(np.float32)).astype(np.float64)
+            if "added_to" in dr:
+                z = (out[dr["added_to"]].astype(np.float32) + z.astype(np.float32)).astype(np.float64)
+            out[dr["name"]] = z
+    finally:
+        torch.random.set_rng_state(state)
+    return out
+
+
+def check_hash_demo():
+    """The Ultralytics page's hashing example: cosines and same-bucket shares of
+    two vectors against a reference, over many rounds of random R."""
     with open(os.path.join(GOLDEN, "hash_demo.json")) as f:
         g = json.load(f)
     rc = g["recipe"]
-    dim, nb, rounds = rc["dim"], rc["n_buckets"], rc["rounds"]
-    gen_state = torch.random.get_rng_state()
-    try:
-        torch.manual_seed(0)
-        query = torch.randn(dim)
-        near = query + rc["near_noise"] * torch.randn(dim)
-        far = torch.randn(dim)
-        R = torch.randn(rounds, dim, nb // 2)
-    finally:
-        torch.random.set_rng_state(gen_state)
-    vecs = {"query": query.numpy(), "near": near.numpy(), "far": far.numpy()}
-    Rn = R.numpy().astype(np.float64)
-    bk = {}
-    for name, x in vecs.items():
-        bk[name] = np.array([O.hash_one(x, Rn[r])[0] for r in range(rounds)])
-    for name in ("near", "far"):
-        q = vecs["query"].astype(np.float64)
-        x = vecs[name].astype(np.float64)
-        cos = float(q @ x / (np.linalg.norm(q) * np.linalg.norm(x)))
-        # The page's example averages in single precision: 85/1000 is then
-        # 0.0850000009 and prints as 9%, where the double 0.085 would print 8%.
-        share = float(np.float32(np.count_nonzero(bk[name] == bk["query"])) / np.float32(rounds))
+    vals = _draw_recipe(rc)
+    R = vals[rc["projection"]]
+    ref = vals[rc["reference"]]
+    ref_b = O.hash_buckets(ref[None, None, None, :], R)[0][0, 0, :, 0]
+    for name in rc["compared"]:
+        x = vals[name]
+        xb = O.hash_buckets(x[None, None, None, :], R)[0][0, 0, :, 0]
+        cos = float(ref @ x / (np.linalg.norm(ref) * np.linalg.norm(x)))
+        # The page averages in single precision: 85/1000 is then 0.0850000009
+        # and prints as 9%, where the double 0.085 would print 8%.
+        share = float(np.float32(np.count_nonzero(xb == ref_b)) / np.float32(len(R)))
         got = {"cosine": f"{cos:.2f}", "same_bucket_percent": f"{share:.0%}"}
         assert got == g["printed"][name], (name, got, g["printed"][name])
 
@@ -123,6 +144,42 @@ def check_hash_labels():
     x[1], x[3] = -1.0, 1.0                             # [p,-p] ties at index 3 and half+1
     assert O.hash_one(x, R)[0] == 3
     assert O.hash_one(np.zeros(d), R) == (0, 0.0)      # zero vector: bucket 0, margin 0
+
+
+def check_hash_margin():
+    """The near-tie margin: the gap between the largest and second-largest
+    entries of [p, -p], on hand-built projections whose top two are known.
+    Runner-up in the same half, runner-up in the negated half, the winner in
+    the negated half, exact ties across and within halves (margin 0), and one
+    column (n_buckets = 2, where the runner-up is the winner's own negation)."""
+    cases = [
+        # p                       bucket  margin
+        ([1.0, 4.0, 3.5],           1,    0.5),    # runner-up p[2], same half
+        ([3.0, 1.0, -2.5],          0,    0.5),    # runner-up -p[2], negated half
+        ([-5.0, 1.0, 4.75],         3,    0.25),   # winner -p[0]; runner-up p[2]
+        ([0.5, -6.0, 2.0, 5.0],     5,    1.0),    # winner -p[1]; runner-up p[3]
+        ([2.0, -2.0],               0,    0.0),    # p[0] ties -p[1]: first index
+        ([-1.0, 3.0, -3.0],         1,    0.0),    # p[1] ties -p[2]
+        ([1.5, 1.5, -0.25],         0,    0.0),    # p[0] ties p[1], same half
+        ([0.7],                     0,    1.4),    # one column: runner-up is -p[0]
+        ([-0.2],                    1,    0.4),
+        ([0.0, 0.0, 0.0],           0,    0.0),    # zero projection
+    ]
+    for p, bucket, margin in cases:
+        b, m = O.bucket_from_projection(np.array([p]))
+        assert int(b[0]) == bucket, (p, int(b[0]), bucket)
+        assert abs(float(m[0]) - margin) < 1e-15, (p, float(m[0]), margin)
+    # through the projection: R's columns pick coordinates of x, so p = x[:3]
+    # exactly, and the margin is in projection units (linear in x)
+    d = 8
+    R = np.zeros((d, 3))
+    R[np.arange(3), np.arange(3)] = 1.0
+    x = np.zeros(d)
+    x[:3] = [3.0, 1.0, -2.5]
+    x[5] = 9.0                                        # outside R's columns: no effect
+    for k in (1.0, 2.0, 0.125):
+        assert O.hash_one(k * x, R) == (0, 0.5 * k)
+    assert O.hash_one(-x, R) == (3, 0.5)
 
 
 def check_hash_antipodal(seed=5):
@@ -534,6 +591,7 @@ def check_block_zero_weights(seed=64):
 ALL_CHECKS = {
     "hash_demo": check_hash_demo,
     "hash_labels": check_hash_labels,
+    "hash_margin": check_hash_margin,
     "hash_antipodal": check_hash_antipodal,
     "hash_scale": check_hash_scale_invariance,
     "simhash": check_simhash_rate,

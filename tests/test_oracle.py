@@ -79,6 +79,38 @@ def _argmin_labels(p):
     return b, np.ones(a.shape[0])
 
 
+def _margin_over_p_only(p):
+    """Bucket right, margin taken between the two largest entries of p alone."""
+    p = np.asarray(p, dtype=np.float64)
+    a = np.concatenate([p, -p], axis=-1)
+    s = np.sort(p, axis=-1)
+    m = s[:, -1] - s[:, -2] if p.shape[1] > 1 else np.abs(2 * s[:, -1])
+    return np.argmax(a, axis=-1).astype(np.int32), m
+
+
+def _margin_skips_negated_runner_up(p):
+    """Bucket right; the runner-up is searched in the winner's own half only."""
+    p = np.asarray(p, dtype=np.float64)
+    a = np.concatenate([p, -p], axis=-1)
+    b = np.argmax(a, axis=-1)
+    half = p.shape[1]
+    m = np.empty(p.shape[0])
+    for i in range(p.shape[0]):
+        side = a[i, :half] if b[i] < half else a[i, half:]
+        s = np.sort(side)
+        m[i] = s[-1] - s[-2] if half > 1 else 2 * abs(s[-1])
+    return b.astype(np.int32), m
+
+
+def _margin_absolute_values(p):
+    """Bucket right; margin from the two largest |p| even with one column."""
+    p = np.asarray(p, dtype=np.float64)
+    a = np.concatenate([p, -p], axis=-1)
+    s = np.sort(np.abs(p), axis=-1)
+    m = s[:, -1] - (s[:, -2] if p.shape[1] > 1 else 0.0)
+    return np.argmax(a, axis=-1).astype(np.int32), m
+
+
 def _unstable_sort(keys, n_keys):
     keys = np.asarray(keys)
     return np.lexsort((-np.arange(keys.size), keys))
@@ -185,6 +217,11 @@ MUTATIONS = {
                                       "backward_finite_differences"),
     "hash drops the negated half": ("bucket_from_projection", _argmax_positive_half_only, "hash_antipodal"),
     "hash takes argmin": ("bucket_from_projection", _argmin_labels, "hash_labels"),
+    "margin over p only": ("bucket_from_projection", _margin_over_p_only, "hash_margin"),
+    "margin skips the negated runner-up": ("bucket_from_projection", _margin_skips_negated_runner_up,
+                                           "hash_margin"),
+    "margin from |p| with one column": ("bucket_from_projection", _margin_absolute_values,
+                                        "hash_margin"),
     "sort not stable": ("stable_counting_sort", _unstable_sort, "sort_library"),
     "no look-back chunk": ("window_slots", _own_chunk_only, "union"),
     "look-back two chunks": ("window_slots", _two_back, "union"),
