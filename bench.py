@@ -8,9 +8,13 @@ stream the calls are launched on.  `roofline` describes the call with the
 largest time: achieved = algorithmic bytes (or FLOPs) per launch / its average
 duration.  `traffic` is the HBM traffic per launch of that kernel measured with
 rocprofv3 counters (profiles/pmc_traffic.json), or null when those counters were
-taken on a different kernel source.  `cpu_baseline` is the CPU oracle timed on
-one (batch row, head) of the same workload on this host, scaled to the whole
-workload.
+taken on a different kernel source.  Every call also carries its MFMA and HBM
+fractions and, for the four steps, the target fraction it is held to.
+`cpu_baseline` is the CPU oracle timed on this host's cores (a process pool,
+one BLAS thread per worker) on the same workload (a prefix of each sequence
+above 64K positions), run before the first GPU call; `hash_check` counts the
+near-ties and mismatches of the GPU's buckets against the oracle's on the
+positions it hashed.
 
 Other modes:
     --layer D_MODEL      time the attention layer instead: the shared-QK and value
@@ -136,6 +140,22 @@ def bound_of(name, w):
                              "lsh_ffn") else "hbm"
 
 
+# Targets per call: at least this fraction of the MI355X peak, of the named
+# resource (chunk attention: bf16 MFMA; hash, sort and combine: HBM).
+NORTH_STAR_TARGET = {"lsh_chunk_attn": ("mfma", 0.5), "lsh_hash": ("hbm", 0.6),
+                     "lsh_sort": ("hbm", 0.6), "lsh_combine_rounds": ("hbm", 0.6)}
+
+
+def both_fractions(name, w, ms, d_model=None, d_ff=None):
+    """(MFMA fraction, HBM fraction) of a call's algorithmic FLOPs and bytes at
+    the published peaks, whichever binds it."""
+    work = algorithmic_work(w, d_model, d_ff)[name]
+    sec = ms * 1e-3
+    mfma = work["flops"] / sec / (PEAK_MFMA_TFLOPS[w.dtype] * 1e12)
+    hbm = work["bytes"] / sec / (PEAK_HBM_GBS * 1e9)
+    return round(mfma, 4), round(hbm, 4)
+
+
 def roofline_entry(name, w, ms, d_model=None, d_ff=None):
     work = algorithmic_work(w, d_model, d_ff)[name]
     if bound_of(name, w) == "mfma":
@@ -170,34 +190,72 @@ def traffic_for(name, workload):
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, min_seconds=10.0, flags=0):
-    """The oracle on whole (batch row, head) slices of the workload, one after
-    another until about `min_seconds` of CPU work is done, scaled to all heads."""
+# The oracle's per-token work does not depend on the sequence length at a fixed
+# bucket count, chunk and round count (the hash costs d * nb/2 per token-round,
+# a query attends to 2 * chunk keys, the sort is linear), so a prefix of every
+# (batch row, head) measures the same tokens/s as the whole sequence.  Longer
+# sequences are timed on a prefix of this many positions.
+CPU_BASELINE_MAX_POSITIONS = 65536
+
+
+def cpu_baseline(w, x, flags=0):
+    """The oracle timed on this host's cores: a process pool (oracle/pool.py),
+    one BLAS thread per worker, over the (batch row, head) slices and rounds of
+    the workload (a prefix of each slice when L is above
+    CPU_BASELINE_MAX_POSITIONS).  Must run before the first GPU call: its
+    workers are spawned processes.  Returns (the JSON entry, the oracle's
+    buckets and margins of the positions it hashed)."""
     import numpy as np
-    import oracle.lsh_oracle as O
+    from oracle.pool import MAX_WORKERS, OraclePool, host_cores
+
+    Lp = min(w.seq_len, CPU_BASELINE_MAX_POSITIONS)
+    qk = np.ascontiguousarray(x["qk"][:, :, :Lp])
+    v = np.ascontiguousarray(x["v"][:, :, :Lp])
+    # Each hash job holds a few [16384, n_buckets] float64 arrays; keep the
+    # workers' peak within half the memory available.
+    per_job = 3 * 16384 * w.n_buckets * 8 + 64 * (2 << 20)
+    avail = _mem_available()
+    cores = min(host_cores(), MAX_WORKERS)
+    workers = max(1, min(cores, int(0.5 * avail / per_job))) if avail else cores
+    with OraclePool(workers) as pool:
+        out = pool.forward(qk, v, x["R"], w.n_buckets, w.chunk, w.causal,
+                           dup_correct=not (flags & 1), wrap=bool(flags & 2),
+                           same_bucket=bool(flags & 4), keep=("buckets", "margins", "o"))
+    assert np.isfinite(out["o"]).all()
+    sec = out["seconds"]
+    tokens = w.batch * Lp
+    sample = (f"the whole workload: {w.batch * w.heads} (batch row, head) slices x {w.n_rounds} rounds x "
+              f"{w.seq_len} positions" if Lp == w.seq_len else
+              f"the first {Lp} of the {w.seq_len} positions of all {w.batch * w.heads} (batch row, head) "
+              f"slices, {w.n_rounds} rounds (same buckets, chunk and rounds: the same work per token)")
+    entry = {"value": round(tokens / sec["total"], 1), "unit": "tokens/s", "cores": workers,
+             "kind": "oracle",
+             "sample": f"{sample}; hash+sort {sec['hash_sort']:.1f} s, attention {sec['attention']:.1f} s, "
+                       f"combine {sec['combine']:.1f} s wall-clock on {workers} worker processes "
+                       f"(one BLAS thread each) of {host_cores()} host cores"}
+    return entry, out["buckets"], out["margins"], Lp
+
+
+def _mem_available():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
-    R = x["R"].astype(np.float64)
-    heads = w.batch * w.heads
-    done, dt = 0, 0.0
-    while done < heads and dt < min_seconds:
-        b, h = divmod(done, w.heads)
-        qk = x["qk"][b:b + 1, h:h + 1].astype(np.float64)
-        v = x["v"][b:b + 1, h:h + 1].astype(np.float64)
-        t0 = time.perf_counter()
-        out = O.forward(qk, v, R, w.n_buckets, w.chunk, w.causal, dup_correct=not (flags & 1),
-                        wrap=bool(flags & 2))
-        dt += time.perf_counter() - t0
-        assert np.isfinite(out["o"]).all()
-        done += 1
-    tokens_per_s = w.batch * w.seq_len * done / (dt * heads)
-    return {"value": round(tokens_per_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {heads} (batch row, head) slices, each with all {w.n_rounds} "
-                      f"rounds over all {w.seq_len} positions, in {dt:.1f} s; "
-                      f"value = B*L*slices / (time * B*H)"}
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 0
+
+
+def hash_check(gpu_buckets, ref_buckets, margins, Lp, L):
+    """Near-ties and mismatches of the GPU's buckets against the oracle's on
+    the positions the CPU baseline hashed."""
+    import numpy as np
+    near = margins <= 1.0e-4
+    mism = gpu_buckets[..., :Lp] != ref_buckets
+    return {"hashes": int(mism.size), "near_ties": int(near.sum()), "mismatches": int(mism.sum()),
+            "mismatches_beyond_near_ties": int((mism & ~near).sum()),
+            "sample": "every hash" if Lp == L else f"the hashes of the first {Lp} positions"}
 
 
 def pmc_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
@@ -341,11 +399,16 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     blk = args.block
+    bwd_mode = args.backward
     if blk and (args.layer or args.backward):
         raise SystemExit("--block, --layer and --backward are separate modes")
     dm = args.layer or blk
     dff = (args.d_ff or 4 * blk) if blk else None
     x = (make_block_inputs(w, dm, dff) if blk else make_layer_inputs(w, dm)) if dm else make_inputs(w)
+    # The CPU baseline spawns worker processes, so it runs before the first GPU call.
+    base = None
+    if not args.no_cpu_baseline and not dm and not bwd_mode:
+        base = cpu_baseline(w, x, flags=args.flags)
     cfg = lsh.LSHConfig(w.batch, w.heads, w.seq_len, w.d_head, w.n_buckets, w.n_rounds, w.chunk,
                         w.causal, dtype=w.dtype, flags=args.flags)
     tdt = cfg.torch_dtype
@@ -479,10 +542,16 @@ def main():
     if blk:
         roof["call"] = dominant
     roof["algorithmic_per_launch"] = work["flops"] if roof["bound"] == "mfma" else work["bytes"]
+    roof["mfma_frac"], roof["hbm_frac"] = both_fractions(kind(dominant), w, per_call[dominant], dm, dff)
     kernels = {}
     for n in names:
         e = roofline_entry(kind(n), w, per_call[n], dm, dff)
         e["ms"] = round(per_call[n], 4)
+        e["mfma_frac"], e["hbm_frac"] = both_fractions(kind(n), w, per_call[n], dm, dff)
+        tgt = NORTH_STAR_TARGET.get(kind(n))
+        if tgt and not dm and not bwd and not blk:
+            got = e[tgt[0] + "_frac"]
+            e["target"] = {"of": tgt[0], "frac": tgt[1], "met": got >= tgt[1]}
         kernels[n] = e
 
     result = {
@@ -500,8 +569,10 @@ def main():
                    **({"backward": True} if bwd else {})},
         "roofline": roof, "kernels": kernels,
     }
-    if not args.no_cpu_baseline and not dm and not bwd:
-        result["cpu_baseline"] = cpu_baseline(w, x, flags=args.flags)
+    if base is not None:
+        entry, ref_b, ref_m, Lp = base
+        result["cpu_baseline"] = entry
+        result["hash_check"] = hash_check(buckets.cpu().numpy(), ref_b, ref_m, Lp, L)
     print(json.dumps(result), flush=True)
 
 

@@ -148,17 +148,20 @@ def full_parity(w: Workload, scale=None, x=None, flags=0) -> dict:
     oc, _ = O.combine_rounds(to_np(g["o_rounds"]).astype(np.float64), to_np(g["lse"]).astype(np.float64))
     rep["combine_err"] = rel_err(to_np(g["o"]), oc)
     assert rep["combine_err"] <= GATE[w.dtype], (w.name, "combine", rep["combine_err"])
-    # forward from scratch, on the heads whose buckets agree everywhere
+    # forward from scratch, on the heads whose buckets agree everywhere.  There
+    # the oracle's own sort equals the sort of the GPU's buckets (asserted), so
+    # its attention is the one computed above and only the combine remains.
     same = np.all(gb == ob, axis=(2, 3))
     rep["heads_bucket_exact"] = f"{int(same.sum())}/{same.size}"
     if same.any():
         pf, cf = O.sort_rounds(ob, w.n_buckets, w.chunk)
-        of_r, lf = O.attention_rounds(qk, v, pf, cf, w.chunk, w.causal, sc, **var,
-                                      buckets=ob if same_bucket(flags) else None)
-        of, _ = O.combine_rounds(of_r, lf)
+        assert np.array_equal(pf[same], sp[same]) and np.array_equal(cf[same], sc_id[same])
+        of, _ = O.combine_rounds(o_r, lse)
         go = to_np(g["o"])
         rep["forward_err"] = rel_err(go[same], of[same])
         assert rep["forward_err"] <= GATE[w.dtype], (w.name, "forward", rep["forward_err"])
+    rep["rows_compared"] = {"o_rounds": int(np.prod(o_r.shape[:-1])), "o": int(np.prod(oc.shape[:-1])),
+                            "o_from_scratch": int(same.sum()) * w.seq_len}
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[parity] {rep}")
     return rep
@@ -189,8 +192,10 @@ def sort_properties(gb: np.ndarray, gp: np.ndarray, gc: np.ndarray, chunk: int, 
     return want
 
 
-def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int = 0) -> dict:
-    """Full-size workload: every sort output, sampled hashes, rows and tokens."""
+def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int = 0,
+                   slices=(), slice_hash: bool = True) -> dict:
+    """Full-size workload: every sort output, sampled hashes, rows and tokens;
+    then every row of the (batch row, head) slices listed (see slice_checks)."""
     t0 = time.time()
     log(f"[sampled] {w.name} flags {flags}: generating inputs")
     x = make_inputs(w)
@@ -242,6 +247,58 @@ def sampled_parity(w: Workload, n_samples: int = 1024, seed: int = 0, flags: int
     assert rep["combine_err"] <= GATE[w.dtype], (w.name, "combine", rep["combine_err"])
     rep["seconds"] = round(time.time() - t0, 1)
     log(f"[sampled] {rep}")
+    for b, h in slices:
+        rep[f"slice_b{b}_h{h}"] = slice_checks(w, x, g, b, h, flags, slice_hash, sc, t0)
+    return rep
+
+
+def slice_checks(w: Workload, x, g, b: int, h: int, flags: int, with_hash: bool, sc: float,
+                 t0: float) -> dict:
+    """Every row of one (batch row, head) of a full-size run: its hashes in every
+    round (with_hash), its perm/cid bit-exact against the oracle's stable sort
+    of the GPU's buckets, every o_rounds row and lse fed the GPU's perm/cid,
+    every combined row fed the GPU's o_rounds/lse, and the forward from scratch
+    when all the slice's hashes agree with the oracle's."""
+    var = variant(flags)
+    rep = {}
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    gb = to_np(g["buckets"][sl])
+    qk = x["qk"][sl].astype(np.float64)
+    v = x["v"][sl].astype(np.float64)
+    ob = None
+    if with_hash:
+        log(f"[slice] {w.name} b {b} h {h}: hashes of {w.n_rounds} x {w.seq_len} ({time.time() - t0:.1f}s)")
+        ob, om = O.hash_buckets(qk, x["R"].astype(np.float64))
+        rep.update(check_hash(gb, ob, om, f"{w.name} slice"))
+    log(f"[slice] {w.name} b {b} h {h}: sort ({time.time() - t0:.1f}s)")
+    sp, sc_id = O.sort_rounds(gb, w.n_buckets, w.chunk)
+    assert np.array_equal(to_np(g["perm"][sl]), sp), f"{w.name} slice: perm differs from the stable sort"
+    gcid = to_np(g["cid"][sl])
+    if same_bucket(flags):
+        assert np.array_equal(gcid.view(np.uint16), window_ids(sc_id, gb, w.n_buckets))
+    else:
+        assert np.array_equal(gcid, sc_id), f"{w.name} slice: cid differs"
+    log(f"[slice] {w.name} b {b} h {h}: attention, {w.n_rounds} rounds x {w.seq_len // w.chunk} "
+        f"chunks ({time.time() - t0:.1f}s)")
+    o_r, lse = O.attention_rounds(qk, v, sp, sc_id, w.chunk, w.causal, sc, **var,
+                                  buckets=gb if same_bucket(flags) else None)
+    g_or = to_np(g["o_rounds"][sl])
+    g_lse = to_np(g["lse"][sl])
+    rep["o_rounds_err"] = rel_err(g_or, o_r)
+    assert rep["o_rounds_err"] <= GATE[w.dtype], (w.name, "slice o_rounds", rep["o_rounds_err"])
+    rep["lse_abs_err"] = check_lse(g_lse, lse, w.dtype, f"{w.name} slice")
+    oc, _ = O.combine_rounds(g_or.astype(np.float64), g_lse.astype(np.float64))
+    go = to_np(g["o"][sl])
+    rep["combine_err"] = rel_err(go, oc)
+    assert rep["combine_err"] <= GATE[w.dtype], (w.name, "slice combine", rep["combine_err"])
+    rep["rows_compared"] = {"o_rounds": w.n_rounds * w.seq_len, "o": w.seq_len}
+    if ob is not None and np.array_equal(ob, gb):
+        # the oracle's own sort of identical buckets is the one above
+        of, _ = O.combine_rounds(o_r, lse)
+        rep["forward_err"] = rel_err(go, of)
+        assert rep["forward_err"] <= GATE[w.dtype], (w.name, "slice forward", rep["forward_err"])
+        rep["rows_compared"]["o_from_scratch"] = w.seq_len
+    log(f"[slice] {w.name} b {b} h {h}: {rep} ({time.time() - t0:.1f}s)")
     return rep
 
 

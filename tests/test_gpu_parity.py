@@ -188,9 +188,37 @@ def test_clustered_16k_full():
     GP.full_parity(WORKLOADS["clustered_16k"])
 
 
+# (batch row, head) slices checked row by row at full size: paper_64k with its
+# hashes, long_1m fed the GPU's sort (a slice's hashes there are 2 TFLOP of fp64)
+FULL_SIZE_SLICES = {"paper_64k": ([(0, 5)], True), "long_1m": ([(0, 2)], False)}
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["paper_64k", "long_1m"])
 def test_full_size_sampled(name):
-    GP.sampled_parity(WORKLOADS[name], n_samples=512)
+    """The benchmark's workloads at full size in its launch configuration:
+    every sort output, 512 sampled hashes / rows / tokens, and every row of one
+    (batch row, head) slice."""
+    slices, with_hash = FULL_SIZE_SLICES[name]
+    GP.sampled_parity(WORKLOADS[name], n_samples=512, slices=slices, slice_hash=with_hash)
+
+
+# Full-tensor cases that reach the kernels the benchmark's workloads run:
+# d 128 with 8 rounds (four chunk-id words, two gather register sets) and runs
+# of 16 chunks, as paper_64k; bf16 d 64 with chunk 128, 4 rounds (two words) and
+# runs of 16 chunks, as long_1m.  Every output of every step is compared.
+HEADLINE_SHAPES = {
+    "paper_path_L16384_r8_d128": W("paper_path", heads=8, seq_len=16384, d_head=128, n_buckets=256,
+                                   n_rounds=8, chunk=64, causal=True, seed=144),
+    "long_path_L65536_r4_c128": W("long_path", heads=8, seq_len=65536, d_head=64, n_buckets=1024,
+                                  n_rounds=4, chunk=128, causal=True, seed=145),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", sorted(HEADLINE_SHAPES))
+def test_full_parity_headline_paths(name):
+    GP.full_parity(HEADLINE_SHAPES[name])
 
 
 def test_streams_and_preallocated_outputs():

@@ -268,3 +268,21 @@ def test_mutation_is_caught(name, monkeypatch):
     monkeypatch.setattr(O, attr, repl)
     with pytest.raises((AssertionError, IndexError, ValueError)):
         P.ALL_CHECKS[check]()
+
+
+# --------------------------------------------------------------------------- pooled oracle
+@pytest.mark.parametrize("kw", [dict(), dict(same_bucket=True), dict(wrap=True, dup_correct=False)])
+def test_pooled_forward_equals_forward(kw):
+    """The benchmark's process-pool driver (oracle/pool.py) splits the oracle's
+    forward into per-(slice, round) jobs; the results are the same arrays."""
+    from oracle.pool import OraclePool
+    w, _, _, R = P.small_case(L=64, d=8, nb=8, n_r=3, chunk=8, causal=True, seed=33)
+    rng = np.random.default_rng(34)
+    qk = rng.standard_normal((2, 2, 64, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 2, 64, 8)).astype(np.float32)
+    ref = O.forward(qk.astype(np.float64), v.astype(np.float64), R, 8, 8, True, **kw)
+    with OraclePool(workers=3) as pool:
+        got = pool.forward(qk, v, R, 8, 8, True, **kw)
+    for k in ("buckets", "margins", "perm", "cid", "o_rounds", "lse", "o", "LSE"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert set(got["seconds"]) == {"hash_sort", "attention", "combine", "total"}
