@@ -27,7 +27,7 @@
  *   current device).  The caller allocates and owns every buffer; the library
  *   allocates nothing, draws no random numbers and keeps no mutable global state,
  *   so calls on different streams may run concurrently.
- *   `stream` is a hipStream_t (NULL = the default stream).
+ *   `stream` is the HIP stream the kernels run on (NULL = the default stream).
  *   dtype LSH_BF16: qk, v, R, o_rounds and o hold bfloat16; products are exact and
  *   accumulate in fp32; outputs are rounded to nearest even.  dtype LSH_F32: all
  *   float32.
@@ -54,6 +54,11 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* hipStream_t.  hipcc defines the platform macro itself; a plain C or C++
+ * compiler building host code against this header adds -D__HIP_PLATFORM_AMD__
+ * and -I/opt/rocm/include, as for any HIP API host code. */
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -121,7 +126,7 @@ typedef struct lsh_config {
  *   buckets  [B, H, n_r, L]      int32 out, values in [0, nb)
  */
 lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R,
-                    int32_t* buckets, void* stream);
+                    int32_t* buckets, hipStream_t stream);
 
 /* Bytes of device workspace lsh_sort needs for `cfg` (0 if cfg is invalid). */
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
@@ -134,11 +139,11 @@ size_t lsh_sort_workspace_bytes(const lsh_config* cfg);
  *   perm       [B, H, n_r, L]   int32 out: perm[b,h,r,slot] = position
  *   cid        [B, H, L, n_r]   int16 out: cid[b,h,pos,r] = slot(pos) / chunk
  *   workspace  device scratch of at least lsh_sort_workspace_bytes(cfg) bytes
- *              (larger with LSH_FLAG_SAME_BUCKET); its contents on entry do
- *              not matter.
+ *              (per-tile bucket counters and per-round bucket totals); its
+ *              contents on entry do not matter.
  */
 lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm,
-                    int16_t* cid, void* workspace, size_t workspace_bytes, void* stream);
+                    int16_t* cid, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Step 3 — chunked attention, one output per round.  [AIS] formula and LSH
@@ -159,7 +164,7 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
  */
 lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v,
                           const int32_t* perm, const int16_t* cid, void* o_rounds,
-                          float* lse, void* stream);
+                          float* lse, hipStream_t stream);
 
 /*
  * Step 4 — combine the rounds.  [MOD] "Multi-round LSH attention"; [ULT].
@@ -168,7 +173,7 @@ lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v,
  *   o        [B, H, L, d]      dtype out.
  */
 lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds,
-                              const float* lse, void* o, void* stream);
+                              const float* lse, void* o, hipStream_t stream);
 
 /*
  * Backward of steps 3-4: gradients with respect to qk and v (bfloat16, chunk 64;
@@ -198,7 +203,7 @@ size_t lsh_backward_workspace_bytes(const lsh_config* cfg);
 lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* v,
                              const int32_t* perm, const int16_t* cid, const float* lse,
                              const void* o, const void* d_o, float* d_qk, float* d_v,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Projections of the LSH-attention layer around steps 1-4 (bfloat16 only).
@@ -217,9 +222,9 @@ lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* 
  * or B*L >= 2^31 (LSH_ERR_INVALID_ARG); dtype not LSH_BF16 (LSH_ERR_UNSUPPORTED).
  */
 lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x, const void* w_qk,
-                          const void* w_v, void* qk, void* v, void* stream);
+                          const void* w_v, void* qk, void* v, hipStream_t stream);
 lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o, const void* w_o,
-                           void* y, void* stream);
+                           void* y, hipStream_t stream);
 
 /*
  * The Reformer block's pieces (bfloat16, fp32 accumulation, outputs rounded to
@@ -250,12 +255,12 @@ lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o
  */
 lsh_status lsh_project_out_add(const lsh_config* cfg, int32_t d_model, const void* o,
                                const void* w_o, const void* residual, float sign, void* y,
-                               void* stream);
+                               hipStream_t stream);
 size_t lsh_ffn_workspace_bytes(int64_t rows, int32_t d_ff, int32_t chunk_rows);
 lsh_status lsh_ffn(int64_t rows, int32_t d_model, int32_t d_ff, int32_t chunk_rows, const void* x,
                    const void* w1, const void* b1, const void* w2, const void* b2,
                    const void* residual, float sign, void* y, void* hidden, size_t hidden_bytes,
-                   void* stream);
+                   hipStream_t stream);
 
 /* Static description of a status code. */
 const char* lsh_status_string(lsh_status status);

@@ -113,11 +113,8 @@ lsh_status check_layer(const lsh_config* cfg, int32_t d_model)
     return LSH_OK;
 }
 
-// counters, then (same-bucket variant) one rank per (segment, bucket)
-size_t ranks_of(const lsh_config* cfg, const lshk::SortPlan& p)
-{
-    return (cfg->flags & LSH_FLAG_SAME_BUCKET) ? (size_t)p.nseg * cfg->n_buckets : 0;
-}
+// counters, then one int32 per (segment, bucket)
+size_t sort_ws_bytes(const lshk::SortPlan& p) { return (p.counters + p.extra) * sizeof(int32_t); }
 
 // Backward workspace: combined lse and Delta (float32, one per token-head), then
 // the three per-round partial tensors (bf16), each part 256-byte aligned.
@@ -167,7 +164,7 @@ const char* lsh_status_string(lsh_status s)
 const char* lsh_last_error(void) { return g_last_error.c_str(); }
 
 lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_t* buckets,
-                    void* stream)
+                    hipStream_t stream)
 {
     LSH_TRY(check_config(cfg));
     LSH_TRY(check_ptr(qk, "qk"));
@@ -175,38 +172,39 @@ lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_
     LSH_TRY(check_ptr(buckets, "buckets"));
     return hip_status(lshk::launch_hash(cfg->dtype, cfg->d_head, qk, R, buckets, bh_of(cfg),
                                         cfg->seq_len, cfg->n_rounds, cfg->n_buckets / 2,
-                                        static_cast<hipStream_t>(stream)),
+                                        stream),
                       "lsh_hash");
 }
 
 size_t lsh_sort_workspace_bytes(const lsh_config* cfg)
 {
     if (check_config(cfg) != LSH_OK) return 0;
-    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
-    return (p.counters + ranks_of(cfg, p)) * sizeof(int32_t);
+    return sort_ws_bytes(lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets,
+                                             (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0));
 }
 
 lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm, int16_t* cid,
-                    void* workspace, size_t workspace_bytes, void* stream)
+                    void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     LSH_TRY(check_config(cfg));
     LSH_TRY(check_ptr(buckets, "buckets"));
     LSH_TRY(check_ptr(perm, "perm"));
     LSH_TRY(check_ptr(cid, "cid"));
     LSH_TRY(check_ptr(workspace, "workspace"));
-    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets);
-    if (workspace_bytes < (p.counters + ranks_of(cfg, p)) * sizeof(int32_t))
+    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets,
+                                             (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0);
+    if (workspace_bytes < sort_ws_bytes(p))
         return fail(LSH_ERR_WORKSPACE, "workspace smaller than lsh_sort_workspace_bytes()");
     int32_t* counters = static_cast<int32_t*>(workspace);
-    int32_t* ranks = ranks_of(cfg, p) ? counters + p.counters : nullptr;
-    return hip_status(lshk::launch_sort(buckets, perm, cid, counters, ranks, p, bh_of(cfg),
+    return hip_status(lshk::launch_sort(buckets, perm, cid, counters, counters + p.counters,
+                                        (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0, p, bh_of(cfg),
                                         cfg->seq_len, cfg->n_rounds, cfg->n_buckets, cfg->chunk,
-                                        static_cast<hipStream_t>(stream)),
+                                        stream),
                       "lsh_sort");
 }
 
 lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v, const int32_t* perm,
-                          const int16_t* cid, void* o_rounds, float* lse, void* stream)
+                          const int16_t* cid, void* o_rounds, float* lse, hipStream_t stream)
 {
     LSH_TRY(check_config(cfg));
     if (cfg->chunk != 32 && cfg->chunk != 64 && cfg->chunk != 128)
@@ -222,12 +220,12 @@ lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v, 
     return hip_status(lshk::launch_chunk_attn(cfg->dtype, cfg->d_head, cfg->chunk, qk, v, perm, cid,
                                               o_rounds, lse, bh_of(cfg), cfg->seq_len,
                                               cfg->n_rounds, cfg->causal, cfg->scale, cfg->flags,
-                                              static_cast<hipStream_t>(stream)),
+                                              stream),
                       "lsh_chunk_attn");
 }
 
 lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds, const float* lse,
-                              void* o, void* stream)
+                              void* o, hipStream_t stream)
 {
     LSH_TRY(check_config(cfg));
     LSH_TRY(check_ptr(o_rounds, "o_rounds"));
@@ -235,7 +233,7 @@ lsh_status lsh_combine_rounds(const lsh_config* cfg, const void* o_rounds, const
     LSH_TRY(check_ptr(o, "o"));
     return hip_status(lshk::launch_combine(cfg->dtype, cfg->d_head, o_rounds, lse, o, bh_of(cfg),
                                            cfg->seq_len, cfg->n_rounds,
-                                           static_cast<hipStream_t>(stream)),
+                                           stream),
                       "lsh_combine_rounds");
 }
 
@@ -248,7 +246,7 @@ size_t lsh_backward_workspace_bytes(const lsh_config* cfg)
 lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* v,
                              const int32_t* perm, const int16_t* cid, const float* lse,
                              const void* o, const void* d_o, float* d_qk, float* d_v,
-                             void* workspace, size_t workspace_bytes, void* stream)
+                             void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     LSH_TRY(check_backward(cfg));
     LSH_TRY(check_ptr(qk, "qk"));
@@ -288,12 +286,12 @@ lsh_status lsh_attn_backward(const lsh_config* cfg, const void* qk, const void* 
     a.dup = !(cfg->flags & LSH_FLAG_NO_DUP_CORRECTION);
     a.wrap = (cfg->flags & LSH_FLAG_WRAP_LOOKBACK) != 0;
     a.same_bucket = (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0;
-    return hip_status(lshk::launch_attn_backward(cfg->d_head, a, static_cast<hipStream_t>(stream)),
+    return hip_status(lshk::launch_attn_backward(cfg->d_head, a, stream),
                       "lsh_attn_backward");
 }
 
 lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x, const void* w_qk,
-                          const void* w_v, void* qk, void* v, void* stream)
+                          const void* w_v, void* qk, void* v, hipStream_t stream)
 {
     LSH_TRY(check_layer(cfg, d_model));
     LSH_TRY(check_ptr(x, "x"));
@@ -303,12 +301,12 @@ lsh_status lsh_project_in(const lsh_config* cfg, int32_t d_model, const void* x,
     LSH_TRY(check_ptr(v, "v"));
     return hip_status(lshk::launch_project_in(x, w_qk, w_v, qk, v, (long)cfg->batch * cfg->seq_len,
                                               cfg->seq_len, cfg->heads, cfg->d_head, d_model,
-                                              static_cast<hipStream_t>(stream)),
+                                              stream),
                       "lsh_project_in");
 }
 
 lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o, const void* w_o,
-                           void* y, void* stream)
+                           void* y, hipStream_t stream)
 {
     LSH_TRY(check_layer(cfg, d_model));
     LSH_TRY(check_ptr(o, "o"));
@@ -316,13 +314,13 @@ lsh_status lsh_project_out(const lsh_config* cfg, int32_t d_model, const void* o
     LSH_TRY(check_ptr(y, "y"));
     return hip_status(lshk::launch_project_out(o, w_o, y, (long)cfg->batch * cfg->seq_len,
                                                cfg->seq_len, cfg->heads, cfg->d_head, d_model,
-                                               nullptr, 0.f, static_cast<hipStream_t>(stream)),
+                                               nullptr, 0.f, stream),
                       "lsh_project_out");
 }
 
 lsh_status lsh_project_out_add(const lsh_config* cfg, int32_t d_model, const void* o,
                                const void* w_o, const void* residual, float sign, void* y,
-                               void* stream)
+                               hipStream_t stream)
 {
     LSH_TRY(check_layer(cfg, d_model));
     if (!std::isfinite(sign)) return fail(LSH_ERR_INVALID_ARG, "sign must be finite");
@@ -332,7 +330,7 @@ lsh_status lsh_project_out_add(const lsh_config* cfg, int32_t d_model, const voi
     LSH_TRY(check_ptr(y, "y"));
     return hip_status(lshk::launch_project_out(o, w_o, y, (long)cfg->batch * cfg->seq_len,
                                                cfg->seq_len, cfg->heads, cfg->d_head, d_model,
-                                               residual, sign, static_cast<hipStream_t>(stream)),
+                                               residual, sign, stream),
                       "lsh_project_out_add");
 }
 
@@ -346,7 +344,7 @@ size_t lsh_ffn_workspace_bytes(int64_t rows, int32_t d_ff, int32_t chunk_rows)
 lsh_status lsh_ffn(int64_t rows, int32_t d_model, int32_t d_ff, int32_t chunk_rows, const void* x,
                    const void* w1, const void* b1, const void* w2, const void* b2,
                    const void* residual, float sign, void* y, void* hidden, size_t hidden_bytes,
-                   void* stream)
+                   hipStream_t stream)
 {
     if (rows <= 0 || rows >= (1LL << 31))
         return fail(LSH_ERR_INVALID_ARG, "rows must be positive and below 2^31");
@@ -365,7 +363,7 @@ lsh_status lsh_ffn(int64_t rows, int32_t d_model, int32_t d_ff, int32_t chunk_ro
     if (hidden_bytes < lsh_ffn_workspace_bytes(rows, d_ff, chunk_rows))
         return fail(LSH_ERR_WORKSPACE, "hidden smaller than lsh_ffn_workspace_bytes()");
     return hip_status(lshk::launch_ffn(x, w1, b1, w2, b2, residual, sign, y, hidden, (long)rows,
-                                       d_model, d_ff, chunk_rows, static_cast<hipStream_t>(stream)),
+                                       d_model, d_ff, chunk_rows, stream),
                       "lsh_ffn");
 }
 

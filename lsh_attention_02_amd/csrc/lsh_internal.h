@@ -13,19 +13,23 @@ hipError_t launch_hash(int dtype, int d_head, const void* qk, const void* R, int
                        long bh, int L, int n_rounds, int ncol, hipStream_t stream);
 
 // Sort geometry: positions of one (b, h, r) segment are split into tiles of
-// `tile` positions; the workspace holds one int32 counter per (segment, tile, bucket).
+// `tile` positions; the workspace holds one int32 counter per (segment, tile,
+// bucket), then one int32 per (segment, bucket) (bucket totals, or the
+// same-bucket variant's bucket ranks).
 struct SortPlan {
     int tile;
     int ntiles;
     long nseg;
     size_t counters;   // nseg * ntiles * n_buckets
+    size_t extra;      // nseg * n_buckets
+    int rounds_per_group;   // rounds per k_sort_place workgroup, 0: k_sort_scatter
 };
-SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets);
+SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket);
 
-// ranks: null, or nseg * n_buckets int32 of scratch for the same-bucket variant.
+// counters, extra: the two workspace parts of SortPlan (int32 each).
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
-                       int32_t* ranks, const SortPlan& plan, long bh, int L, int n_rounds,
-                       int n_buckets, int chunk, hipStream_t stream);
+                       int32_t* extra, bool same_bucket, const SortPlan& plan, long bh, int L,
+                       int n_rounds, int n_buckets, int chunk, hipStream_t stream);
 
 hipError_t launch_chunk_attn(int dtype, int d_head, int chunk, const void* qk, const void* v,
                              const int32_t* perm, const int16_t* cid, void* o_rounds, float* lse,

@@ -3,23 +3,40 @@
 // "LSH attention": tokens sorted by bucket, then cut into equal chunks).
 //
 // Counting sort in three launches:
-//   k_sort_hist     one workgroup per (segment, tile): LDS histogram of the
-//                   tile's buckets -> counters[seg][tile][bucket]
+//   k_sort_hist     one workgroup per (segment, tile of positions): LDS
+//                   histogram of the tile's buckets -> counters[seg][tile][bucket]
 //   k_sort_scan     one workgroup per segment: counters become the first slot
 //                   of each (tile, bucket): sum of all earlier buckets plus the
 //                   same bucket in earlier tiles
-//   k_sort_scatter  one workgroup per (segment, tile): walks its tile in
-//                   position order, 256 positions at a time; inside a wave,
-//                   equal buckets are ranked by lane with ballots; the four
-//                   waves take their offsets in order (barrier phases), so equal
-//                   buckets keep position order across the whole segment.
+//   k_sort_place    one workgroup per (batch row, head, tile, group of rounds),
+//                   one wave per round.  The wave reads its round's buckets of
+//                   the tile into LDS, orders the tile by bucket there (stable:
+//                   positions are ranked in increasing order, equal buckets
+//                   inside a wave by ballots), then writes perm in that order,
+//                   so that each bucket's slots of the tile are one contiguous
+//                   run of stores.  The chunk ids of the tile's positions stay
+//                   in LDS until every round of the group is placed and are
+//                   written as whole rows of cid.
+//   k_sort_scatter  (used instead of k_sort_place when a round's tile does not
+//                   fit in LDS: many buckets with large tiles) one workgroup per
+//                   (segment, tile): walks the tile 256 positions at a time,
+//                   equal buckets ranked by lane with ballots, the four waves
+//                   taking their offsets in order (barrier phases).
 // Outputs: perm[seg][slot] = position and cid[b,h][position][round] = slot / chunk
 // (with the same-bucket variant: slot / chunk + 2 * rank of the bucket among the
 // segment's non-empty buckets, computed by the scan).
+//
+// Why the placement is staged: every store the L2 receives is one request, and
+// a store instruction whose 64 lanes hit 64 different lines costs 64 of them.
+// Stored per position, perm (4 bytes) and cid (2 bytes, at a 2 * n_rounds byte
+// stride) cost about one request per element each, and the L2's request rate,
+// not HBM, bounded the sort.  In tile order a wave's 64 perm stores fall in a
+// few runs, and the cid rows of a tile form one contiguous block.
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace lshk {
 namespace {
@@ -38,9 +55,14 @@ void k_sort_hist(const int32_t* __restrict__ buckets, int32_t* __restrict__ coun
     __syncthreads();
     const int32_t* bk = buckets + seg * L;
     const int p1 = min(L, (t + 1) * tile);
-    for (int p = t * tile + threadIdx.x; p < p1; p += SORT_THREADS) {
-        const int b = bk[p];
-        if ((unsigned)b < (unsigned)nb) atomicAdd(&hist[b], 1);
+    // eight loads in flight per thread before the first LDS update
+    for (int p = t * tile + threadIdx.x; p < p1; p += 8 * SORT_THREADS) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = p + k * SORT_THREADS < p1 ? bk[min(p + k * SORT_THREADS, p1 - 1)] : -1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if ((unsigned)v[k] < (unsigned)nb) atomicAdd(&hist[v[k]], 1);
     }
     __syncthreads();
     int32_t* out = counters + (seg * ntiles + t) * (long)nb;
@@ -77,6 +99,11 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* wave_sums, int* 
 
 // ranks (may be null): ranks[seg][b] = number of non-empty buckets below b in
 // the segment (used by the same-bucket variant's window ids).
+// Thread b of a block of SCAN_THREADS buckets owns column b: up to SCAN_KEEP
+// tiles' counts are loaded at once and kept in registers; more tiles take two
+// passes (sum, then rewrite) in batches of SCAN_KEEP loads.
+constexpr int SCAN_KEEP = 16;
+
 __global__ __launch_bounds__(SCAN_THREADS)
 void k_sort_scan(int32_t* __restrict__ counters, int32_t* __restrict__ ranks, int nb, int ntiles)
 {
@@ -85,17 +112,41 @@ void k_sort_scan(int32_t* __restrict__ counters, int32_t* __restrict__ ranks, in
     int carry = 0, rank_carry = 0;
     for (int b0 = 0; b0 < nb; b0 += SCAN_THREADS) {
         const int b = b0 + threadIdx.x;
+        const bool own = b < nb;
+        int x[SCAN_KEEP];
         int tot = 0;
-        if (b < nb)
-            for (int t = 0; t < ntiles; ++t) tot += c[(long)t * nb + b];
+        if (own) {
+            for (int t0 = 0; t0 < ntiles; t0 += SCAN_KEEP) {
+#pragma unroll
+                for (int k = 0; k < SCAN_KEEP; ++k)
+                    x[k] = t0 + k < ntiles ? c[(long)(t0 + k) * nb + b] : 0;
+#pragma unroll
+                for (int k = 0; k < SCAN_KEEP; ++k) tot += x[k];
+            }
+        }
         int group_total;
         const int incl = block_inclusive_scan(tot, wave_sums, &group_total);
-        if (b < nb) {
+        if (own) {
             int run = carry + incl - tot;              // first slot of bucket b
-            for (int t = 0; t < ntiles; ++t) {
-                const int x = c[(long)t * nb + b];
-                c[(long)t * nb + b] = run;
-                run += x;
+            if (ntiles <= SCAN_KEEP) {
+#pragma unroll
+                for (int k = 0; k < SCAN_KEEP; ++k)
+                    if (k < ntiles) {
+                        c[(long)k * nb + b] = run;
+                        run += x[k];
+                    }
+            } else {
+                for (int t0 = 0; t0 < ntiles; t0 += SCAN_KEEP) {
+#pragma unroll
+                    for (int k = 0; k < SCAN_KEEP; ++k)
+                        x[k] = t0 + k < ntiles ? c[(long)(t0 + k) * nb + b] : 0;
+#pragma unroll
+                    for (int k = 0; k < SCAN_KEEP; ++k)
+                        if (t0 + k < ntiles) {
+                            c[(long)(t0 + k) * nb + b] = run;
+                            run += x[k];
+                        }
+                }
             }
         }
         carry += group_total;
@@ -103,7 +154,7 @@ void k_sort_scan(int32_t* __restrict__ counters, int32_t* __restrict__ ranks, in
             const int nz = tot > 0 ? 1 : 0;
             int group_nz;
             const int incl_nz = block_inclusive_scan(nz, wave_sums, &group_nz);
-            if (b < nb) ranks[(long)blockIdx.x * nb + b] = rank_carry + incl_nz - nz;
+            if (own) ranks[(long)blockIdx.x * nb + b] = rank_carry + incl_nz - nz;
             rank_carry += group_nz;
         }
     }
@@ -187,26 +238,392 @@ void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restri
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_sort_colscan: the column half of the scan, for k_sort_place.  One thread per
+// (segment, bucket): counters[seg][tile][b] becomes the number of positions of
+// bucket b in the earlier tiles, and totals[seg][b] the bucket's count.  The
+// offsets along the bucket axis are summed by k_sort_place itself.
+constexpr int COLSCAN_THREADS = 256;
+
+__global__ __launch_bounds__(COLSCAN_THREADS)
+void k_sort_colscan(int32_t* __restrict__ counters, int32_t* __restrict__ totals, int nb, int ntiles,
+                    int blocks_per_seg)
+{
+    const long seg = blockIdx.x / blocks_per_seg;
+    const int b = (blockIdx.x % blocks_per_seg) * COLSCAN_THREADS + threadIdx.x;
+    if (b >= nb) return;
+    int32_t* c = counters + seg * ntiles * (long)nb + b;
+    int run = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += SCAN_KEEP) {
+        int x[SCAN_KEEP];
+#pragma unroll
+        for (int k = 0; k < SCAN_KEEP; ++k) x[k] = c[(long)min(t0 + k, ntiles - 1) * nb];
+#pragma unroll
+        for (int k = 0; k < SCAN_KEEP; ++k)
+            if (t0 + k < ntiles) {
+                c[(long)(t0 + k) * nb] = run;
+                run += x[k];
+            }
+    }
+    totals[seg * nb + b] = run;
+}
+
+// ---------------------------------------------------------------------------
+// k_sort_place: one workgroup per (batch row, head, tile, group of RG rounds),
+// wave w placing round g * RG + w of the tile.  Per wave, in LDS:
+//   cnt[nb]     u32: next tile-local sorted index of each bucket
+//   rep[nb]     u32: the representative lane of each bucket in a ranking step;
+//               after the ranking, dlt[nb]: first slot of (tile, bucket) in
+//               the segment minus its first tile-local index, so that
+//               slot = tile-local index + dlt[bucket]
+//   rk[nb]      u16 (padded to 8 bytes), same-bucket variant only: 2 * rank of
+//               the bucket among the round's non-empty buckets
+//   bt[P]       u16 (padded to 8 bytes): bucket of each tile position, then
+//               its cid value
+//   stg[P]      u16: the tile's positions in sorted order
+//   peer[64]    u64: per representative lane, the lanes of its bucket
+// Every step issues its loads before it uses any of them: with one workgroup
+// per CU and a wave per SIMD nothing else hides their latency.
+constexpr int PLACE_MAX_WAVES = 16;
+constexpr int PLACE_BATCH = 8;              // ranking steps whose LDS atomics are issued together
+constexpr int PLACE_LOADS = 16;             // loads in flight per lane
+
+struct PlaceLayout {                         // offsets in 16-bit units within a wave's region
+    int rep, rk, bt, stg, peer, words;
+};
+
+__host__ __device__ inline PlaceLayout place_layout(int nb, int P, bool same)
+{
+    auto up4 = [](int x) { return (x + 3) & ~3; };
+    PlaceLayout l;
+    l.rep = 2 * nb;                          // u32 per bucket; after the ranking, dlt
+    l.rk = 4 * nb;
+    l.bt = l.rk + (same ? up4(nb) : 0);
+    l.stg = l.bt + up4(P);
+    l.peer = l.stg + up4(P);                 // u64 per lane
+    l.words = (l.peer + 4 * 64) / 2;
+    return l;
+}
+
+// Stores the cid values of a tile's positions for RG rounds: one vector store of
+// the RG u16 values per position (RG = 1, 2, 4, 8), or element by element.
+template <int RGV>
+__device__ __forceinline__ void store_cid_rows(int16_t* __restrict__ cd, const uint16_t* const* bts,
+                                               int np, int n_r, int r0)
+{
+    for (int p = threadIdx.x; p < np; p += blockDim.x) {
+        int16_t* dst = cd + (long)p * n_r + r0;
+        if constexpr (RGV == 1) {
+            dst[0] = (int16_t)bts[0][p];
+        } else if constexpr (RGV == 2) {
+            *reinterpret_cast<uint32_t*>(dst) = bts[0][p] | ((uint32_t)bts[1][p] << 16);
+        } else if constexpr (RGV == 4) {
+            u32x2 v;
+            v.x = bts[0][p] | ((uint32_t)bts[1][p] << 16);
+            v.y = bts[2][p] | ((uint32_t)bts[3][p] << 16);
+            *reinterpret_cast<u32x2*>(dst) = v;
+        } else if constexpr (RGV == 8) {
+            u32x4 v;
+            v.x = bts[0][p] | ((uint32_t)bts[1][p] << 16);
+            v.y = bts[2][p] | ((uint32_t)bts[3][p] << 16);
+            v.z = bts[4][p] | ((uint32_t)bts[5][p] << 16);
+            v.w = bts[6][p] | ((uint32_t)bts[7][p] << 16);
+            *reinterpret_cast<u32x4*>(dst) = v;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t x, int lane, uint32_t* total)
+{
+    uint32_t incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    *total = __shfl(incl, 63);
+    return incl - x;
+}
+
+template <bool SAME>
+__global__ __launch_bounds__(PLACE_MAX_WAVES * 64)
+void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict__ colpre,
+                  const int32_t* __restrict__ totals, int32_t* __restrict__ perm,
+                  int16_t* __restrict__ cid, int L, int nb, int nbits, int P, int ntiles, int n_r,
+                  int RG, int ngroups, long nkeys, int chunk, int chunk_shift)
+{
+    extern __shared__ uint32_t lds[];
+    // all tiles of one (batch row, head, round group) on one XCD (see ScatterMap)
+    const int xcd = blockIdx.x % NXCD;
+    const long j = blockIdx.x / NXCD;
+    const long key = (j / ntiles) * NXCD + xcd;
+    if (key >= nkeys) return;                      // padding of the last row of keys
+    const int t = (int)(j % ntiles);
+    const long bh = key / ngroups;
+    const int r0 = (int)(key % ngroups) * RG;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = r0 + w;
+    const long seg = bh * n_r + r;
+    const int p0 = t * P, np = min(P, L - p0);
+    const PlaceLayout ly = place_layout(nb, P, SAME);
+
+    uint16_t* base16 = reinterpret_cast<uint16_t*>(lds + (long)w * ly.words);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base16);
+    uint32_t* rep = reinterpret_cast<uint32_t*>(base16 + ly.rep);
+    uint32_t* dlt = rep;                           // once the ranking is done
+    uint16_t* rk = base16 + ly.rk;
+    uint16_t* bt = base16 + ly.bt;
+    uint16_t* stg = base16 + ly.stg;
+
+    // 1. the round's buckets of the tile -> bt, and their histogram -> cnt
+    for (int b = lane; b < nb; b += 64) {
+        cnt[b] = 0;
+        rep[b] = 0;
+    }
+    const int32_t* bk = buckets + seg * (long)L + p0;
+    if ((L & 3) == 0) {                            // 16-byte aligned rows: 4 positions per load
+        for (int s = 4 * lane; s < np; s += 4 * 64 * PLACE_LOADS) {
+            int4 v[PLACE_LOADS];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k)
+                v[k] = *reinterpret_cast<const int4*>(bk + min(s + 256 * k, np - 4));   // np % 4 == 0
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) {
+                if (s + 256 * k < np) {
+                    const int e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+                    uint32_t h[2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool ok = (unsigned)e[i] < (unsigned)nb;
+                        const uint32_t u = ok ? (uint32_t)e[i] : 0xFFFFu;
+                        if (i % 2 == 0) h[i / 2] = u; else h[i / 2] |= u << 16;
+                        if (ok) atomicAdd(&cnt[e[i]], 1u);
+                    }
+                    *reinterpret_cast<uint2*>(bt + s + 256 * k) = make_uint2(h[0], h[1]);
+                }
+            }
+        }
+    } else {
+        for (int s = lane; s < np; s += 64 * PLACE_LOADS) {
+            int v[PLACE_LOADS];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) v[k] = bk[min(s + 64 * k, np - 1)];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) {
+                if (s + 64 * k < np) {
+                    const bool ok = (unsigned)v[k] < (unsigned)nb;
+                    bt[s + 64 * k] = ok ? (uint16_t)v[k] : (uint16_t)0xFFFF;
+                    if (ok) atomicAdd(&cnt[v[k]], 1u);
+                }
+            }
+        }
+    }
+    // 2. first tile-local index of each bucket: an exclusive scan of cnt
+    //    (lane l owns buckets [l * per, (l + 1) * per))
+    const int per = (nb + 63) / 64;
+    const int bl0 = min(nb, lane * per), bl1 = min(nb, bl0 + per);
+    uint32_t s_cnt = 0;
+    for (int b = bl0; b < bl1; ++b) s_cnt += cnt[b];
+    uint32_t nvalid_u;
+    uint32_t run_cnt = wave_exclusive_scan(s_cnt, lane, &nvalid_u);
+    const int nvalid = (int)nvalid_u;
+    for (int b = bl0; b < bl1; ++b) {
+        const uint32_t c = cnt[b];
+        cnt[b] = run_cnt;
+        run_cnt += c;
+    }
+    // 3. rank the positions in increasing order.  Inside one step of 64
+    //    positions the lanes of one bucket agree on a representative (the
+    //    highest of their lane ids, an LDS max of (step + 1) * 64 + lane, above
+    //    every earlier step's value), set their bits in its word of peer[] and
+    //    read the word back: the lanes of equal bucket.  Across steps the
+    //    per-bucket counters keep the order: one LDS add-and-return by the
+    //    representative.  LDS operations of one wave execute in program order,
+    //    so a batch of steps is issued before its results are waited for.
+    unsigned long long* peer = reinterpret_cast<unsigned long long*>(base16 + ly.peer);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    // Full batches run without per-position guards (a guarded LDS read becomes a
+    // branch with a wait around it); the last, partial batch is guarded.
+    auto rank_batch = [&](int s0, auto tail) __attribute__((always_inline)) {
+        constexpr bool TAIL = decltype(tail)::value;
+        int bb[PLACE_BATCH], rp[PLACE_BATCH], rnk[PLACE_BATCH], cntp[PLACE_BATCH];
+        uint64_t pw[PLACE_BATCH];
+        uint32_t base[PLACE_BATCH];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            const int p = s0 + 64 * k + lane;
+            const int b = (int)bt[TAIL ? min(p, P - 1) : p];
+            bb[k] = (!TAIL || p < np) && b < nb ? b : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            if (bb[k] >= 0) atomicMax(&rep[bb[k]], ((uint32_t)(s0 / 64 + k + 1) << 6) | (uint32_t)lane);
+            rp[k] = (int)(rep[bb[k] >= 0 ? bb[k] : 0] & 63u);
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            if (bb[k] >= 0 && rp[k] == lane) peer[lane] = 0ull;
+            if (bb[k] >= 0) atomicOr(&peer[rp[k]], 1ull << lane);
+            pw[k] = peer[rp[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            rnk[k] = __popcll(pw[k] & below);
+            cntp[k] = __popcll(pw[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            base[k] = 0;
+            if (bb[k] >= 0 && lane == rp[k]) base[k] = atomicAdd(&cnt[bb[k]], (uint32_t)cntp[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            const uint32_t b0 = __shfl(base[k], rp[k]);
+            if (bb[k] >= 0) stg[b0 + rnk[k]] = (uint16_t)(s0 + 64 * k + lane);
+        }
+    };
+    int s0 = 0;
+    for (; s0 + 64 * PLACE_BATCH <= np; s0 += 64 * PLACE_BATCH) rank_batch(s0, std::false_type{});
+    if (s0 < np) rank_batch(s0, std::true_type{});
+
+    // 2b. slot of each (tile, bucket) = (all positions of smaller buckets: a
+    //     scan of the totals) + (the bucket in earlier tiles: colpre), stored
+    //     as dlt = slot - first tile-local index.  After the ranking cnt[b] is
+    //     the first index of bucket b + 1, so that of b is cnt[b - 1].
+    {
+        const int32_t* tot = totals + seg * (long)nb;
+        const int32_t* cp = colpre + (seg * ntiles + t) * (long)nb;
+        uint32_t s_tot = 0, s_nz = 0;
+        for (int b0 = bl0; b0 < bl1; b0 += PLACE_LOADS) {
+            int x[PLACE_LOADS];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) x[k] = tot[min(b0 + k, bl1 - 1)];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) {
+                if (b0 + k < bl1) {
+                    s_tot += (uint32_t)x[k];
+                    s_nz += x[k] > 0 ? 1u : 0u;
+                    dlt[b0 + k] = (uint32_t)x[k];          // the bucket's total, for now
+                }
+            }
+        }
+        uint32_t dummy;
+        uint32_t run_tot = wave_exclusive_scan(s_tot, lane, &dummy);
+        uint32_t run_nz = SAME ? wave_exclusive_scan(s_nz, lane, &dummy) : 0u;
+        for (int b0 = bl0; b0 < bl1; b0 += PLACE_LOADS) {
+            int x[PLACE_LOADS];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) x[k] = cp[min(b0 + k, bl1 - 1)];
+#pragma unroll
+            for (int k = 0; k < PLACE_LOADS; ++k) {
+                if (b0 + k < bl1) {
+                    const int b = b0 + k;
+                    const uint32_t total = dlt[b];
+                    const uint32_t first = b > 0 ? cnt[b - 1] : 0u;
+                    dlt[b] = run_tot + (uint32_t)x[k] - first;
+                    if constexpr (SAME) {
+                        rk[b] = (uint16_t)(2 * run_nz);
+                        run_nz += total > 0 ? 1u : 0u;
+                    }
+                    run_tot += total;
+                }
+            }
+        }
+    }
+
+    // 4. perm in sorted order (each bucket's run of slots is contiguous); the
+    //    position's cid value replaces its bucket in bt (each position once, so
+    //    the reads of a batch never meet its writes)
+    int32_t* pm = perm + seg * (long)L;
+    auto write_batch = [&](int i0, auto tail) __attribute__((always_inline)) {
+        constexpr bool TAIL = decltype(tail)::value;
+        int p[PLACE_BATCH], b[PLACE_BATCH];
+        uint32_t dl[PLACE_BATCH], id[PLACE_BATCH];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k)
+            p[k] = TAIL ? min((int)stg[min(i0 + 64 * k, P - 1)], P - 1) : (int)stg[i0 + 64 * k];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) b[k] = bt[p[k]];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) dl[k] = dlt[TAIL ? (b[k] < nb ? b[k] : 0) : b[k]];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            const uint32_t slot = (uint32_t)(i0 + 64 * k) + dl[k];
+            id[k] = chunk_shift >= 0 ? slot >> chunk_shift : slot / (uint32_t)chunk;
+            if constexpr (SAME) id[k] += rk[TAIL ? (b[k] < nb ? b[k] : 0) : b[k]];
+            // in range unless the input changed under the sort
+            if ((!TAIL || i0 + 64 * k < nvalid) && slot < (uint32_t)L) pm[slot] = p0 + p[k];
+        }
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k)
+            if (!TAIL || i0 + 64 * k < nvalid) bt[p[k]] = (uint16_t)id[k];
+    };
+    int i0 = 0;
+    for (; i0 + 64 * PLACE_BATCH <= nvalid; i0 += 64 * PLACE_BATCH) write_batch(i0 + lane, std::false_type{});
+    if (i0 < nvalid) write_batch(i0 + lane, std::true_type{});
+    __syncthreads();
+    // 5. the tile's cid rows for the group's rounds
+    const uint16_t* bts[PLACE_MAX_WAVES];
+#pragma unroll
+    for (int k = 0; k < PLACE_MAX_WAVES; ++k)
+        bts[k] = reinterpret_cast<const uint16_t*>(lds + (long)k * ly.words) + ly.bt;
+    int16_t* cd = cid + (bh * (long)L + p0) * n_r;
+    switch (RG) {
+        case 1: store_cid_rows<1>(cd, bts, np, n_r, r0); break;
+        case 2: store_cid_rows<2>(cd, bts, np, n_r, r0); break;
+        case 4: store_cid_rows<4>(cd, bts, np, n_r, r0); break;
+        case 8: store_cid_rows<8>(cd, bts, np, n_r, r0); break;
+        default:
+            for (int e = threadIdx.x; e < np * RG; e += blockDim.x) {
+                const int p = e / RG, k = e - p * RG;
+                cd[(long)p * n_r + r0 + k] = (int16_t)bts[k][p];
+            }
+    }
+}
+
+// Rounds per k_sort_place workgroup: the largest divisor of n_rounds (at most
+// PLACE_MAX_WAVES) whose waves' LDS fits; 0 if not even one round fits, or if
+// tile positions do not fit in 16 bits (then k_sort_scatter is used).
+constexpr size_t PLACE_LDS_LIMIT = 160 * 1024;
+
+int place_rounds_per_group(int nb, int P, int n_r, bool same)
+{
+    if (P > 65536) return 0;
+    const size_t per = (size_t)place_layout(nb, P, same).words * 4;
+    int best = 0;
+    for (int rg = 1; rg <= n_r && rg <= PLACE_MAX_WAVES; ++rg)
+        if (n_r % rg == 0 && rg * per <= PLACE_LDS_LIMIT) best = rg;
+    return best;
+}
+
 }  // namespace
 
-SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets)
+SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket)
 {
-    // Tiles hold at least 4 positions per bucket so that the counters stay a
-    // fraction of the keys; at least 2048 and at most 65536 positions.
-    long tile = 2048;
-    while (tile < 4L * n_buckets && tile < 65536) tile <<= 1;
-    if (tile > L) tile = L;
+    // k_sort_place: tiles of at least 2 positions per bucket (and at least 2048),
+    // so that every round of a workgroup fits in LDS; k_sort_scatter: at least 4
+    // per bucket, so that the counters stay a fraction of the keys.  At most
+    // 65536 positions and at most L.
+    auto tile_for = [&](long per_bucket) {
+        long tile = 2048;
+        while (tile < per_bucket * n_buckets && tile < 65536) tile <<= 1;
+        return tile > L ? (long)L : tile;
+    };
     SortPlan p;
+    long tile = tile_for(2);
+    p.rounds_per_group = place_rounds_per_group(n_buckets, (int)tile, n_rounds, same_bucket);
+    if (p.rounds_per_group == 0) tile = tile_for(4);
     p.tile = (int)tile;
     p.ntiles = (int)((L + tile - 1) / tile);
     p.nseg = bh * n_rounds;
     p.counters = (size_t)p.nseg * p.ntiles * n_buckets;
+    p.extra = (size_t)p.nseg * n_buckets;
     return p;
 }
 
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
-                       int32_t* ranks, const SortPlan& plan, long bh, int L, int n_rounds,
-                       int n_buckets, int chunk, hipStream_t s)
+                       int32_t* extra, bool same_bucket, const SortPlan& plan, long bh, int L,
+                       int n_rounds, int n_buckets, int chunk, hipStream_t s)
 {
     const size_t lds = (size_t)n_buckets * sizeof(int);
     // Up to 32768 buckets need 128 KiB of dynamic LDS per workgroup.
@@ -216,12 +633,38 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * sizeof(int));
         (void)hipFuncSetAttribute((const void*)k_sort_scatter,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * sizeof(int));
+        (void)hipFuncSetAttribute((const void*)k_sort_place<false>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE_LDS_LIMIT);
+        (void)hipFuncSetAttribute((const void*)k_sort_place<true>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE_LDS_LIMIT);
     });
     int nbits = 0;
     while ((1 << nbits) < n_buckets) ++nbits;
     const unsigned blocks = (unsigned)(plan.nseg * plan.ntiles);
     hipLaunchKernelGGL(k_sort_hist, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters, L,
                        n_buckets, plan.tile, plan.ntiles);
+    const int rg = plan.rounds_per_group;
+    if (rg > 0) {
+        const int bps = (n_buckets + COLSCAN_THREADS - 1) / COLSCAN_THREADS;
+        hipLaunchKernelGGL(k_sort_colscan, dim3((unsigned)(plan.nseg * bps)), dim3(COLSCAN_THREADS), 0, s,
+                           counters, extra, n_buckets, plan.ntiles, bps);
+        const int ngroups = n_rounds / rg;
+        const long nkeys = bh * ngroups;
+        const long rows = (nkeys + NXCD - 1) / NXCD;
+        const unsigned pblocks = (unsigned)(rows * NXCD * plan.ntiles);
+        const size_t plds = (size_t)rg * place_layout(n_buckets, plan.tile, same_bucket).words * 4;
+        const int shift = (chunk & (chunk - 1)) == 0 ? __builtin_ctz((unsigned)chunk) : -1;
+        if (same_bucket)
+            hipLaunchKernelGGL(k_sort_place<true>, dim3(pblocks), dim3(64 * rg), plds, s, buckets,
+                               counters, extra, perm, cid, L, n_buckets, nbits, plan.tile,
+                               plan.ntiles, n_rounds, rg, ngroups, nkeys, chunk, shift);
+        else
+            hipLaunchKernelGGL(k_sort_place<false>, dim3(pblocks), dim3(64 * rg), plds, s, buckets,
+                               counters, extra, perm, cid, L, n_buckets, nbits, plan.tile,
+                               plan.ntiles, n_rounds, rg, ngroups, nkeys, chunk, shift);
+        return hipGetLastError();
+    }
+    int32_t* ranks = same_bucket ? extra : nullptr;
     hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)plan.nseg), dim3(SCAN_THREADS), 0, s, counters,
                        ranks, n_buckets, plan.ntiles);
     ScatterMap map;

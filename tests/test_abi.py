@@ -255,20 +255,20 @@ def test_ffn_checks(lib):
 
 
 def test_sort_workspace(lib):
-    # tile = smallest power of two >= max(2048, 4 * n_buckets), at most 65536, at most L;
-    # one int32 counter per (segment, tile, bucket)
+    # tile = smallest power of two >= max(2048, 2 * n_buckets) where a workgroup's
+    # rounds fit in LDS, else >= max(2048, 4 * n_buckets); at most 65536, at most L.
+    # One int32 counter per (segment, tile, bucket).
     cases = [(dict(), 1 * 8 * 2 * 2 * 64),
-             (dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8), 8 * 8 * 16 * 1024),
+             (dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8), 8 * 8 * 32 * 1024),
              (dict(seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128), 8 * 4 * 16 * 16384),
              (dict(seq_len=1024, n_buckets=32, n_rounds=1, heads=1), 1 * 1 * 1 * 32)]
-    for kw, counters in cases:
-        c = cfg(**kw)
-        assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * counters, kw
-    # same-bucket variant: plus one int32 rank per (segment, bucket)
-    for kw, counters in cases:
-        c = cfg(flags=B.LSH_FLAG_SAME_BUCKET, **kw)
-        nseg = c.batch * c.heads * c.n_rounds
-        assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * (counters + nseg * c.n_buckets), kw
+    # plus one int32 per (segment, bucket): the bucket totals (or, with the
+    # same-bucket variant, possibly its bucket ranks)
+    for flags in (0, B.LSH_FLAG_SAME_BUCKET):
+        for kw, counters in cases:
+            c = cfg(flags=flags, **kw)
+            nseg = c.batch * c.heads * c.n_rounds
+            assert lib.lsh_sort_workspace_bytes(raw(c)) == 4 * (counters + nseg * c.n_buckets), kw
     for flags in (0, B.LSH_FLAG_SAME_BUCKET):
         c = cfg(flags=flags)
         need = lib.lsh_sort_workspace_bytes(raw(c))
@@ -289,3 +289,18 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/liblsh_attention.so")
     with pytest.raises(RuntimeError, match="missing"):
         B.load_library()
+
+
+def test_header_is_plain_c_with_hip_streams():
+    """The header compiles as C99 host code, and every stream is a hipStream_t."""
+    import shutil
+    import subprocess
+    text = open(HEADER).read()
+    assert "void* stream" not in text
+    assert len(re.findall(r"hipStream_t stream\)", text)) >= 9
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("gcc or the ROCm headers are not installed")
+    subprocess.run([gcc, "-x", "c", "-std=c99", "-fsyntax-only", "-Wall", "-Werror",
+                    "-D__HIP_PLATFORM_AMD__", "-I" + rocm_inc, HEADER], check=True)
