@@ -146,6 +146,23 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
                     int16_t* cid, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Step 2 without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same inputs, outputs and results as lsh_sort; the
+ * counters live in a static device array of LSH_SORT_NOALLOC_MAX_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's array, so calls
+ * whose executions overlap on one GPU (different streams, or several host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  Errors as lsh_sort, and LSH_ERR_WORKSPACE when the configuration
+ * needs more than LSH_SORT_NOALLOC_MAX_BYTES (lsh_sort_workspace_bytes(cfg)
+ * tells how much).
+ */
+#define LSH_SORT_NOALLOC_MAX_BYTES (64u << 20)
+lsh_status lsh_sort_noalloc(const lsh_config* cfg, const int32_t* buckets, int32_t* perm,
+                            int16_t* cid, hipStream_t stream);
+
+/*
  * Step 3 — chunked attention, one output per round.  [AIS] formula and LSH
  * section; [ULT]; [MOD] "LSH attention".
  *   In round r, the query at sorted slot s (chunk k = s / c) attends to the keys

@@ -15,4 +15,5 @@ from ._binding import (EXPORTED, LIB_PATH, LSH_BF16, LSH_ERR_HIP, LSH_ERR_INVALI
                        lsh_project_out_add,
                        lsh_attn_backward, lsh_backward_workspace_bytes, lsh_chunk_attn,
                        lsh_combine_rounds, lsh_hash, lsh_project_in, lsh_project_out, lsh_sort,
-                       lsh_sort_workspace_bytes, sort_workspace)
+                       lsh_sort_noalloc, lsh_sort_workspace_bytes, sort_workspace,
+                       SORT_NOALLOC_MAX_BYTES)

@@ -25,7 +25,7 @@ LSH_F32, LSH_BF16 = 0, 1
 # variant flags of lsh_config.flags (see include/lsh_attention.h)
 LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2, 4
 
-EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_chunk_attn",
+EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_sort_noalloc", "lsh_chunk_attn",
             "lsh_combine_rounds", "lsh_backward_workspace_bytes", "lsh_attn_backward",
             "lsh_project_in", "lsh_project_out", "lsh_project_out_add", "lsh_ffn_workspace_bytes",
             "lsh_ffn", "lsh_status_string", "lsh_last_error")
@@ -92,6 +92,7 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_sort_workspace_bytes.argtypes = [CP]
     lib.lsh_sort_workspace_bytes.restype = ctypes.c_size_t
     lib.lsh_sort.argtypes = [CP, P, P, P, P, ctypes.c_size_t, P]
+    lib.lsh_sort_noalloc.argtypes = [CP, P, P, P, P]
     lib.lsh_chunk_attn.argtypes = [CP, P, P, P, P, P, P, P]
     lib.lsh_combine_rounds.argtypes = [CP, P, P, P, P]
     lib.lsh_backward_workspace_bytes.argtypes = [CP]
@@ -104,7 +105,7 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_ffn_workspace_bytes.restype = ctypes.c_size_t
     lib.lsh_ffn.argtypes = [ctypes.c_int64, I32, I32, I32, P, P, P, P, P, P, ctypes.c_float, P, P,
                             ctypes.c_size_t, P]
-    for f in ("lsh_hash", "lsh_sort", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_attn_backward",
+    for f in ("lsh_hash", "lsh_sort", "lsh_sort_noalloc", "lsh_chunk_attn", "lsh_combine_rounds", "lsh_attn_backward",
               "lsh_project_in", "lsh_project_out", "lsh_project_out_add", "lsh_ffn"):
         getattr(lib, f).restype = I32
     lib.lsh_status_string.argtypes = [I32]
@@ -201,6 +202,32 @@ def lsh_sort(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor]
     c = cfg.to_c()
     _check(lib.lsh_sort(ctypes.byref(c), _ptr(buckets), _ptr(perm), _ptr(cid), _ptr(workspace),
                         ctypes.c_size_t(nbytes), _stream(dev, stream)), "lsh_sort")
+    return perm, cid
+
+
+# bytes of the static scratch array behind lsh_sort_noalloc (the header's
+# LSH_SORT_NOALLOC_MAX_BYTES)
+SORT_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def lsh_sort_noalloc(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor] = None,
+                     cid: Optional[torch.Tensor] = None, stream=None):
+    """Step 2 with the library's static scratch instead of a workspace (see
+    lsh_sort_noalloc in the header): (perm, cid).  Calls that overlap on one GPU
+    share that scratch and race."""
+    lib = load_library()
+    sh = _shapes(cfg)
+    _expect(buckets, "buckets", sh["buckets"], torch.int32)
+    dev = buckets.device
+    if perm is None:
+        perm = torch.empty(sh["perm"], dtype=torch.int32, device=dev)
+    if cid is None:
+        cid = torch.empty(sh["cid"], dtype=torch.int16, device=dev)
+    _expect(perm, "perm", sh["perm"], torch.int32, dev)
+    _expect(cid, "cid", sh["cid"], torch.int16, dev)
+    c = cfg.to_c()
+    _check(lib.lsh_sort_noalloc(ctypes.byref(c), _ptr(buckets), _ptr(perm), _ptr(cid),
+                                _stream(dev, stream)), "lsh_sort_noalloc")
     return perm, cid
 
 

@@ -203,6 +203,32 @@ lsh_status lsh_sort(const lsh_config* cfg, const int32_t* buckets, int32_t* perm
                       "lsh_sort");
 }
 
+lsh_status lsh_sort_noalloc(const lsh_config* cfg, const int32_t* buckets, int32_t* perm,
+                            int16_t* cid, hipStream_t stream)
+{
+    LSH_TRY(check_config(cfg));
+    LSH_TRY(check_ptr(buckets, "buckets"));
+    LSH_TRY(check_ptr(perm, "perm"));
+    LSH_TRY(check_ptr(cid, "cid"));
+    const bool same = (cfg->flags & LSH_FLAG_SAME_BUCKET) != 0;
+    const lshk::SortPlan p = lshk::sort_plan(bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets, same);
+    const size_t need = sort_ws_bytes(p);
+    if (need > (size_t)LSH_SORT_NOALLOC_MAX_BYTES) {
+        g_last_error = "lsh_sort_noalloc: this configuration needs " + std::to_string(need) +
+                       " bytes of scratch, the static buffer holds " +
+                       std::to_string((size_t)LSH_SORT_NOALLOC_MAX_BYTES) +
+                       " (use lsh_sort with a workspace)";
+        return LSH_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    LSH_TRY(hip_status(lshk::sort_scratch(&ws), "lsh_sort_noalloc"));
+    int32_t* counters = static_cast<int32_t*>(ws);
+    return hip_status(lshk::launch_sort(buckets, perm, cid, counters, counters + p.counters, same, p,
+                                        bh_of(cfg), cfg->seq_len, cfg->n_rounds, cfg->n_buckets,
+                                        cfg->chunk, stream),
+                      "lsh_sort_noalloc");
+}
+
 lsh_status lsh_chunk_attn(const lsh_config* cfg, const void* qk, const void* v, const int32_t* perm,
                           const int16_t* cid, void* o_rounds, float* lse, hipStream_t stream)
 {

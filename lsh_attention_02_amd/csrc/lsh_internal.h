@@ -26,6 +26,10 @@ struct SortPlan {
 };
 SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket);
 
+// Device address of the static scratch array of lsh_sort_noalloc on the
+// current device (LSH_SORT_NOALLOC_MAX_BYTES), looked up on first use per device.
+hipError_t sort_scratch(void** ptr);
+
 // counters, extra: the two workspace parts of SortPlan (int32 each).
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
                        int32_t* extra, bool same_bucket, const SortPlan& plan, long bh, int L,

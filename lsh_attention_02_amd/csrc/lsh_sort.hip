@@ -32,6 +32,7 @@
 // stride) cost about one request per element each, and the L2's request rate,
 // not HBM, bounded the sort.  In tile order a wave's 64 perm stores fall in a
 // few runs, and the cid rows of a tile form one contiguous block.
+#include "lsh_attention.h"
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
@@ -597,6 +598,32 @@ int place_rounds_per_group(int nb, int P, int n_r, bool same)
 }
 
 }  // namespace
+
+// The workspace of lsh_sort_noalloc: a static device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): sort_scratch() looks up its device address once per device.
+static __device__ __align__(256) int32_t scratch[LSH_SORT_NOALLOC_MAX_BYTES / sizeof(int32_t)];
+
+hipError_t sort_scratch(void** ptr)
+{
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEVICES] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket)
 {

@@ -106,6 +106,7 @@ def test_bad_config_every_call(lib, kw, status, msg):
     calls = [
         lambda: lib.lsh_hash(raw(c), FAKE, FAKE, FAKE, NULL),
         lambda: lib.lsh_sort(raw(c), FAKE, FAKE, FAKE, FAKE, 1 << 40, NULL),
+        lambda: lib.lsh_sort_noalloc(raw(c), FAKE, FAKE, FAKE, NULL),
         lambda: lib.lsh_chunk_attn(raw(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL),
         lambda: lib.lsh_combine_rounds(raw(c), FAKE, FAKE, FAKE, NULL),
         lambda: lib.lsh_attn_backward(raw(c), *[FAKE] * 10, 1 << 40, NULL),
@@ -304,3 +305,25 @@ def test_header_is_plain_c_with_hip_streams():
         pytest.skip("gcc or the ROCm headers are not installed")
     subprocess.run([gcc, "-x", "c", "-std=c99", "-fsyntax-only", "-Wall", "-Werror",
                     "-D__HIP_PLATFORM_AMD__", "-I" + rocm_inc, HEADER], check=True)
+
+
+def test_sort_noalloc_checks(lib):
+    """The entry point without a workspace checks its pointers, and rejects a
+    configuration whose counters exceed the static scratch buffer, before any
+    HIP call."""
+    c = cfg()
+    for which in range(3):
+        for bad in (NULL, MISALIGNED):
+            args = [FAKE] * 3
+            args[which] = bad
+            assert lib.lsh_sort_noalloc(raw(c), *args, NULL) == B.LSH_ERR_INVALID_ARG
+    text = open(HEADER).read()
+    m = re.search(r"#define LSH_SORT_NOALLOC_MAX_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.SORT_NOALLOC_MAX_BYTES
+    big = cfg(heads=64, seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128)
+    assert lib.lsh_sort_workspace_bytes(raw(big)) > B.SORT_NOALLOC_MAX_BYTES
+    assert lib.lsh_sort_noalloc(raw(big), FAKE, FAKE, FAKE, NULL) == B.LSH_ERR_WORKSPACE
+    assert "static buffer" in lib.lsh_last_error().decode()
+    # the 1M-token workload fits
+    long_1m = cfg(seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128)
+    assert lib.lsh_sort_workspace_bytes(raw(long_1m)) <= B.SORT_NOALLOC_MAX_BYTES
