@@ -184,8 +184,8 @@ def traffic_for(name, workload):
         return None
     with open(PMC_TRAFFIC) as f:
         rec = json.load(f)
-    ent = rec.get("kernels", {}).get(name)
-    if not ent or ent.get("workload") != workload or ent.get("source_sha256") != source_sha(name):
+    ent = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(name)
+    if not ent or ent.get("source_sha256") != source_sha(name):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -295,7 +295,7 @@ def pmc_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
 
         def per_launch(table):
             # Launch count = dispatches of the call's first kernel; the sort's
-            # three kernels add up to one call.
+            # kernels add up to one call.
             hits = {k: v for k, v in table.items()
                     if re.search(r"::" + re.escape(prefix) + r"\w*[<(]", k)}
             if not hits:
@@ -303,23 +303,65 @@ def pmc_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
             launches = max(len(v) for v in hits.values())
             return sum(sum(v) for v in hits.values()) / launches
         f_kib, w_kib = per_launch(fetch), per_launch(write)
-        if f_kib is None or w_kib is None:
+        if f_kib is None or w_kib is None or name not in work:
             continue
         hbm = 1024.0 * (f_kib * ff + w_kib * wf)
         kernels[name] = {
-            "workload": workload, "source_sha256": source_sha(name),
+            "source_sha256": source_sha(name),
             "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
             "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": work[name]["bytes"],
             "traffic_over_algorithmic": round(hbm / work[name]["bytes"], 3),
         }
-    rec = {"fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
-           "calibration": "1 GiB device copy (bench.py --copy-calibration), counter read "
-                          "per copyBuffer dispatch",
-           "commands": commands, "kernels": kernels}
+    rec = {}
+    if os.path.exists(PMC_TRAFFIC):
+        with open(PMC_TRAFFIC) as f:
+            rec = json.load(f)
+        if "workloads" not in rec:          # an older single-workload record
+            rec = {}
+    rec.update({"fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                "calibration": "1 GiB device copy (bench.py --copy-calibration), counter read "
+                               "per copyBuffer dispatch"})
+    rec.setdefault("workloads", {})[workload] = {"commands": commands, "kernels": kernels}
     with open(PMC_TRAFFIC, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps(rec, indent=1))
+    print(json.dumps(rec["workloads"][workload], indent=1))
+
+
+def trace_summary(workload, stats_csv, bench_log, command, out_md):
+    """A rocprofv3 --kernel-trace --stats summary (the library's kernels) next to
+    the per-call event times the same bench run printed, as a short Markdown file."""
+    import csv
+    from synthetic_inputs import WORKLOADS
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "lshk::" in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    w = WORKLOADS[workload]
+    line = [l for l in open(bench_log) if l.startswith("{")][-1]
+    res = json.loads(line)
+    out = [f"# Kernel trace summary: forward pass, {workload} workload", "",
+           f"Workload {workload}: {w.description} (synthetic, seed {w.seed}).", "",
+           "Command (repository root, MI355X):", "",
+           "    cd /root/repo && export TMPDIR=/tmp", f"    {command}", "",
+           "Library kernels only (torch kernels of the input upload omitted); averages over every "
+           "launch of the run, warm-up included.", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share of library GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("lshk::", "")
+        name = re.sub(r"\(.*", "", name).replace("void ", "").replace("attn::", "")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    out += ["", "Per-call averages the same run printed (HIP events on the launch stream, timed "
+                "steps only), with each call's fraction of the MFMA and HBM peaks:", "",
+            "| call | ms | MFMA fraction | HBM fraction |", "|---|---|---|---|"]
+    for n, e in res["kernels"].items():
+        out.append(f"| {n} | {e['ms']:.4f} | {e['mfma_frac']:.3f} | {e['hbm_frac']:.3f} |")
+    out += ["", f"bench.py ms_per_step in this run: {res['ms_per_step']} "
+                f"({res['value'] / 1e6:.1f} M tokens/s)", ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
 
 
 def copy_calibration():
@@ -366,10 +408,20 @@ def main():
     ap.add_argument("--layer", type=int, default=0, metavar="D_MODEL",
                     help="time the attention layer (projections included) at this model width")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write profiles/forward_<workload>_kernel_stats.md from a rocprofv3 "
+                         "--kernel-trace --stats run of this benchmark (no GPU needed)")
     ap.add_argument("--pmc-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/pmc_traffic.json from rocprofv3 --pmc output folders")
     args = ap.parse_args()
+    if args.trace_summary:
+        stats, blog = args.trace_summary
+        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_{args.workload} "
+               f"-o run -- python bench.py --no-cpu-baseline --workload {args.workload}")
+        trace_summary(args.workload, stats, blog, cmd,
+                      os.path.join(ROOT, "profiles", f"forward_{args.workload}_kernel_stats.md"))
+        return
     if args.pmc_summary:
         fd, wd, cfd, cwd = args.pmc_summary
         cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python bench.py "
