@@ -305,6 +305,7 @@ constexpr int TR_ROWB = TR_COLS * 2;             // bytes per staged row
 __device__ __forceinline__ int tr_piece(int p, int d) { return p ^ (4 * (d & 3)); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf16x4 tr_read(const char* p)
 {
@@ -421,6 +422,32 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
             keep[u] = up ? ac[u] : keep[u];
         }
     };
+    // d 64: the same in two steps.  tile_max runs under the MFMAs; record is
+    // a branch, so that lanes without a new record (and waves where no lane
+    // has one, most late tiles of a long round) skip the copy, which moves
+    // 64-bit register pairs.  The moves are written as asm: the compiler
+    // would otherwise turn the branch back into one select per value.
+    auto tile_max = [&](const f32x16& ac) __attribute__((always_inline)) {
+        float m = fabsf(ac[0]);
+#pragma unroll
+        for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(ac[j]));
+        return m;
+    };
+    auto record = [&](int u, float m, const f32x16& ac, int tile) __attribute__((always_inline)) {
+        if (m > bmag[u]) {
+            bmag[u] = m;
+            btile[u] = tile;
+            const u64x8 src = __builtin_bit_cast(u64x8, ac);
+            u64x8 dst;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint64_t t;
+                asm volatile("v_mov_b64 %0, %1" : "=v"(t) : "v"(src[i]));
+                dst[i] = t;
+            }
+            keep[u] = __builtin_bit_cast(f32x16, dst);
+        }
+    };
     // end of round r: first kept entry with the record magnitude (one always
     // matches), then the better of the two lanes that hold the token
     auto resolve = [&](int r) __attribute__((always_inline)) {
@@ -446,28 +473,34 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         }
     };
 
-    // PIPE (d 128): software pipeline over column tiles.  The MFMAs of tile t
-    // go into accumulator set t % 2 while the scan of tile t - 1 reads the
-    // other set, about three VALU instructions per MFMA, and the operands of
-    // tile t + 1 are read into the operand registers that each MFMA pair
-    // frees.  A wave's own scan and LDS reads thus run under its matrix
-    // instructions instead of waiting for the other wave of its SIMD (the
-    // group barriers keep the two in phase).  The last tile of a group is
-    // scanned under the first tile of the next group, and a round is resolved
-    // after the scan of its last tile.  All four tiles of a group are
-    // computed: staged columns past ncol hold zeros, whose projections are
-    // exactly 0 and never beat a record.  At d 64 the second accumulator set
-    // would cost the third wave per SIMD, so each tile is scanned right after
-    // its own MFMAs.
+    // d 128: software pipeline over column tiles.  The MFMAs of tile t go
+    // into accumulator set t % 2 while the scan of tile t - 1 reads the other
+    // set, about three VALU instructions per MFMA, and the operands of tile
+    // t + 1 are read into the operand registers that each MFMA pair frees.  A
+    // wave's own scan and LDS reads thus run under its matrix instructions
+    // instead of waiting for the other wave of its SIMD (the group barriers
+    // keep the two in phase).  The last tile of a group is scanned under the
+    // first tile of the next group, and a round is resolved after the scan of
+    // its last tile.  All four tiles of a group are computed: staged columns
+    // past ncol hold zeros, whose projections are exactly 0 and never beat a
+    // record.
+    //
+    // d 64: a second accumulator set would cost the third wave per SIMD, so
+    // the pipeline runs over the two token tiles instead: the MFMAs of token
+    // tile 0 run under the scan of token tile 1 of the previous column tile,
+    // and those of token tile 1 under the scan of token tile 0 of this column
+    // tile.  The operands of the next column tile of the group are read into a
+    // second operand set at the start of each tile.
     constexpr bool PIPE = hash_pipe<D>();
-    f32x16 acc[PIPE ? 2 : 1][HASH_NT];
-    if constexpr (PIPE) {
+    f32x16 acc[2][HASH_NT];                // d 64: acc[0] only
 #pragma unroll
-        for (int u = 0; u < HASH_NT; ++u) acc[1][u] = f32x16{};
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) acc[s][u] = f32x16{};
     }
     reset();
-    int ptile = 0, pr = 0;                 // previous group's last tile and round (PIPE)
-    bool pend = false;                     // previous group ended its round (PIPE)
+    int ptile = 0, pr = 0;                 // previous group's last tile and round
+    bool pend = false;                     // previous group ended its round
 
     auto group = [&](int g, const char* buf, char* nbuf) __attribute__((always_inline)) {
         int r, c0;
@@ -476,10 +509,6 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
         tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
         const int tbase = c0 >> 5;
-        if constexpr (!PIPE) {
-            if (c0 == 0) reset();
-        }
-        const int tiles = PIPE ? TR_TILES : min(TR_TILES, (ncol - c0 + 31) >> 5);
         typename M::Frag a[NKS];
         auto read_tile = [&](int ct, int ks) __attribute__((always_inline)) {
             const char* p = buf + toff[ct] + 16 * ks * TR_ROWB;
@@ -488,69 +517,135 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         };
 #pragma unroll
         for (int ct = 0; ct < TR_TILES; ++ct) {
-            if (ct < tiles) {
-                // operands: all at once, or (PIPE) for tile 0 only, the
-                // others being read under the previous tile's MFMAs
-                if (!PIPE || ct == 0) {
+            // operands of tile 0; the others are read under the previous
+            // tile's MFMAs
+            if (ct == 0) {
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) read_tile(ct, ks);
+                for (int ks = 0; ks < NKS; ++ks) read_tile(ct, ks);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 (&ac)[HASH_NT] = acc[ct & 1];
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u) ac[u] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) ac[u] = M::mma(a[ks], bq[u][ks], ac[u]);
+                if (ct + 1 < TR_TILES) read_tile(ct + 1, ks);   // into a[ks], now free
+            }
+            scan(acc[(ct + 1) & 1], ct == 0 ? ptile : tbase + ct - 1);
+            // an IR-level scheduler would otherwise sink the scans of a group
+            // below all of its MFMAs
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u)
+                asm volatile("" :: "v"(bmag[u]), "v"(btile[u]), "v"(keep[u]));
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) {
+#pragma unroll
+                for (int u = 0; u < HASH_NT; ++u) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                f32x16 (&ac)[HASH_NT] = acc[PIPE ? ct & 1 : 0];
-#pragma unroll
-                for (int u = 0; u < HASH_NT; ++u) ac[u] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-                    for (int u = 0; u < HASH_NT; ++u) ac[u] = M::mma(a[ks], bq[u][ks], ac[u]);
-                    if (PIPE && ct + 1 < TR_TILES) read_tile(ct + 1, ks);   // into a[ks], now free
-                }
-                if constexpr (PIPE) {
-                    scan(acc[(ct + 1) & 1], ct == 0 ? ptile : tbase + ct - 1);
-                    // an IR-level scheduler would otherwise sink the scans of
-                    // a group below all of its MFMAs
-#pragma unroll
-                    for (int u = 0; u < HASH_NT; ++u)
-                        asm volatile("" :: "v"(bmag[u]), "v"(btile[u]), "v"(keep[u]));
-#pragma unroll
-                    for (int i = 0; i < NKS; ++i) {
-#pragma unroll
-                        for (int u = 0; u < HASH_NT; ++u) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-                            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU
-                        }
-                        if (ct + 1 < TR_TILES)
-                            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (ct == 0) {
-                        if (pend) resolve(pr);
-                        if (c0 == 0) reset();
-                    }
-                } else {
-                    scan(ac, tbase + ct);
-                }
+                if (ct + 1 < TR_TILES)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ct == 0) {
+                if (pend) resolve(pr);
+                if (c0 == 0) reset();
             }
         }
-        if constexpr (PIPE) {
-            ptile = tbase + TR_TILES - 1;
-            pr = r;
-            pend = c0 + TR_COLS >= ncol;
-        } else {
-            if (c0 + TR_COLS >= ncol) resolve(r);    // last group of round r
-        }
+        ptile = tbase + TR_TILES - 1;
+        pr = r;
+        pend = c0 + TR_COLS >= ncol;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next group has landed
         if (g + 1 < ngroups && c1 + TR_COLS > ncol) tr_zero_tail<D>(c1, ncol, nbuf);
         __syncthreads();
     };
+
+    auto group_split = [&](int g, const char* buf, char* nbuf) __attribute__((always_inline)) {
+        int r, c0;
+        group_rc(g, r, c0);
+        int r1, c1;
+        group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
+        tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
+        const int tbase = c0 >> 5;
+        // column tiles of this group that hold columns below ncol (the others
+        // are skipped; a tile is never partly past ncol, as ncol % 8 == 0 and
+        // staged columns past it are zero)
+        const int tiles = min(TR_TILES, (ncol - c0 + 31) >> 5);
+        typename M::Frag a[NKS];
+        auto read_tile = [&](int ct, int ks) __attribute__((always_inline)) {
+            const char* p = buf + toff[ct] + 16 * ks * TR_ROWB;
+            a[ks] = __builtin_shufflevector(tr_read(p), tr_read(p + 4 * TR_ROWB),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
+        };
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) read_tile(0, ks);
+#pragma unroll
+        for (int ct = 0; ct < TR_TILES; ++ct) {
+            if (ct < tiles) {
+                __builtin_amdgcn_sched_barrier(0);
+                // token tile 0 under the scan of the pending token tile 1
+                acc[0][0] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) acc[0][0] = M::mma(a[ks], bq[0][ks], acc[0][0]);
+                const float m1 = tile_max(acc[0][1]);
+                asm volatile("" :: "v"(m1));
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         // two MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);         // five VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                record(1, m1, acc[0][1], ptile);
+                if (ct == 0) {
+                    if (pend) resolve(pr);
+                    if (c0 == 0) reset();
+                }
+                // token tile 1 under the scan of token tile 0; the operands of
+                // the next column tile are read as each MFMA frees its set
+                acc[0][1] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    acc[0][1] = M::mma(a[ks], bq[1][ks], acc[0][1]);
+                    if (ct + 1 < TR_TILES) read_tile(ct + 1, ks);      // past `tiles`: read, unused
+                }
+                const float m0 = tile_max(acc[0][0]);
+                asm volatile("" :: "v"(m0));
+                const bool rd = ct + 1 < TR_TILES;                    // two LDS reads per MFMA
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                record(0, m0, acc[0][0], tbase + ct);
+                ptile = tbase + ct;
+            }
+        }
+        pr = r;
+        pend = c0 + TR_COLS >= ncol;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next group has landed
+        if (g + 1 < ngroups && c1 + TR_COLS > ncol) tr_zero_tail<D>(c1, ncol, nbuf);
+        __syncthreads();
+    };
+
     for (int g = 0; g < ngroups; g += 2) {
-        group(g, rt0, rt1);
-        if (g + 1 < ngroups) group(g + 1, rt1, rt0);
+        if constexpr (PIPE) {
+            group(g, rt0, rt1);
+            if (g + 1 < ngroups) group(g + 1, rt1, rt0);
+        } else {
+            group_split(g, rt0, rt1);
+            if (g + 1 < ngroups) group_split(g + 1, rt1, rt0);
+        }
     }
-    if constexpr (PIPE) {
-        scan(acc[1], ptile);
-        resolve(pr);
-    }
+    if constexpr (PIPE) scan(acc[1], ptile);
+    else record(1, tile_max(acc[0][1]), acc[0][1], ptile);
+    resolve(pr);
 }
 
 template <typename T, int D>
