@@ -408,25 +408,13 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
 #pragma unroll
         for (int u = 0; u < HASH_NT; ++u) { bmag[u] = 0.f; btile[u] = -1; keep[u] = f32x16{}; }
     };
-    // one column tile's projections (16 per lane and token tile) against the
-    // round's record: the largest |p| so far, its tile, and that tile's values
-    auto scan = [&](const f32x16 (&ac)[HASH_NT], int tile) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < HASH_NT; ++u) {
-            float m = fabsf(ac[u][0]);
-#pragma unroll
-            for (int j = 1; j < 16; ++j) m = __builtin_elementwise_maximum(m, fabsf(ac[u][j]));
-            const bool up = m > bmag[u];
-            bmag[u] = up ? m : bmag[u];
-            btile[u] = up ? tile : btile[u];
-            keep[u] = up ? ac[u] : keep[u];
-        }
-    };
-    // d 64: the same in two steps.  tile_max runs under the MFMAs; record is
-    // a branch, so that lanes without a new record (and waves where no lane
-    // has one, most late tiles of a long round) skip the copy, which moves
-    // 64-bit register pairs.  The moves are written as asm: the compiler
-    // would otherwise turn the branch back into one select per value.
+    // One column tile's projections (16 per lane and token tile) against the
+    // round's record: the largest |p| so far, its tile, and that tile's
+    // values, in two steps.  tile_max runs under the MFMAs; record is a
+    // branch, so that lanes without a new record (and waves where no lane has
+    // one, most late tiles of a long round) skip the copy, which moves 64-bit
+    // register pairs.  The moves are written as asm: the compiler would
+    // otherwise turn the branch back into one select per value.
     auto tile_max = [&](const f32x16& ac) __attribute__((always_inline)) {
         float m = fabsf(ac[0]);
 #pragma unroll
@@ -533,23 +521,28 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
                 for (int u = 0; u < HASH_NT; ++u) ac[u] = M::mma(a[ks], bq[u][ks], ac[u]);
                 if (ct + 1 < TR_TILES) read_tile(ct + 1, ks);   // into a[ks], now free
             }
-            scan(acc[(ct + 1) & 1], ct == 0 ? ptile : tbase + ct - 1);
-            // an IR-level scheduler would otherwise sink the scans of a group
+            const f32x16 (&pv)[HASH_NT] = acc[(ct + 1) & 1];
+            const int ptl = ct == 0 ? ptile : tbase + ct - 1;
+            float pm[HASH_NT];
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u) pm[u] = tile_max(pv[u]);
+            // an IR-level scheduler would otherwise sink the maxima of a group
             // below all of its MFMAs
 #pragma unroll
-            for (int u = 0; u < HASH_NT; ++u)
-                asm volatile("" :: "v"(bmag[u]), "v"(btile[u]), "v"(keep[u]));
+            for (int u = 0; u < HASH_NT; ++u) asm volatile("" :: "v"(pm[u]));
 #pragma unroll
             for (int i = 0; i < NKS; ++i) {
 #pragma unroll
                 for (int u = 0; u < HASH_NT; ++u) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU
+                    if (i > 0) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // one VALU
                 }
                 if (ct + 1 < TR_TILES)
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
             }
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < HASH_NT; ++u) record(u, pm[u], pv[u], ptl);
             if (ct == 0) {
                 if (pend) resolve(pr);
                 if (c0 == 0) reset();
@@ -643,8 +636,12 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
             if (g + 1 < ngroups) group_split(g + 1, rt1, rt0);
         }
     }
-    if constexpr (PIPE) scan(acc[1], ptile);
-    else record(1, tile_max(acc[0][1]), acc[0][1], ptile);
+    if constexpr (PIPE) {
+#pragma unroll
+        for (int u = 0; u < HASH_NT; ++u) record(u, tile_max(acc[1][u]), acc[1][u], ptile);
+    } else {
+        record(1, tile_max(acc[0][1]), acc[0][1], ptile);
+    }
     resolve(pr);
 }
 
