@@ -131,6 +131,18 @@ def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(shape, dtype: torch.dtype, device, stream=None) -> torch.Tensor:
+    """torch.empty taken on `stream` (the current stream when None).  The caching
+    allocator hands a block back out only in the order of the stream it was taken
+    on, so a buffer the binding allocates for a call on a caller's stream (an
+    output, a workspace, an intermediate that forward() drops) is not reused
+    before that call's kernels have run."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _expect(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device=None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -161,7 +173,7 @@ def lsh_hash(cfg: LSHConfig, qk: torch.Tensor, R: torch.Tensor,
     _expect(qk, "qk", sh["qk"], cfg.torch_dtype)
     _expect(R, "R", sh["R"], cfg.torch_dtype, qk.device)
     if buckets is None:
-        buckets = torch.empty(sh["buckets"], dtype=torch.int32, device=qk.device)
+        buckets = _empty(sh["buckets"], torch.int32, qk.device, stream)
     _expect(buckets, "buckets", sh["buckets"], torch.int32, qk.device)
     c = cfg.to_c()
     _check(lib.lsh_hash(ctypes.byref(c), _ptr(qk), _ptr(R), _ptr(buckets),
@@ -174,10 +186,11 @@ def lsh_sort_workspace_bytes(cfg: LSHConfig) -> int:
     return int(load_library().lsh_sort_workspace_bytes(ctypes.byref(c)))
 
 
-def sort_workspace(cfg: LSHConfig, device) -> torch.Tensor:
-    """A device buffer large enough for lsh_sort (at least 16 bytes)."""
+def sort_workspace(cfg: LSHConfig, device, stream=None) -> torch.Tensor:
+    """A device buffer large enough for lsh_sort (at least 16 bytes), taken on
+    `stream` (the current stream when None)."""
     n = max(16, lsh_sort_workspace_bytes(cfg))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return _empty(n, torch.uint8, device, stream)
 
 
 def lsh_sort(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor] = None,
@@ -189,11 +202,11 @@ def lsh_sort(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor]
     _expect(buckets, "buckets", sh["buckets"], torch.int32)
     dev = buckets.device
     if perm is None:
-        perm = torch.empty(sh["perm"], dtype=torch.int32, device=dev)
+        perm = _empty(sh["perm"], torch.int32, dev, stream)
     if cid is None:
-        cid = torch.empty(sh["cid"], dtype=torch.int16, device=dev)
+        cid = _empty(sh["cid"], torch.int16, dev, stream)
     if workspace is None:
-        workspace = sort_workspace(cfg, dev)
+        workspace = sort_workspace(cfg, dev, stream)
     _expect(perm, "perm", sh["perm"], torch.int32, dev)
     _expect(cid, "cid", sh["cid"], torch.int16, dev)
     if workspace.device != dev or not workspace.is_contiguous():
@@ -220,9 +233,9 @@ def lsh_sort_noalloc(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch
     _expect(buckets, "buckets", sh["buckets"], torch.int32)
     dev = buckets.device
     if perm is None:
-        perm = torch.empty(sh["perm"], dtype=torch.int32, device=dev)
+        perm = _empty(sh["perm"], torch.int32, dev, stream)
     if cid is None:
-        cid = torch.empty(sh["cid"], dtype=torch.int16, device=dev)
+        cid = _empty(sh["cid"], torch.int16, dev, stream)
     _expect(perm, "perm", sh["perm"], torch.int32, dev)
     _expect(cid, "cid", sh["cid"], torch.int16, dev)
     c = cfg.to_c()
@@ -243,9 +256,9 @@ def lsh_chunk_attn(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: torc
     _expect(perm, "perm", sh["perm"], torch.int32, dev)
     _expect(cid, "cid", sh["cid"], torch.int16, dev)
     if o_rounds is None:
-        o_rounds = torch.empty(sh["o_rounds"], dtype=cfg.torch_dtype, device=dev)
+        o_rounds = _empty(sh["o_rounds"], cfg.torch_dtype, dev, stream)
     if lse is None:
-        lse = torch.empty(sh["lse"], dtype=torch.float32, device=dev)
+        lse = _empty(sh["lse"], torch.float32, dev, stream)
     _expect(o_rounds, "o_rounds", sh["o_rounds"], cfg.torch_dtype, dev)
     _expect(lse, "lse", sh["lse"], torch.float32, dev)
     c = cfg.to_c()
@@ -263,7 +276,7 @@ def lsh_combine_rounds(cfg: LSHConfig, o_rounds: torch.Tensor, lse: torch.Tensor
     dev = o_rounds.device
     _expect(lse, "lse", sh["lse"], torch.float32, dev)
     if o is None:
-        o = torch.empty(sh["o"], dtype=cfg.torch_dtype, device=dev)
+        o = _empty(sh["o"], cfg.torch_dtype, dev, stream)
     _expect(o, "o", sh["o"], cfg.torch_dtype, dev)
     c = cfg.to_c()
     _check(lib.lsh_combine_rounds(ctypes.byref(c), _ptr(o_rounds), _ptr(lse), _ptr(o),
@@ -276,10 +289,11 @@ def lsh_backward_workspace_bytes(cfg: LSHConfig) -> int:
     return int(load_library().lsh_backward_workspace_bytes(ctypes.byref(c)))
 
 
-def backward_workspace(cfg: LSHConfig, device) -> torch.Tensor:
-    """A device buffer large enough for lsh_attn_backward (at least 16 bytes)."""
+def backward_workspace(cfg: LSHConfig, device, stream=None) -> torch.Tensor:
+    """A device buffer large enough for lsh_attn_backward (at least 16 bytes),
+    taken on `stream` (the current stream when None)."""
     n = max(16, lsh_backward_workspace_bytes(cfg))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return _empty(n, torch.uint8, device, stream)
 
 
 def lsh_attn_backward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: torch.Tensor,
@@ -298,13 +312,13 @@ def lsh_attn_backward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: t
     _expect(o, "o", sh["o"], cfg.torch_dtype, dev)
     _expect(d_o, "d_o", sh["o"], cfg.torch_dtype, dev)
     if d_qk is None:
-        d_qk = torch.empty(sh["qk"], dtype=torch.float32, device=dev)
+        d_qk = _empty(sh["qk"], torch.float32, dev, stream)
     if d_v is None:
-        d_v = torch.empty(sh["v"], dtype=torch.float32, device=dev)
+        d_v = _empty(sh["v"], torch.float32, dev, stream)
     _expect(d_qk, "d_qk", sh["qk"], torch.float32, dev)
     _expect(d_v, "d_v", sh["v"], torch.float32, dev)
     if workspace is None:
-        workspace = backward_workspace(cfg, dev)
+        workspace = backward_workspace(cfg, dev, stream)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous buffer on the same device")
     nbytes = workspace.numel() * workspace.element_size()
@@ -342,9 +356,9 @@ def lsh_project_in(cfg: LSHConfig, d_model: int, x: torch.Tensor, w_qk: torch.Te
     _expect(w_qk, "w_qk", (hd, d_model), cfg.torch_dtype, dev)
     _expect(w_v, "w_v", (hd, d_model), cfg.torch_dtype, dev)
     if qk is None:
-        qk = torch.empty(sh["qk"], dtype=cfg.torch_dtype, device=dev)
+        qk = _empty(sh["qk"], cfg.torch_dtype, dev, stream)
     if v is None:
-        v = torch.empty(sh["v"], dtype=cfg.torch_dtype, device=dev)
+        v = _empty(sh["v"], cfg.torch_dtype, dev, stream)
     _expect(qk, "qk", sh["qk"], cfg.torch_dtype, dev)
     _expect(v, "v", sh["v"], cfg.torch_dtype, dev)
     c = cfg.to_c()
@@ -363,7 +377,7 @@ def lsh_project_out(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torch.Te
     dev = o.device
     _expect(w_o, "w_o", (d_model, cfg.heads * cfg.d_head), cfg.torch_dtype, dev)
     if y is None:
-        y = torch.empty((cfg.batch, cfg.seq_len, d_model), dtype=cfg.torch_dtype, device=dev)
+        y = _empty((cfg.batch, cfg.seq_len, d_model), cfg.torch_dtype, dev, stream)
     _expect(y, "y", (cfg.batch, cfg.seq_len, d_model), cfg.torch_dtype, dev)
     c = cfg.to_c()
     _check(lib.lsh_project_out(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(y),
@@ -383,7 +397,7 @@ def lsh_project_out_add(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torc
     _expect(w_o, "w_o", (d_model, cfg.heads * cfg.d_head), cfg.torch_dtype, dev)
     _expect(residual, "residual", shape, cfg.torch_dtype, dev)
     if y is None:
-        y = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+        y = _empty(shape, cfg.torch_dtype, dev, stream)
     _expect(y, "y", shape, cfg.torch_dtype, dev)
     c = cfg.to_c()
     _check(lib.lsh_project_out_add(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(residual),
@@ -412,11 +426,11 @@ def lsh_ffn(x: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tenso
                            (b2, "b2", (d_model,)), (residual, "residual", tuple(x.shape))):
         _expect(t, name, shape, torch.bfloat16, dev)
     if y is None:
-        y = torch.empty_like(x)
+        y = _empty(x.shape, x.dtype, dev, stream)
     _expect(y, "y", tuple(x.shape), torch.bfloat16, dev)
     need = lsh_ffn_workspace_bytes(rows, d_ff, chunk_rows)
     if hidden is None:
-        hidden = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        hidden = _empty(max(16, need), torch.uint8, dev, stream)
     if hidden.device != dev or not hidden.is_contiguous():
         raise ValueError("hidden must be a contiguous buffer on the same device")
     _check(lib.lsh_ffn(int(rows), int(d_model), int(d_ff), int(chunk_rows), _ptr(x), _ptr(w1), _ptr(b1),

@@ -73,7 +73,45 @@ def build(verbose: bool = False) -> str:
         print(out, file=sys.stderr)
         raise RuntimeError("linking the LSH-attention library failed")
     os.replace(tmp, LIB_PATH)
+    build_asan_check(objs, verbose)
     return LIB_PATH
+
+
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_CHECK = os.path.join(ASAN_DIR, "abi_asan_check")
+
+
+def build_asan_check(objs, verbose: bool = False) -> str:
+    """The host-only AddressSanitizer check of the C ABI's argument validation
+    (tests/abi_asan_check.c, run by tests/test_abi.py): lsh_api.hip's host code
+    compiled with ASan (device code untouched), linked with the other objects
+    of the library build.  Not part of the library."""
+    rocm = os.path.realpath(os.path.join(os.path.dirname(os.path.realpath(hipcc())), ".."))
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    clangxx = clang + "++"
+    rocm_inc = os.path.join(rocm, "include")
+    rocm_lib = os.path.join(rocm, "lib")
+    driver = os.path.join(ROOT, "tests", "abi_asan_check.c")
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    api_o = os.path.join(ASAN_DIR, "lsh_api.o")
+    drv_o = os.path.join(ASAN_DIR, "abi_asan_check.o")
+    host_asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in CXXFLAGS if f != "-O3"] + ["-O1", "-g"]
+    steps = [
+        [hipcc(), *flags, *VGPR_FORM, *host_asan, "-c", os.path.join(CSRC, "lsh_api.hip"), "-o", api_o],
+        [clang, "-std=c99", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-Wall",
+         "-D__HIP_PLATFORM_AMD__", f"-I{rocm_inc}", f"-I{INCLUDE}", "-c", driver, "-o", drv_o],
+        [clangxx, "-fsanitize=address", drv_o, api_o,
+         *[o for o in objs if os.path.basename(o) != "lsh_api.o"],
+         f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{rocm_lib}", "-o", ASAN_CHECK],
+    ]
+    for cmd in steps:
+        rc, out = _run(cmd)
+        if verbose or rc:
+            print(f"[build] {' '.join(cmd[:3])} ...\n{out}", file=sys.stderr)
+        if rc:
+            raise RuntimeError("building the ASan check of the C ABI failed")
+    return ASAN_CHECK
 
 
 if __name__ == "__main__":

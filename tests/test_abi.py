@@ -327,3 +327,22 @@ def test_sort_noalloc_checks(lib):
     # the 1M-token workload fits
     long_1m = cfg(seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128)
     assert lib.lsh_sort_workspace_bytes(raw(long_1m)) <= B.SORT_NOALLOC_MAX_BYTES
+
+
+def test_validation_under_host_asan():
+    """The checks above, and more, in an AddressSanitizer build of the C ABI's
+    host code (tests/abi_asan_check.c; built by the package build): every call
+    fails validation before any HIP call, and ASan watches the message strings,
+    the size arithmetic and the config reads."""
+    import subprocess
+    import torch
+    from lsh_attention_02_amd import build as BLD
+    if torch.cuda.is_available():
+        pytest.skip("fake device pointers: runs on hosts without a GPU")
+    if not os.path.exists(BLD.ASAN_CHECK):
+        pytest.skip("ASan check not built (python -m lsh_attention_02_amd.build)")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1")
+    p = subprocess.run([BLD.ASAN_CHECK], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True, env=env, timeout=120)
+    assert p.returncode == 0, p.stdout[-4000:]
+    assert "ok: 0 failure(s)" in p.stdout

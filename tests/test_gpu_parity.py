@@ -240,6 +240,29 @@ def test_streams_and_preallocated_outputs():
         assert torch.equal(ref[k], outs[k]), k
 
 
+def test_side_stream_with_library_allocations():
+    """On a side stream, with every output, workspace and intermediate allocated
+    by the binding (taken on that stream), forward() and the backward give the
+    default stream's results."""
+    w = WORKLOADS["short_4k"]
+    x = make_inputs(w)
+    cfg, t, ref = GP.run_gpu(w, x)
+    d_o = torch.randn(ref["o"].shape, generator=torch.Generator().manual_seed(7)).to(
+        device=ref["o"].device, dtype=ref["o"].dtype)
+    g_ref = lsh.lsh_attn_backward(cfg, t["qk"], t["v"], ref["perm"], ref["cid"], ref["lse"],
+                                  ref["o"], d_o)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o = lsh.forward(cfg, t["qk"], t["v"], t["R"], stream=s)
+        g = lsh.lsh_attn_backward(cfg, t["qk"], t["v"], ref["perm"], ref["cid"], ref["lse"],
+                                  ref["o"], d_o, stream=s)
+    s.synchronize()
+    assert torch.equal(o, ref["o"])
+    for a, b in zip(g, g_ref):
+        assert torch.equal(a, b)
+
+
 def test_workspace_too_small_is_rejected():
     w = WORKLOADS["short_4k"]
     cfg = GP.cfg_of(w)
