@@ -346,6 +346,21 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t x, int lane, ui
     return incl - x;
 }
 
+// Inclusive sum over the 64 lanes with DPP moves: shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then the row totals carried across rows with the
+// row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_inclusive_scan_dpp(uint32_t x)
+{
+    int v = (int)x;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    return (uint32_t)v;
+}
+
 template <bool SAME>
 __global__ __launch_bounds__(PLACE_MAX_WAVES * 64)
 void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict__ colpre,
@@ -582,6 +597,234 @@ void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// k_sort_place2: k_sort_place for tiles of at most 64 * BPL positions (BPL per
+// lane), with far fewer LDS operations, most of them free of bank conflicts.
+// Wave w places round r0 + w of the tile; per wave, in LDS:
+//   tab[nb]   u64: low word the bucket's running count during the ranking,
+//             then its first tile-local index (bits 0-15) and, same-bucket
+//             variant, 2 * its rank among the round's non-empty buckets (bits
+//             16-31); high word dlt = first slot of (tile, bucket) in the
+//             segment minus its first tile-local index
+//   stg[P]    u32: (bucket << 16) | position, in sorted order
+//   bt[P]     u16: cid value of each tile position
+// The tile's buckets stay in registers (position 64 k + lane in register k).
+// Ranking step k: the lanes holding one bucket find each other with one ballot
+// per bucket bit (the lanes whose bits all agree), the lowest of them adds the
+// group's size to the bucket's count (an LDS add-and-return; the LDS
+// operations of one wave execute in program order, so earlier steps come
+// first), and each lane's rank is that old count plus the group members below
+// it.  The histogram of the tile is the counts left at the end.
+constexpr int PLACE2_MAX_BPL = 32;
+constexpr size_t PLACE2_LDS_TARGET = 80 * 1024;   // two workgroups per CU
+
+struct Place2Layout {                             // offsets in bytes within a wave's region
+    int stg, bt, bytes;
+};
+
+__host__ __device__ inline Place2Layout place2_layout(int nb, int P)
+{
+    Place2Layout l;
+    l.stg = 8 * nb;
+    l.bt = l.stg + 4 * P;
+    l.bytes = (l.bt + 2 * P + 15) & ~15;
+    return l;
+}
+
+constexpr int PLACE2_MAX_WAVES = 8;              // 256 VGPRs per lane: no spills at 32 steps
+
+template <bool SAME, int BPL>
+__global__ __launch_bounds__(PLACE2_MAX_WAVES * 64)
+void k_sort_place2(const int32_t* __restrict__ buckets, const int32_t* __restrict__ colpre,
+                   const int32_t* __restrict__ totals, int32_t* __restrict__ perm,
+                   int16_t* __restrict__ cid, int L, int nb, int nbits, int P, int ntiles, int n_r,
+                   int RG, int ngroups, long nkeys, int chunk, int chunk_shift)
+{
+    extern __shared__ uint32_t lds[];
+    // all tiles of one (batch row, head, round group) on one XCD (see ScatterMap)
+    const int xcd = blockIdx.x % NXCD;
+    const long j = blockIdx.x / NXCD;
+    const long key = (j / ntiles) * NXCD + xcd;
+    if (key >= nkeys) return;                      // padding of the last row of keys
+    const int t = (int)(j % ntiles);
+    const long bh = key / ngroups;
+    const int r0 = (int)(key % ngroups) * RG;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = r0 + w;
+    const long seg = bh * n_r + r;
+    const int p0 = t * P, np = min(P, L - p0);
+    const Place2Layout ly = place2_layout(nb, P);
+
+    char* base8 = reinterpret_cast<char*>(lds) + (long)w * ly.bytes;
+    uint32_t* tab = reinterpret_cast<uint32_t*>(base8);             // tab[2 b] low, tab[2 b + 1] high
+    uint32_t* stg = reinterpret_cast<uint32_t*>(base8 + ly.stg);
+    uint16_t* bt = reinterpret_cast<uint16_t*>(base8 + ly.bt);
+
+    // 1. the round's buckets of the tile into registers; counts to zero
+    const int32_t* bk = buckets + seg * (long)L + p0;
+    int bv[BPL];
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+        const int p = 64 * k + lane;
+        bv[k] = bk[min(p, np - 1)];
+        if (p >= np) bv[k] = -1;
+    }
+    for (int b = lane; b < nb; b += 64) tab[2 * b] = 0u;
+
+    // 2. ranks, 8 steps at a time (their group masks in registers); each
+    //    step's register then holds (rank << 16) | bucket (0xFFFF: no bucket)
+    constexpr int GRP = BPL < 8 ? BPL : 8;
+#pragma unroll
+    for (int k0 = 0; k0 < BPL; k0 += GRP) {
+        uint32_t mlo[GRP], mhi[GRP];
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const uint64_t v = __ballot((unsigned)bv[k0 + k] < (unsigned)nb);
+            mlo[k] = (uint32_t)v;
+            mhi[k] = (uint32_t)(v >> 32);
+        }
+        for (int bit = 0; bit < nbits; ++bit) {
+#pragma unroll
+            for (int k = 0; k < GRP; ++k) {
+                const uint32_t x = (uint32_t)__builtin_amdgcn_sbfe(bv[k0 + k], bit, 1);   // 0 or ~0
+                const uint64_t B = __ballot(x != 0u);
+                // one three-input bitwise instruction per half
+                mlo[k] &= ~((uint32_t)B ^ x);
+                mhi[k] &= ~((uint32_t)(B >> 32) ^ x);
+            }
+        }
+        uint64_t m[GRP];
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) m[k] = ((uint64_t)mhi[k] << 32) | mlo[k];
+        uint32_t old[GRP];
+        int rep[GRP];
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const int b = bv[k0 + k];
+            const bool ok = (unsigned)b < (unsigned)nb;
+            rep[k] = ok ? __builtin_ctzll(m[k]) : lane;
+            old[k] = 0u;
+            if (ok && rep[k] == lane) old[k] = atomicAdd(&tab[2 * b], (uint32_t)__popcll(m[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const int b = bv[k0 + k];
+            const bool ok = (unsigned)b < (unsigned)nb;
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[k] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m[k], 0u));
+            const uint32_t rank = (uint32_t)__shfl((int)old[k], rep[k]) + below;
+            bv[k0 + k] = ok ? (int)((rank << 16) | (uint32_t)b) : 0xFFFF;
+        }
+    }
+
+    // 3. tile-local first index of each bucket (exclusive scan of the counts);
+    //    segment slot offsets (scan of the totals plus colpre) -> dlt.  Chunks
+    //    of 64 consecutive buckets, lane l taking bucket 64 c + l, scanned
+    //    across the lanes (DPP) with a running carry; nb <= 1024 here
+    uint32_t nvalid_u;
+    {
+        const int32_t* tot = totals + seg * (long)nb;
+        const int32_t* cp = colpre + (seg * ntiles + t) * (long)nb;
+        constexpr int NCH = 1024 / 64;
+        int tv[NCH], cv[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int b = min(64 * c + lane, nb - 1);
+            tv[c] = 64 * c < nb ? tot[b] : 0;
+            cv[c] = 64 * c < nb ? cp[b] : 0;
+        }
+        uint32_t carry_cnt = 0, carry_tot = 0, carry_nz = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (64 * c < nb) {
+                const int b = 64 * c + lane;
+                const bool in = b < nb;
+                const uint32_t cnt = in ? tab[2 * b] : 0u;
+                const uint32_t tt = in ? (uint32_t)tv[c] : 0u;
+                const uint32_t ic = wave_inclusive_scan_dpp(cnt);
+                const uint32_t it = wave_inclusive_scan_dpp(tt);
+                const uint32_t start = carry_cnt + ic - cnt;
+                uint32_t lo = start;
+                if constexpr (SAME) {
+                    const uint32_t nz = tt > 0 ? 1u : 0u;
+                    const uint32_t inz = wave_inclusive_scan_dpp(nz);
+                    lo |= (2u * (carry_nz + inz - nz)) << 16;
+                    carry_nz += (uint32_t)__builtin_amdgcn_readlane((int)inz, 63);
+                }
+                const uint32_t gfirst = carry_tot + it - tt + (uint32_t)cv[c];
+                if (in) *reinterpret_cast<uint2*>(&tab[2 * b]) = make_uint2(lo, gfirst - start);
+                carry_cnt += (uint32_t)__builtin_amdgcn_readlane((int)ic, 63);
+                carry_tot += (uint32_t)__builtin_amdgcn_readlane((int)it, 63);
+            }
+        }
+        nvalid_u = carry_cnt;
+    }
+    const int nvalid = (int)nvalid_u;
+
+    // 4. each position to its sorted index (stg) and its cid value (bt)
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+        const int p = 64 * k + lane;
+        const int b = bv[k] & 0xFFFF;
+        const bool ok = b < nb;
+        const uint2 e = *reinterpret_cast<const uint2*>(&tab[2 * (ok ? b : 0)]);
+        const uint32_t li = (e.x & 0xFFFFu) + ((uint32_t)bv[k] >> 16);
+        const uint32_t slot = li + e.y;
+        uint32_t id = chunk_shift >= 0 ? slot >> chunk_shift : slot / (uint32_t)chunk;
+        if constexpr (SAME) id += e.x >> 16;
+        if (ok) stg[li] = ((uint32_t)b << 16) | (uint32_t)p;
+        if (p < P) bt[p] = ok ? (uint16_t)id : (uint16_t)0xFFFF;
+    }
+
+    // 5. perm in sorted order (each bucket's run of slots is contiguous)
+    int32_t* pm = perm + seg * (long)L;
+    for (int i0 = 0; i0 < nvalid; i0 += 64 * PLACE_BATCH) {
+        uint32_t e[PLACE_BATCH], dl[PLACE_BATCH];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) e[k] = stg[min(i0 + 64 * k + lane, P - 1)];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) dl[k] = tab[2 * min((int)(e[k] >> 16), nb - 1) + 1];
+#pragma unroll
+        for (int k = 0; k < PLACE_BATCH; ++k) {
+            const int i = i0 + 64 * k + lane;
+            const uint32_t slot = (uint32_t)i + dl[k];
+            // in range unless the input changed under the sort
+            if (i < nvalid && slot < (uint32_t)L) pm[slot] = p0 + (int)(e[k] & 0xFFFFu);
+        }
+    }
+    __syncthreads();
+    // 6. the tile's cid rows for the group's rounds
+    const uint16_t* bts[PLACE2_MAX_WAVES];
+#pragma unroll
+    for (int k = 0; k < PLACE2_MAX_WAVES; ++k)
+        bts[k] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(lds) + (long)k * ly.bytes + ly.bt);
+    int16_t* cd = cid + (bh * (long)L + p0) * n_r;
+    switch (RG) {
+        case 1: store_cid_rows<1>(cd, bts, np, n_r, r0); break;
+        case 2: store_cid_rows<2>(cd, bts, np, n_r, r0); break;
+        case 4: store_cid_rows<4>(cd, bts, np, n_r, r0); break;
+        case 8: store_cid_rows<8>(cd, bts, np, n_r, r0); break;
+        default:
+            for (int e = threadIdx.x; e < np * RG; e += blockDim.x) {
+                const int p = e / RG, k = e - p * RG;
+                cd[(long)p * n_r + r0 + k] = (int16_t)bts[k][p];
+            }
+    }
+}
+
+// Rounds per k_sort_place2 workgroup: the largest divisor of n_rounds (at most
+// PLACE2_MAX_WAVES) whose waves' LDS fits in PLACE2_LDS_TARGET; 0 when the tile
+// is longer than 64 * PLACE2_MAX_BPL positions or one round does not fit.
+int place2_rounds_per_group(int nb, int P, int n_r)
+{
+    if (P > 64 * PLACE2_MAX_BPL) return 0;
+    const size_t per = (size_t)place2_layout(nb, P).bytes;
+    int best = 0;
+    for (int rg = 1; rg <= n_r && rg <= PLACE2_MAX_WAVES; ++rg)
+        if (n_r % rg == 0 && rg * per <= PLACE2_LDS_TARGET) best = rg;
+    return best;
+}
+
 // Rounds per k_sort_place workgroup: the largest divisor of n_rounds (at most
 // PLACE_MAX_WAVES) whose waves' LDS fits; 0 if not even one round fits, or if
 // tile positions do not fit in 16 bits (then k_sort_scatter is used).
@@ -675,12 +918,42 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
         const int bps = (n_buckets + COLSCAN_THREADS - 1) / COLSCAN_THREADS;
         hipLaunchKernelGGL(k_sort_colscan, dim3((unsigned)(plan.nseg * bps)), dim3(COLSCAN_THREADS), 0, s,
                            counters, extra, n_buckets, plan.ntiles, bps);
+        const int shift = (chunk & (chunk - 1)) == 0 ? __builtin_ctz((unsigned)chunk) : -1;
+        const int rg2 = place2_rounds_per_group(n_buckets, plan.tile, n_rounds);
+        if (rg2 > 0) {
+            const int ngroups = n_rounds / rg2;
+            const long nkeys = bh * ngroups;
+            const long rows = (nkeys + NXCD - 1) / NXCD;
+            const unsigned pblocks = (unsigned)(rows * NXCD * plan.ntiles);
+            const size_t plds = (size_t)rg2 * place2_layout(n_buckets, plan.tile).bytes;
+            int bpl = 1;
+            while (64 * bpl < plan.tile) bpl <<= 1;
+            auto go = [&](auto same, auto bplc) {
+                constexpr bool SM = decltype(same)::value;
+                constexpr int BP = decltype(bplc)::value;
+                hipLaunchKernelGGL((k_sort_place2<SM, BP>), dim3(pblocks), dim3(64 * rg2), plds, s, buckets,
+                                   counters, extra, perm, cid, L, n_buckets, nbits, plan.tile,
+                                   plan.ntiles, n_rounds, rg2, ngroups, nkeys, chunk, shift);
+            };
+            auto by_bpl = [&](auto same) {
+                switch (bpl) {
+                    case 1: go(same, std::integral_constant<int, 1>{}); break;
+                    case 2: go(same, std::integral_constant<int, 2>{}); break;
+                    case 4: go(same, std::integral_constant<int, 4>{}); break;
+                    case 8: go(same, std::integral_constant<int, 8>{}); break;
+                    case 16: go(same, std::integral_constant<int, 16>{}); break;
+                    default: go(same, std::integral_constant<int, 32>{}); break;
+                }
+            };
+            if (same_bucket) by_bpl(std::true_type{});
+            else by_bpl(std::false_type{});
+            return hipGetLastError();
+        }
         const int ngroups = n_rounds / rg;
         const long nkeys = bh * ngroups;
         const long rows = (nkeys + NXCD - 1) / NXCD;
         const unsigned pblocks = (unsigned)(rows * NXCD * plan.ntiles);
         const size_t plds = (size_t)rg * place_layout(n_buckets, plan.tile, same_bucket).words * 4;
-        const int shift = (chunk & (chunk - 1)) == 0 ? __builtin_ctz((unsigned)chunk) : -1;
         if (same_bucket)
             hipLaunchKernelGGL(k_sort_place<true>, dim3(pblocks), dim3(64 * rg), plds, s, buckets,
                                counters, extra, perm, cid, L, n_buckets, nbits, plan.tile,
