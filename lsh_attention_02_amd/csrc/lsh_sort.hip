@@ -616,7 +616,10 @@ void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict
 // first), and each lane's rank is that old count plus the group members below
 // it.  The histogram of the tile is the counts left at the end.
 constexpr int PLACE2_MAX_BPL = 32;
-constexpr size_t PLACE2_LDS_TARGET = 80 * 1024;   // two workgroups per CU
+// All rounds of a tile in one workgroup where they fit, so that each cid row is
+// written whole by one workgroup (split rows were measured to add a write of
+// the cid array's size in partial lines)
+constexpr size_t PLACE2_LDS_TARGET = 160 * 1024;
 
 struct Place2Layout {                             // offsets in bytes within a wave's region
     int stg, bt, bytes;
@@ -907,6 +910,15 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE_LDS_LIMIT);
         (void)hipFuncSetAttribute((const void*)k_sort_place<true>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE_LDS_LIMIT);
+        auto p2 = [](const void* f) {
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE2_LDS_TARGET);
+        };
+        p2((const void*)k_sort_place2<false, 1>); p2((const void*)k_sort_place2<false, 2>);
+        p2((const void*)k_sort_place2<false, 4>); p2((const void*)k_sort_place2<false, 8>);
+        p2((const void*)k_sort_place2<false, 16>); p2((const void*)k_sort_place2<false, 32>);
+        p2((const void*)k_sort_place2<true, 1>); p2((const void*)k_sort_place2<true, 2>);
+        p2((const void*)k_sort_place2<true, 4>); p2((const void*)k_sort_place2<true, 8>);
+        p2((const void*)k_sort_place2<true, 16>); p2((const void*)k_sort_place2<true, 32>);
     });
     int nbits = 0;
     while ((1 << nbits) < n_buckets) ++nbits;
