@@ -263,6 +263,41 @@ def test_side_stream_with_library_allocations():
         assert torch.equal(a, b)
 
 
+# (L, n_buckets, n_rounds, chunk): power-of-two and other bucket counts, tiles
+# cut short by L (L not a multiple of the 2048-position tile), one bucket
+# holding most positions, bucket counts where some lanes own no bucket in the
+# placement's scan (nb not a multiple of 64) and where the tile is L itself; up
+# to 1024 buckets the register placement runs, above it the LDS placement, and
+# at 16384 buckets the per-segment scatter
+SORT_SWEEP = [
+    (2560, 40, 2, 128), (4096, 48, 3, 64), (6144, 100, 4, 32), (4096, 126, 1, 64),
+    (4096, 128, 2, 64), (5000, 250, 5, 8), (2048, 2, 2, 64), (1344, 10, 3, 64),
+    (8192, 1000, 8, 64), (4096, 1024, 2, 32), (12288, 2046, 2, 64), (6000, 4098, 3, 40),
+    (32768, 16384, 2, 64),
+]
+
+
+@pytest.mark.parametrize("L,nb,nr,chunk", SORT_SWEEP)
+@pytest.mark.parametrize("flags", [0, lsh.LSH_FLAG_SAME_BUCKET])
+def test_sort_sweep(L, nb, nr, chunk, flags):
+    """perm and cid bit-exact against the oracle's stable sort on uniform and
+    skewed bucket draws (the skewed ones put half the positions in bucket 0)."""
+    rng = np.random.default_rng(L * 31 + nb * 7 + nr)
+    cfg = lsh.LSHConfig(batch=1, heads=3, seq_len=L, d_head=64, n_buckets=nb, n_rounds=nr,
+                        chunk=chunk, causal=True, dtype="bf16", flags=flags)
+    for skew in (False, True):
+        b = rng.integers(0, nb, (1, 3, nr, L)).astype(np.int32)
+        if skew:
+            b[rng.random(b.shape) < 0.5] = 0
+        perm, cid = lsh.lsh_sort(cfg, torch.from_numpy(b).cuda())
+        torch.cuda.synchronize()
+        sp, sc_id = O.sort_rounds(b, nb, chunk)
+        assert np.array_equal(perm.cpu().numpy(), sp), (L, nb, nr, chunk, flags, skew)
+        gc = cid.cpu().numpy()
+        want = GP.window_ids(sc_id, b, nb) if flags else sc_id.view(np.uint16)
+        assert np.array_equal(gc.view(np.uint16), want), (L, nb, nr, chunk, flags, skew)
+
+
 def test_workspace_too_small_is_rejected():
     w = WORKLOADS["short_4k"]
     cfg = GP.cfg_of(w)
