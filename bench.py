@@ -328,7 +328,7 @@ def pmc_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
     print(json.dumps(rec["workloads"][workload], indent=1))
 
 
-def trace_summary(workload, stats_csv, bench_log, command, out_md):
+def trace_summary(workload, stats_csv, bench_log, command, out_md, title="forward pass"):
     """A rocprofv3 --kernel-trace --stats summary (the library's kernels) next to
     the per-call event times the same bench run printed, as a short Markdown file."""
     import csv
@@ -338,7 +338,7 @@ def trace_summary(workload, stats_csv, bench_log, command, out_md):
     w = WORKLOADS[workload]
     line = [l for l in open(bench_log) if l.startswith("{")][-1]
     res = json.loads(line)
-    out = [f"# Kernel trace summary: forward pass, {workload} workload", "",
+    out = [f"# Kernel trace summary: {title}, {workload} workload", "",
            f"Workload {workload}: {w.description} (synthetic, seed {w.seed}).", "",
            "Command (repository root, MI355X):", "",
            "    cd /root/repo && export TMPDIR=/tmp", f"    {command}", "",
@@ -417,10 +417,21 @@ def main():
     args = ap.parse_args()
     if args.trace_summary:
         stats, blog = args.trace_summary
-        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_{args.workload} "
-               f"-o run -- python bench.py --no-cpu-baseline --workload {args.workload}")
-        trace_summary(args.workload, stats, blog, cmd,
-                      os.path.join(ROOT, "profiles", f"forward_{args.workload}_kernel_stats.md"))
+        wl = args.workload
+        mode, extra, title, tag = "forward", "", "forward pass", ""
+        if args.backward:
+            mode, extra, title = "backward", " --backward", "forward + backward (lsh_attn_backward)"
+        elif args.layer:
+            mode, extra, tag = "layer", f" --layer {args.layer}", f"_d{args.layer}"
+            title = f"attention layer (projections around the four steps) at d_model {args.layer}"
+        elif args.block:
+            mode, extra, tag = "block", f" --block {args.block}", f"_d{args.block}"
+            title = f"Reformer block forward and input recompute at d_model {args.block}"
+        trace = "trace" if mode == "forward" else f"trace_{mode}"
+        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/{trace}_{wl} "
+               f"-o run -- python bench.py --no-cpu-baseline --workload {wl}{extra}")
+        trace_summary(wl, stats, blog, cmd,
+                      os.path.join(ROOT, "profiles", f"{mode}_{wl}{tag}_kernel_stats.md"), title)
         return
     if args.pmc_summary:
         fd, wd, cfd, cwd = args.pmc_summary
