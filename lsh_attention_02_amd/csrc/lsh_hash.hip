@@ -335,6 +335,23 @@ __device__ __forceinline__ void tr_stage(const bf16_t* __restrict__ Rr, int c0, 
     }
 }
 
+// tr_stage when ncol is a multiple of TR_COLS (no piece past ncol).  Step i
+// advances every lane by NTH / 16 rows (a multiple of 4, so the swizzle is
+// unchanged): a lane's byte offset within a step (loff) is the same for every
+// step and group, and a group costs uniform base addresses only; wv is the
+// wave index, uniform
+template <int D>
+__device__ __forceinline__ void tr_stage_full(const char* Rg, uint32_t loff, int ncol, int wv, char* buf)
+{
+    constexpr int NTH = tr_waves<D>() * 64;
+    const long step = 2L * (NTH / TR_PPR) * ncol;
+#pragma unroll
+    for (int i = 0; i < D * TR_PPR / NTH; ++i)
+        __builtin_amdgcn_global_load_lds(Rg + i * step + loff,
+                                         (__attribute__((address_space(3))) void*)(buf + 16 * (i * NTH + wv * 64)),
+                                         16, 0, 0);
+}
+
 template <int D>
 __device__ __forceinline__ void tr_zero_tail(int c0, int ncol, char* buf)
 {
@@ -376,6 +393,17 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
 
     const int groups_per_round = (ncol + TR_COLS - 1) / TR_COLS;
     const int ngroups = n_r * groups_per_round;
+    static_assert((tr_waves<D>() * 64 / TR_PPR) % 4 == 0, "staging step must keep the swizzle");
+    const bool full = ncol % TR_COLS == 0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // this lane's staging offset (bytes) within a step of a group
+    const uint32_t loff = (uint32_t)(2 * ((tid / TR_PPR) * ncol + 8 * tr_piece(tid % TR_PPR, tid / TR_PPR)));
+    // group (r, c0) of R into buf
+    auto stage = [&](int r, int c0, char* buf) __attribute__((always_inline)) {
+        const bf16_t* Rr = R + (long)r * D * ncol;
+        if (full) tr_stage_full<D>(reinterpret_cast<const char*>(Rr + c0), loff, ncol, wv, buf);
+        else tr_stage<D>(Rr, c0, ncol, buf);
+    };
 
     // this lane's transposing-read offsets, per column tile: group G = lane / 16
     // (column half G % 2, k half G / 2), lane 4k + q of it addresses row
@@ -398,7 +426,7 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         c0 = (g % groups_per_round) * TR_COLS;
     };
     {
-        tr_stage<D>(R, 0, ncol, rt0);
+        stage(0, 0, rt0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (TR_COLS > ncol) tr_zero_tail<D>(0, ncol, rt0);
         __syncthreads();
@@ -495,7 +523,7 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         group_rc(g, r, c0);
         int r1, c1;
         group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
-        tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
+        stage(r1, c1, nbuf);
         const int tbase = c0 >> 5;
         typename M::Frag a[NKS];
         auto read_tile = [&](int ct, int ks) __attribute__((always_inline)) {
@@ -561,7 +589,7 @@ void k_hash_tr(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ R, int3
         group_rc(g, r, c0);
         int r1, c1;
         group_rc(min(g + 1, ngroups - 1), r1, c1);     // past the last group: the last again, never read
-        tr_stage<D>(R + (long)r1 * D * ncol, c1, ncol, nbuf);
+        stage(r1, c1, nbuf);
         const int tbase = c0 >> 5;
         // column tiles of this group that hold columns below ncol (the others
         // are skipped; a tile is never partly past ncol, as ncol % 8 == 0 and
