@@ -425,8 +425,10 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                 if (t % SGRP == SGRP - 1) __builtin_amdgcn_sched_barrier(0);
             }
 
-            // ---- scale and duplicate counts; self penalty on the diagonal tile;
-            //      causal cut; running max
+            // ---- scale and duplicate counts; causal cut; at chunk 128 also the
+            //      self penalty and the running max (the separate passes below
+            //      make the compiler spill there)
+            constexpr bool SELF_BRANCH = C <= 64;
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
@@ -452,7 +454,7 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                             reinterpret_cast<const char*>(sm.neg_log2) + outs8);
                     }
                     float sc = fmaf(s[t][j], scale_log2, nlg);
-                    if (diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
+                    if (!SELF_BRANCH && diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
                     if constexpr (SAME) {
                         // another bucket: window ids differ by something other than 0 or 1
@@ -460,9 +462,31 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                         if ((unsigned)(kid - rq1) > 1u) sc = -INFINITY;
                     }
                     s[t][j] = sc;
-                    mx = fmaxf(mx, sc);
+                    if (!SELF_BRANCH) mx = fmaxf(mx, sc);
                 }
                 if (t % SGRP == SGRP - 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (SELF_BRANCH) {
+                // ---- self penalty.  The query's own key is in the current
+                //      chunk's tile CT + wave (the tile of this wave's query rows),
+                //      as key 4g + j == r16: a round's chunks hold distinct
+                //      positions, so that is the one key with kpos == qpos.  The
+                //      branch is uniform (the empty asm keeps it a branch instead
+                //      of selects on every tile).
+#pragma unroll
+                for (int w = 0; w < CT; ++w) {
+                    if (w == wave) {
+                        asm volatile("");
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (4 * g + j == r16) s[CT + w][j] -= SELF_PENALTY * LOG2E;
+                    }
+                }
+                // ---- running max
+#pragma unroll
+                for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[t][j]);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
