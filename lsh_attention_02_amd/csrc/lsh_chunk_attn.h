@@ -430,6 +430,16 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
             //      make the compiler spill there)
             constexpr bool SELF_BRANCH = C <= 64;
             float mx = -INFINITY;
+            // chunk 128, bf16 at d 64 with up to 8 rounds and no bucket test:
+            // the penalty of key 4g + j in the diagonal tile (the query itself
+            // when 4g + j == r16), added by one fma per current-chunk pair with
+            // a factor that is uniform over the wave (1 on the diagonal tile).
+            // The other chunk-128 kernels have no registers to spare for it
+            // and keep the compare and select.
+            constexpr bool SELF_FMA = C == 128 && D == 64 && sizeof(T) == 2 && !SAME && NDW <= 4;
+            float pen[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pen[j] = 4 * g + j == r16 ? -SELF_PENALTY * LOG2E : 0.f;
 #pragma unroll
             for (int t = 0; t < NKT; ++t) {
                 if (t < CT && !has_prev) {
@@ -454,7 +464,8 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
                             reinterpret_cast<const char*>(sm.neg_log2) + outs8);
                     }
                     float sc = fmaf(s[t][j], scale_log2, nlg);
-                    if (!SELF_BRANCH && diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
+                    if (SELF_FMA && t >= CT) sc = fmaf(diag ? 1.f : 0.f, pen[j], sc);
+                    if (!SELF_BRANCH && !SELF_FMA && diag && kpos == qpos) sc -= SELF_PENALTY * LOG2E;
                     if (causal && kpos > qpos) sc = -INFINITY;
                     if constexpr (SAME) {
                         // another bucket: window ids differ by something other than 0 or 1
