@@ -39,6 +39,9 @@ SMALL = {
     "chunk128_L2560": W("c128", heads=2, seq_len=2560, n_buckets=40, chunk=128, seed=103),
     "chunk128_d128_L2048_r3": W("c128d128", heads=2, seq_len=2048, d_head=128, n_buckets=32,
                                 n_rounds=3, chunk=128, seed=113),
+    # chunk 128 with 8 rounds (four packed chunk-id words) and several runs
+    "chunk128_L4096_r8": W("c128r8", heads=2, seq_len=4096, n_buckets=32, n_rounds=8, chunk=128,
+                           seed=114),
     "chunk32_noncausal_r5": W("c32", heads=2, seq_len=1056, n_buckets=16, n_rounds=5, chunk=32,
                               causal=False, seed=104),
     "f32_d128_r2_scale1": W("f32d128", seq_len=576, d_head=128, dtype="f32", n_buckets=16,
@@ -69,13 +72,14 @@ def test_full_parity(name):
 # Variant flags: LSH_FLAG_NO_DUP_CORRECTION (1), LSH_FLAG_WRAP_LOOKBACK (2), both,
 # LSH_FLAG_SAME_BUCKET (4) and 4 without the correction, on cases with several
 # 16-chunk attention runs (the wrapped look-back of chunk 0 and of every later
-# run), one chunk, 16 rounds, f32 and d128.
+# run), one chunk, 16 rounds, f32, d128 and bf16 chunk 128.
 FLAG_CASES = {
     "short_4k": WORKLOADS["short_4k"],
     "ragged_b2h3_L1344_nb10_r3": SMALL["ragged_b2h3_L1344_nb10_r3"],
     "d128_L2048_r4": SMALL["d128_L2048_r4"],
     "chunk32_noncausal_r5": SMALL["chunk32_noncausal_r5"],
     "f32_chunk128_d64": SMALL["f32_chunk128_d64"],
+    "chunk128_L2560": SMALL["chunk128_L2560"],
     "rounds16_buckets1000": SMALL["rounds16_buckets1000"],
     "one_chunk": SMALL["one_chunk"],
     "two_chunks_nb2": SMALL["two_chunks_nb2"],
