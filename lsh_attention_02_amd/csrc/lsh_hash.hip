@@ -61,12 +61,35 @@ __device__ __forceinline__ int swz(int c) { return (c ^ (c >> 3)) & (NP - 1); }
 
 // Global -> registers: block b of the group covers d-rows VE*(b / CB) .. +VE and
 // columns c0 + VE*(b % CB) .. +VE (one 16-byte load per d-row; consecutive
-// threads read consecutive column blocks of a row, coalesced).
+// threads read consecutive column blocks of a row, coalesced).  Returns the
+// mask of this thread's pieces that hold columns of R; stage_store zeroes the
+// others.  With 16-byte aligned rows every lane loads a valid piece (clamped
+// into the row) and nothing tests the loaded values here: a test would make
+// the wave wait for every load in flight, the next group's included.
 template <typename T, int D, int NREG>
-__device__ __forceinline__ void stage_load(u32x4 (&reg)[NREG], const T* __restrict__ Rr, int c0,
-                                           int ncol, bool vec_ok)
+__device__ __forceinline__ uint32_t stage_load(u32x4 (&reg)[NREG], const T* __restrict__ Rr, int c0,
+                                               int ncol, bool vec_ok)
 {
     using S = HashStage<T, D>;
+    static_assert(NREG == S::PER_THREAD * S::VE && NREG <= 32, "one mask bit per piece");
+    uint32_t valid = 0u;
+    // (bf16 comes here only with unaligned rows: k_hash_tr takes the others)
+    if (sizeof(T) == 4 && vec_ok) {                // ncol is a multiple of VE (and at least VE)
+#pragma unroll
+        for (int i = 0; i < S::PER_THREAD; ++i) {
+            const int b = threadIdx.x + i * HASH_THREADS;
+            const int bb = min(b, S::BLOCKS - 1);
+            const int c = c0 + S::VE * (bb % S::CB);
+            const int cc = min(c, ncol - S::VE);
+#pragma unroll
+            for (int y = 0; y < S::VE; ++y) {
+                const int d = S::VE * (bb / S::CB) + y;
+                reg[i * S::VE + y] = *reinterpret_cast<const u32x4*>(Rr + (long)d * ncol + cc);
+                if (b < S::BLOCKS && c < ncol) valid |= 1u << (i * S::VE + y);
+            }
+        }
+        return valid;
+    }
 #pragma unroll
     for (int i = 0; i < S::PER_THREAD; ++i) {
         const int b = threadIdx.x + i * HASH_THREADS;
@@ -77,32 +100,33 @@ __device__ __forceinline__ void stage_load(u32x4 (&reg)[NREG], const T* __restri
                 const int d = S::VE * (b / S::CB) + y;
                 const int c = c0 + S::VE * (b % S::CB);
                 const T* src = Rr + (long)d * ncol + c;
-                if (vec_ok && c + S::VE <= ncol) {
-                    v = *reinterpret_cast<const u32x4*>(src);
-                } else {
 #pragma unroll
-                    for (int x = 0; x < S::VE; ++x) {
-                        if (c + x < ncol) {
-                            uint32_t e;
-                            if constexpr (sizeof(T) == 2) e = reinterpret_cast<const uint16_t*>(src)[x];
-                            else e = __float_as_uint(reinterpret_cast<const float*>(src)[x]);
-                            if constexpr (sizeof(T) == 2) v[x >> 1] |= e << (16 * (x & 1));
-                            else v[x] = e;
-                        }
+                for (int x = 0; x < S::VE; ++x) {
+                    if (c + x < ncol) {
+                        uint32_t e;
+                        if constexpr (sizeof(T) == 2) e = reinterpret_cast<const uint16_t*>(src)[x];
+                        else e = __float_as_uint(reinterpret_cast<const float*>(src)[x]);
+                        if constexpr (sizeof(T) == 2) v[x >> 1] |= e << (16 * (x & 1));
+                        else v[x] = e;
                     }
                 }
             }
             reg[i * S::VE + y] = v;
         }
     }
+    return ~0u;                                    // zero-filled element by element
 }
 
 // Registers -> LDS: transpose each VE x VE block in registers; column x of the
-// block becomes one 16-byte piece (VE consecutive d) of R^T row c.
+// block becomes one 16-byte piece (VE consecutive d) of R^T row c.  Pieces
+// outside stage_load's mask (columns past ncol) are stored as zeros.
 template <typename T, int D, int NREG>
-__device__ __forceinline__ void stage_store(const u32x4 (&reg)[NREG], char* buf)
+__device__ __forceinline__ void stage_store(u32x4 (&reg)[NREG], uint32_t valid, char* buf)
 {
     using S = HashStage<T, D>;
+#pragma unroll
+    for (int k = 0; k < NREG; ++k)
+        if (!((valid >> k) & 1u)) reg[k] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < S::PER_THREAD; ++i) {
         const int b = threadIdx.x + i * HASH_THREADS;
@@ -146,13 +170,30 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     const int tok0 = (blockIdx.x % tiles_per_bh) * HASH_TOK_WG + wave * HASH_NT * 32;
     const T* q = qk + bh * (long)L * D;
 
+    // float: step ks takes d = 8 (ks / 4) + 4 hh + ks % 4 (the contraction order
+    // is free as long as both operands use it), so a lane reads 4 consecutive
+    // d per 4 steps, one 16-byte load, instead of one 4-byte load per step:
+    // many narrow loads of scattered rows queue in the CU's address unit.
+    // Tokens past L read row L - 1; their buckets are never stored.  Not at
+    // d 128, whose 64 steps of operands do not fit in registers either way
+    // (this order would raise the spill).
+    constexpr bool F4 = sizeof(T) == 4 && D == 64;
     typename M::Frag bq[HASH_NT][NKS];
 #pragma unroll
     for (int u = 0; u < HASH_NT; ++u) {
         const int tok = tok0 + 32 * u + n;
+        if constexpr (F4) {
+            const float* row = reinterpret_cast<const float*>(q) + (long)min(tok, L - 1) * D + 4 * hh;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            bq[u][ks] = tok < L ? M::load(q + (long)tok * D + ks * KSTEP + hh * KPL) : M::zero();
+            for (int m = 0; m < NKS / 4; ++m) {
+                const float4 v = *reinterpret_cast<const float4*>(row + 8 * m);
+                bq[u][4 * m] = v.x; bq[u][4 * m + 1] = v.y; bq[u][4 * m + 2] = v.z; bq[u][4 * m + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                bq[u][ks] = tok < L ? M::load(q + (long)tok * D + ks * KSTEP + hh * KPL) : M::zero();
+        }
     }
 
     const int groups_per_round = (ncol + GROUP_COLS - 1) / GROUP_COLS;
@@ -160,8 +201,8 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
     const bool vec_ok = (ncol % S::VE) == 0;           // 16-byte aligned R rows
 
     u32x4 reg[S::PER_THREAD * S::VE];
-    stage_load<T, D>(reg, R, 0, ncol, vec_ok);
-    stage_store<T, D>(reg, rt[0]);
+    uint32_t rvalid = stage_load<T, D>(reg, R, 0, ncol, vec_ok);
+    stage_store<T, D>(reg, rvalid, rt[0]);
     __syncthreads();
 
     // Per token tile u, over the round so far: the largest |p| among this lane's
@@ -199,10 +240,10 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
         if (g + 1 < ngroups) {
             const int r1 = (g + 1) / groups_per_round;
             const int c1 = ((g + 1) % groups_per_round) * GROUP_COLS;
-            stage_load<T, D>(reg, R + (long)r1 * D * ncol, c1, ncol, vec_ok);
+            rvalid = stage_load<T, D>(reg, R + (long)r1 * D * ncol, c1, ncol, vec_ok);
         }
         const char* buf = rt[g & 1];
-        // R^T rows past ncol hold zeros (stage_load), so their projections are
+        // R^T rows past ncol hold zeros (stage_store), so their projections are
         // exactly 0 and can never beat a record: no column test is needed.
         const int tiles = min(GROUP_TILES, (ncol - c0 + 31) >> 5);
 #pragma unroll
@@ -220,6 +261,16 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         a[ks] = *reinterpret_cast<const typename M::Frag*>(tb + off0[ks ^ kx]);
+                } else if constexpr (F4) {
+                    // the d order of bq: piece 2m + hh of the row holds steps 4m .. 4m+3
+                    const int c = ct * 32 + n;
+                    const char* rowp = buf + c * S::ROWB;
+                    const int sw = swz<S::NP>(c);
+#pragma unroll
+                    for (int m = 0; m < NKS / 4; ++m) {
+                        const float4 v = *reinterpret_cast<const float4*>(rowp + 16 * ((2 * m + hh) ^ sw));
+                        a[4 * m] = v.x; a[4 * m + 1] = v.y; a[4 * m + 2] = v.z; a[4 * m + 3] = v.w;
+                    }
                 } else {
                     const int c = ct * 32 + n;
                     const char* rowp = buf + c * S::ROWB;
@@ -274,7 +325,7 @@ void k_hash(const T* __restrict__ qk, const T* __restrict__ R, int32_t* __restri
                     buckets[((long)bh * n_r + r) * L + tok] = bi + (bv < 0.f ? ncol : 0);
             }
         }
-        if (g + 1 < ngroups) stage_store<T, D>(reg, rt[(g + 1) & 1]);
+        if (g + 1 < ngroups) stage_store<T, D>(reg, rvalid, rt[(g + 1) & 1]);
         __syncthreads();
     }
 }
