@@ -36,6 +36,7 @@
 #include "lsh_device.h"
 #include "lsh_internal.h"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -884,6 +885,17 @@ SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket
     };
     SortPlan p;
     long tile = tile_for(2);
+    // Small problems: k_sort_place2 runs one workgroup per (b, h, group of
+    // rounds, tile), and a wave walks its tile in steps of 64 positions; halve
+    // the tile (down to 2 positions per bucket and 64 positions) while that
+    // leaves fewer workgroups than CUs, so the placement spreads over the GPU
+    // instead of walking long tiles on a few CUs.
+    auto place2_wgs = [&](long t) -> long {
+        const int rg2 = place2_rounds_per_group(n_buckets, (int)t, n_rounds);
+        return rg2 > 0 ? bh * (n_rounds / rg2) * ((L + t - 1) / t) : 0;
+    };
+    while (place2_wgs(tile) > 0 && place2_wgs(tile) < 256 && tile / 2 >= std::max(64L, 2L * n_buckets))
+        tile /= 2;
     p.rounds_per_group = place_rounds_per_group(n_buckets, (int)tile, n_rounds, same_bucket);
     if (p.rounds_per_group == 0) tile = tile_for(4);
     p.tile = (int)tile;

@@ -258,11 +258,14 @@ def test_ffn_checks(lib):
 def test_sort_workspace(lib):
     # tile = smallest power of two >= max(2048, 2 * n_buckets) where a workgroup's
     # rounds fit in LDS, else >= max(2048, 4 * n_buckets); at most 65536, at most L.
+    # With up to 1024 buckets the tile is then halved, down to max(64, 2 * n_buckets),
+    # while the placement has fewer than 256 workgroups (one per (b, h, group of
+    # rounds, tile); all rounds of a tile in one group at these sizes).
     # One int32 counter per (segment, tile, bucket).
-    cases = [(dict(), 1 * 8 * 2 * 2 * 64),
+    cases = [(dict(), 1 * 8 * 2 * 32 * 64),                          # tile 128: 8 x 32 workgroups
              (dict(seq_len=65536, d_head=128, n_buckets=1024, n_rounds=8), 8 * 8 * 32 * 1024),
              (dict(seq_len=1 << 20, n_buckets=16384, n_rounds=4, chunk=128), 8 * 4 * 16 * 16384),
-             (dict(seq_len=1024, n_buckets=32, n_rounds=1, heads=1), 1 * 1 * 1 * 32)]
+             (dict(seq_len=1024, n_buckets=32, n_rounds=1, heads=1), 1 * 1 * 16 * 32)]   # tile 64
     # plus one int32 per (segment, bucket): the bucket totals (or, with the
     # same-bucket variant, possibly its bucket ranks)
     for flags in (0, B.LSH_FLAG_SAME_BUCKET):
