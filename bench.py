@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload paper_64k]
 
 One step = the four calls over one batch of synthetic input already resident in
-HBM.  Prints one JSON line.  Per-call times come from HIP events recorded on the
-stream the calls are launched on.  `roofline` describes the call with the
+HBM.  Prints one JSON line.  The K timed steps are bracketed by two HIP events
+and nothing else; per-call times come from a second pass of K steps with an
+event pair around every call (event records cost host time, which a small step,
+bound by the host time of its calls, would otherwise include).  `roofline` describes the call with the
 largest time: achieved = algorithmic bytes (or FLOPs) per launch / its average
 duration.  `traffic` is the HBM traffic per launch of that kernel measured with
 rocprofv3 counters (profiles/pmc_traffic.json), or null when those counters were
@@ -352,8 +354,9 @@ def trace_summary(workload, stats_csv, bench_log, command, out_md, title="forwar
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
-    out += ["", "Per-call averages the same run printed (HIP events on the launch stream, timed "
-                "steps only), with each call's fraction of the MFMA and HBM peaks:", "",
+    out += ["", "Per-call averages the same run printed (HIP events on the launch stream, from a "
+                "pass of as many steps after the timed ones), with each call's fraction of the "
+                "MFMA and HBM peaks:", "",
             "| call | ms | MFMA fraction | HBM fraction |", "|---|---|---|---|"]
     for n, e in res["kernels"].items():
         out.append(f"| {n} | {e['ms']:.4f} | {e['mfma_frac']:.3f} | {e['hbm_frac']:.3f} |")
@@ -556,15 +559,19 @@ def main():
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
-              for _ in range(args.steps)]
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(stream)
         for k in range(args.steps):
-            step(ev[k])
+            step()
         end.record(stream)
+        torch.cuda.synchronize()
+        # per-call times: the same number of steps again, an event pair around each call
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+              for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(ev[k])
         torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps

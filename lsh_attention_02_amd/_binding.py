@@ -10,6 +10,7 @@ There is no fallback: if the library is missing, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import dataclasses
 import math
 import os
@@ -146,11 +147,12 @@ def _empty(shape, dtype: torch.dtype, device, stream=None) -> torch.Tensor:
 def _expect(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device=None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
-    if device is not None and t.device != device:
+    if device is not None and (t.get_device() != device.index if device.index is not None
+                               else t.device != device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -158,6 +160,14 @@ def _expect(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device=None) 
         raise ValueError(f"{name} must be contiguous")
 
 
+@functools.lru_cache(maxsize=256)
+def _cconfig(cfg: LSHConfig) -> CConfig:
+    """The C struct of a config, built once per config (the library only reads
+    it), since a small step is bound by the host time of its calls."""
+    return cfg.to_c()
+
+
+@functools.lru_cache(maxsize=256)
 def _shapes(cfg: LSHConfig):
     B, H, L, d, nr = cfg.batch, cfg.heads, cfg.seq_len, cfg.d_head, cfg.n_rounds
     return {"qk": (B, H, L, d), "v": (B, H, L, d), "R": (nr, d, cfg.n_buckets // 2),
@@ -175,14 +185,14 @@ def lsh_hash(cfg: LSHConfig, qk: torch.Tensor, R: torch.Tensor,
     if buckets is None:
         buckets = _empty(sh["buckets"], torch.int32, qk.device, stream)
     _expect(buckets, "buckets", sh["buckets"], torch.int32, qk.device)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_hash(ctypes.byref(c), _ptr(qk), _ptr(R), _ptr(buckets),
                         _stream(qk.device, stream)), "lsh_hash")
     return buckets
 
 
 def lsh_sort_workspace_bytes(cfg: LSHConfig) -> int:
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     return int(load_library().lsh_sort_workspace_bytes(ctypes.byref(c)))
 
 
@@ -212,7 +222,7 @@ def lsh_sort(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch.Tensor]
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous buffer on the same device")
     nbytes = workspace.numel() * workspace.element_size()
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_sort(ctypes.byref(c), _ptr(buckets), _ptr(perm), _ptr(cid), _ptr(workspace),
                         ctypes.c_size_t(nbytes), _stream(dev, stream)), "lsh_sort")
     return perm, cid
@@ -238,7 +248,7 @@ def lsh_sort_noalloc(cfg: LSHConfig, buckets: torch.Tensor, perm: Optional[torch
         cid = _empty(sh["cid"], torch.int16, dev, stream)
     _expect(perm, "perm", sh["perm"], torch.int32, dev)
     _expect(cid, "cid", sh["cid"], torch.int16, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_sort_noalloc(ctypes.byref(c), _ptr(buckets), _ptr(perm), _ptr(cid),
                                 _stream(dev, stream)), "lsh_sort_noalloc")
     return perm, cid
@@ -261,7 +271,7 @@ def lsh_chunk_attn(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: torc
         lse = _empty(sh["lse"], torch.float32, dev, stream)
     _expect(o_rounds, "o_rounds", sh["o_rounds"], cfg.torch_dtype, dev)
     _expect(lse, "lse", sh["lse"], torch.float32, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_chunk_attn(ctypes.byref(c), _ptr(qk), _ptr(v), _ptr(perm), _ptr(cid),
                               _ptr(o_rounds), _ptr(lse), _stream(dev, stream)), "lsh_chunk_attn")
     return o_rounds, lse
@@ -278,14 +288,14 @@ def lsh_combine_rounds(cfg: LSHConfig, o_rounds: torch.Tensor, lse: torch.Tensor
     if o is None:
         o = _empty(sh["o"], cfg.torch_dtype, dev, stream)
     _expect(o, "o", sh["o"], cfg.torch_dtype, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_combine_rounds(ctypes.byref(c), _ptr(o_rounds), _ptr(lse), _ptr(o),
                                   _stream(dev, stream)), "lsh_combine_rounds")
     return o
 
 
 def lsh_backward_workspace_bytes(cfg: LSHConfig) -> int:
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     return int(load_library().lsh_backward_workspace_bytes(ctypes.byref(c)))
 
 
@@ -322,7 +332,7 @@ def lsh_attn_backward(cfg: LSHConfig, qk: torch.Tensor, v: torch.Tensor, perm: t
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous buffer on the same device")
     nbytes = workspace.numel() * workspace.element_size()
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_attn_backward(ctypes.byref(c), _ptr(qk), _ptr(v), _ptr(perm), _ptr(cid),
                                  _ptr(lse), _ptr(o), _ptr(d_o), _ptr(d_qk), _ptr(d_v),
                                  _ptr(workspace), ctypes.c_size_t(nbytes), _stream(dev, stream)),
@@ -361,7 +371,7 @@ def lsh_project_in(cfg: LSHConfig, d_model: int, x: torch.Tensor, w_qk: torch.Te
         v = _empty(sh["v"], cfg.torch_dtype, dev, stream)
     _expect(qk, "qk", sh["qk"], cfg.torch_dtype, dev)
     _expect(v, "v", sh["v"], cfg.torch_dtype, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_project_in(ctypes.byref(c), int(d_model), _ptr(x), _ptr(w_qk), _ptr(w_v),
                               _ptr(qk), _ptr(v), _stream(dev, stream)), "lsh_project_in")
     return qk, v
@@ -379,7 +389,7 @@ def lsh_project_out(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torch.Te
     if y is None:
         y = _empty((cfg.batch, cfg.seq_len, d_model), cfg.torch_dtype, dev, stream)
     _expect(y, "y", (cfg.batch, cfg.seq_len, d_model), cfg.torch_dtype, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_project_out(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(y),
                                _stream(dev, stream)), "lsh_project_out")
     return y
@@ -399,7 +409,7 @@ def lsh_project_out_add(cfg: LSHConfig, d_model: int, o: torch.Tensor, w_o: torc
     if y is None:
         y = _empty(shape, cfg.torch_dtype, dev, stream)
     _expect(y, "y", shape, cfg.torch_dtype, dev)
-    c = cfg.to_c()
+    c = _cconfig(cfg)
     _check(lib.lsh_project_out_add(ctypes.byref(c), int(d_model), _ptr(o), _ptr(w_o), _ptr(residual),
                                    ctypes.c_float(sign), _ptr(y), _stream(dev, stream)),
            "lsh_project_out_add")
