@@ -36,6 +36,7 @@
 // one byte permute per two words gathers the flags and v_bcnt counts them.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "lsh_device.h"
@@ -58,6 +59,43 @@ inline int run_length(int nchunks, long segments)
 {
     const long len = ((long)nchunks * segments + RUN_TARGET_WGS - 1) / RUN_TARGET_WGS;
     return (int)(len < 1 ? 1 : len > RUN ? RUN : len);
+}
+
+// The forward's run length: a workgroup's time grows with its run (one step
+// per chunk, plus its look-back), and the launch takes as many rounds of
+// workgroups as it has workgroups per `slots` (the workgroups the GPU holds at
+// once); take the run of 1 .. RUN_MAX chunks with the fewest rounds x steps
+// (the shorter on a tie).  A round only partly filled costs almost a whole
+// one: clustered_16k's 1024 workgroups of 16 chunks on 768 slots took two,
+// 768 of 22 one, 11% faster.
+constexpr int RUN_MAX = 32;
+
+inline int run_length_fit(int nchunks, long segments, long slots)
+{
+    int best = 1;
+    long best_cost = -1;
+    for (int len = 1; len <= RUN_MAX; ++len) {
+        const long wgs = segments * ((nchunks + len - 1) / len);
+        const long cost = ((wgs + slots - 1) / slots) * (len + 1);
+        if (best_cost < 0 || cost < best_cost) { best = len; best_cost = cost; }
+        if (len >= nchunks) break;
+    }
+    return best;
+}
+
+// Compute units of the current device (queried once per device).
+inline int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
 __device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b)
@@ -631,7 +669,15 @@ hipError_t launch_one(const void* qk, const void* v, const int32_t* perm, const 
                       hipStream_t s)
 {
     const int nchunks = L / C;
-    const int run_len = run_length(nchunks, bh * n_r);
+    // workgroups per CU of this kernel (registers and LDS), computed once
+    static const int per_cu = [] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void*)k_chunk_attn<T, D, C, NDW, WRAP, SAME>,
+                                                         4 * C, 0) != hipSuccess || b < 1)
+            b = 1;
+        return b;
+    }();
+    const int run_len = run_length_fit(nchunks, bh * n_r, (long)per_cu * device_cus());
     const int nruns = (nchunks + run_len - 1) / run_len;
     const long blocks = bh * nruns * n_r;
     hipLaunchKernelGGL((k_chunk_attn<T, D, C, NDW, WRAP, SAME>), dim3((unsigned)blocks), dim3(4 * C), 0, s,
