@@ -395,7 +395,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="paper_64k")
     ap.add_argument("--flags", type=int, default=0,
                     help="LSH_FLAG_* bits for the attention variants (0: the method as described)")
