@@ -291,7 +291,12 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     const int r = bid % n_r;
     bid /= n_r;
     const int run = bid % nruns;
-    const long bh = bid / nruns;
+    // (batch row, head) pairs in descending order: the hash reads them in
+    // ascending order and the combine that follows does too, so the first
+    // heads walked here are the ones whose qk the hash read last, and the last
+    // ones written here are the combine's first reads; both still sit in the
+    // Infinity Cache at small enough sizes
+    const long bh = (long)(gridDim.x / ((unsigned)nruns * (unsigned)n_r)) - 1 - bid / nruns;
     const int nchunks = L / C;
     const int k0 = run * run_len, k1 = min(k0 + run_len, nchunks);
 
