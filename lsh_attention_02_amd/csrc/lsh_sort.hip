@@ -765,19 +765,32 @@ void k_sort_place2(const int32_t* __restrict__ buckets, const int32_t* __restric
     }
     const int nvalid = (int)nvalid_u;
 
-    // 4. each position to its sorted index (stg) and its cid value (bt)
+    // 4. each position to its sorted index (stg) and its cid value (bt).  The
+    //    table entries of 8 steps are read before their stores: the compiler
+    //    cannot tell that the stores (stg, bt) miss the table, so a read after
+    //    a store would wait for it, one LDS round trip per step
+    constexpr int PB = BPL < 8 ? BPL : 8;
 #pragma unroll
-    for (int k = 0; k < BPL; ++k) {
-        const int p = 64 * k + lane;
-        const int b = bv[k] & 0xFFFF;
-        const bool ok = b < nb;
-        const uint2 e = *reinterpret_cast<const uint2*>(&tab[2 * (ok ? b : 0)]);
-        const uint32_t li = (e.x & 0xFFFFu) + ((uint32_t)bv[k] >> 16);
-        const uint32_t slot = li + e.y;
-        uint32_t id = chunk_shift >= 0 ? slot >> chunk_shift : slot / (uint32_t)chunk;
-        if constexpr (SAME) id += e.x >> 16;
-        if (ok) stg[li] = ((uint32_t)b << 16) | (uint32_t)p;
-        if (p < P) bt[p] = ok ? (uint16_t)id : (uint16_t)0xFFFF;
+    for (int k0 = 0; k0 < BPL; k0 += PB) {
+        uint2 e[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = bv[k0 + j] & 0xFFFF;
+            e[j] = *reinterpret_cast<const uint2*>(&tab[2 * (b < nb ? b : 0)]);
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int k = k0 + j;
+            const int p = 64 * k + lane;
+            const int b = bv[k] & 0xFFFF;
+            const bool ok = b < nb;
+            const uint32_t li = (e[j].x & 0xFFFFu) + ((uint32_t)bv[k] >> 16);
+            const uint32_t slot = li + e[j].y;
+            uint32_t id = chunk_shift >= 0 ? slot >> chunk_shift : slot / (uint32_t)chunk;
+            if constexpr (SAME) id += e[j].x >> 16;
+            if (ok) stg[li] = ((uint32_t)b << 16) | (uint32_t)p;
+            if (p < P) bt[p] = ok ? (uint16_t)id : (uint16_t)0xFFFF;
+        }
     }
 
     // 5. perm in sorted order (each bucket's run of slots is contiguous)
