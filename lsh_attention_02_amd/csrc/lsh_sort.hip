@@ -2,26 +2,31 @@
 // (ai-scholar Reformer article, section on LSH attention; modulabs-hub notes,
 // "LSH attention": tokens sorted by bucket, then cut into equal chunks).
 //
-// Counting sort in three launches:
-//   k_sort_hist     one workgroup per (segment, tile of positions): LDS
-//                   histogram of the tile's buckets -> counters[seg][tile][bucket]
-//   k_sort_scan     one workgroup per segment: counters become the first slot
-//                   of each (tile, bucket): sum of all earlier buckets plus the
-//                   same bucket in earlier tiles
-//   k_sort_place    one workgroup per (batch row, head, tile, group of rounds),
-//                   one wave per round.  The wave reads its round's buckets of
-//                   the tile into LDS, orders the tile by bucket there (stable:
-//                   positions are ranked in increasing order, equal buckets
-//                   inside a wave by ballots), then writes perm in that order,
-//                   so that each bucket's slots of the tile are one contiguous
-//                   run of stores.  The chunk ids of the tile's positions stay
-//                   in LDS until every round of the group is placed and are
-//                   written as whole rows of cid.
-//   k_sort_scatter  (used instead of k_sort_place when a round's tile does not
-//                   fit in LDS: many buckets with large tiles) one workgroup per
-//                   (segment, tile): walks the tile 256 positions at a time,
-//                   equal buckets ranked by lane with ballots, the four waves
-//                   taking their offsets in order (barrier phases).
+// Counting sort in two or three launches.  Counting:
+//   k_sort_count    one workgroup per segment, where every tile's histogram of
+//                   the segment fits in LDS: counts per (tile, bucket), then
+//                   the column prefixes (the bucket in earlier tiles) and the
+//                   bucket totals
+//   k_sort_hist     otherwise: one workgroup per (segment, tile of positions),
+//                   LDS histogram of the tile -> counters[seg][tile][bucket];
+//                   then k_sort_colscan (column prefixes and totals, for the
+//                   placement kernels) or k_sort_scan (first slot of each
+//                   (tile, bucket), for k_sort_scatter)
+// Placement:
+//   k_sort_place2 / k_sort_place
+//                   one workgroup per (batch row, head, tile, group of rounds),
+//                   one wave per round.  The wave orders its round's buckets
+//                   of the tile (stable: positions are ranked in increasing
+//                   order, equal buckets inside a wave found by ballots), then
+//                   writes perm in that order, so that each bucket's slots of
+//                   the tile are one contiguous run of stores.  The chunk ids
+//                   of the tile's positions stay in LDS until every round of
+//                   the group is placed and are written as whole rows of cid.
+//   k_sort_scatter  (when a round's tile does not fit in LDS: many buckets with
+//                   large tiles) one workgroup per (segment, tile): walks the
+//                   tile 256 positions at a time, equal buckets ranked by lane
+//                   with ballots, the four waves taking their offsets in order
+//                   (barrier phases).
 // Outputs: perm[seg][slot] = position and cid[b,h][position][round] = slot / chunk
 // (with the same-bucket variant: slot / chunk + 2 * rank of the bucket among the
 // segment's non-empty buckets, computed by the scan).
@@ -268,6 +273,70 @@ void k_sort_colscan(int32_t* __restrict__ counters, int32_t* __restrict__ totals
             }
     }
     totals[seg * nb + b] = run;
+}
+
+// ---------------------------------------------------------------------------
+// k_sort_count: k_sort_hist and k_sort_colscan in one launch, where every tile's
+// histogram of a segment fits in LDS as 16-bit counts (tiles of at most 32768
+// positions).  One workgroup per segment: the whole segment's buckets are
+// counted per (tile, bucket) in LDS, then thread b writes the column prefix of
+// bucket b (its count in the earlier tiles) for every tile, and its total.  The
+// counters go to HBM once, instead of being written, re-read and rewritten.
+constexpr int COUNT_THREADS = 1024;
+constexpr int COUNT_LOADS = 16;            // loads in flight per thread
+constexpr size_t COUNT_LDS_LIMIT = 128 * 1024;
+
+__global__ __launch_bounds__(COUNT_THREADS)
+void k_sort_count(const int32_t* __restrict__ buckets, int32_t* __restrict__ colpre,
+                  int32_t* __restrict__ totals, int L, int nb, int tile_shift, int ntiles)
+{
+    extern __shared__ uint32_t cnt2[];          // [tile][bucket / 2]: two 16-bit counts per word
+    const long seg = blockIdx.x;
+    const int half = nb >> 1;                   // nb is even
+    for (int i = threadIdx.x; i < ntiles * half; i += COUNT_THREADS) cnt2[i] = 0u;
+    __syncthreads();
+    const int32_t* bk = buckets + seg * (long)L;
+    auto add = [&](int p, int b) __attribute__((always_inline)) {
+        if ((unsigned)b < (unsigned)nb)
+            atomicAdd(&cnt2[(p >> tile_shift) * half + (b >> 1)], 1u << ((b & 1) << 4));
+    };
+    if ((L & 3) == 0) {                         // 16-byte aligned rows: 4 positions per load
+        const int L4 = L >> 2;
+        for (int i0 = threadIdx.x; i0 < L4; i0 += COUNT_LOADS * COUNT_THREADS) {
+            int4 v[COUNT_LOADS];
+#pragma unroll
+            for (int k = 0; k < COUNT_LOADS; ++k)
+                v[k] = reinterpret_cast<const int4*>(bk)[min(i0 + k * COUNT_THREADS, L4 - 1)];
+#pragma unroll
+            for (int k = 0; k < COUNT_LOADS; ++k) {
+                if (i0 + k * COUNT_THREADS < L4) {
+                    const int p = 4 * (i0 + k * COUNT_THREADS);
+                    add(p, v[k].x); add(p + 1, v[k].y); add(p + 2, v[k].z); add(p + 3, v[k].w);
+                }
+            }
+        }
+    } else {
+        for (int i0 = threadIdx.x; i0 < L; i0 += COUNT_LOADS * COUNT_THREADS) {
+            int v[COUNT_LOADS];
+#pragma unroll
+            for (int k = 0; k < COUNT_LOADS; ++k) v[k] = bk[min(i0 + k * COUNT_THREADS, L - 1)];
+#pragma unroll
+            for (int k = 0; k < COUNT_LOADS; ++k)
+                if (i0 + k * COUNT_THREADS < L) add(i0 + k * COUNT_THREADS, v[k]);
+        }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < nb; b += COUNT_THREADS) {
+        int32_t* cp = colpre + seg * (long)ntiles * nb + b;
+        const int sh = (b & 1) << 4;
+        uint32_t run = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const uint32_t c = (cnt2[t * half + (b >> 1)] >> sh) & 0xFFFFu;
+            cp[(long)t * nb] = (int32_t)run;
+            run += c;
+        }
+        totals[seg * (long)nb + b] = (int32_t)run;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -931,6 +1000,8 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * sizeof(int));
         (void)hipFuncSetAttribute((const void*)k_sort_scatter,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * sizeof(int));
+        (void)hipFuncSetAttribute((const void*)k_sort_count,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)COUNT_LDS_LIMIT);
         (void)hipFuncSetAttribute((const void*)k_sort_place<false>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)PLACE_LDS_LIMIT);
         (void)hipFuncSetAttribute((const void*)k_sort_place<true>,
@@ -948,13 +1019,25 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
     int nbits = 0;
     while ((1 << nbits) < n_buckets) ++nbits;
     const unsigned blocks = (unsigned)(plan.nseg * plan.ntiles);
-    hipLaunchKernelGGL(k_sort_hist, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters, L,
-                       n_buckets, plan.tile, plan.ntiles);
     const int rg = plan.rounds_per_group;
+    // the placement kernels take column prefixes and totals: from k_sort_count
+    // where the tile histograms fit in LDS (tile a power of two, or one tile)
+    const size_t count_lds = (size_t)plan.ntiles * n_buckets * sizeof(uint16_t);
+    const bool pow2_tile = (plan.tile & (plan.tile - 1)) == 0;
+    if (rg > 0 && plan.tile <= 32768 && count_lds <= COUNT_LDS_LIMIT && (pow2_tile || plan.ntiles == 1)) {
+        const int tile_shift = plan.ntiles == 1 ? 30 : __builtin_ctz((unsigned)plan.tile);
+        hipLaunchKernelGGL(k_sort_count, dim3((unsigned)plan.nseg), dim3(COUNT_THREADS), count_lds, s, buckets,
+                           counters, extra, L, n_buckets, tile_shift, plan.ntiles);
+    } else {
+        hipLaunchKernelGGL(k_sort_hist, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters, L,
+                           n_buckets, plan.tile, plan.ntiles);
+        if (rg > 0) {
+            const int bps = (n_buckets + COLSCAN_THREADS - 1) / COLSCAN_THREADS;
+            hipLaunchKernelGGL(k_sort_colscan, dim3((unsigned)(plan.nseg * bps)), dim3(COLSCAN_THREADS), 0, s,
+                               counters, extra, n_buckets, plan.ntiles, bps);
+        }
+    }
     if (rg > 0) {
-        const int bps = (n_buckets + COLSCAN_THREADS - 1) / COLSCAN_THREADS;
-        hipLaunchKernelGGL(k_sort_colscan, dim3((unsigned)(plan.nseg * bps)), dim3(COLSCAN_THREADS), 0, s,
-                           counters, extra, n_buckets, plan.ntiles, bps);
         const int shift = (chunk & (chunk - 1)) == 0 ? __builtin_ctz((unsigned)chunk) : -1;
         const int rg2 = place2_rounds_per_group(n_buckets, plan.tile, n_rounds);
         if (rg2 > 0) {
