@@ -278,27 +278,37 @@ void k_sort_colscan(int32_t* __restrict__ counters, int32_t* __restrict__ totals
 // ---------------------------------------------------------------------------
 // k_sort_count: k_sort_hist and k_sort_colscan in one launch, where every tile's
 // histogram of a segment fits in LDS as 16-bit counts (tiles of at most 32768
-// positions).  One workgroup per segment: the whole segment's buckets are
-// counted per (tile, bucket) in LDS, then thread b writes the column prefix of
+// positions).  A segment's buckets are split into nsplit equal ranges, one
+// workgroup each: it reads all of the segment's buckets, counts those in its
+// range per (tile, bucket) in LDS, then thread b writes the column prefix of
 // bucket b (its count in the earlier tiles) for every tile, and its total.  The
-// counters go to HBM once, instead of being written, re-read and rewritten.
+// counters go to HBM once, instead of being written, re-read and rewritten.  The
+// workgroups of one segment run on one XCD, so that all but the first read of
+// its buckets come from that XCD's L2 (see ScatterMap).
 constexpr int COUNT_THREADS = 1024;
 constexpr int COUNT_LOADS = 16;            // loads in flight per thread
 constexpr size_t COUNT_LDS_LIMIT = 128 * 1024;
 
 __global__ __launch_bounds__(COUNT_THREADS)
 void k_sort_count(const int32_t* __restrict__ buckets, int32_t* __restrict__ colpre,
-                  int32_t* __restrict__ totals, int L, int nb, int tile_shift, int ntiles)
+                  int32_t* __restrict__ totals, long nseg, int L, int nb, int tile_shift, int ntiles,
+                  int nsplit)
 {
-    extern __shared__ uint32_t cnt2[];          // [tile][bucket / 2]: two 16-bit counts per word
-    const long seg = blockIdx.x;
-    const int half = nb >> 1;                   // nb is even
+    extern __shared__ uint32_t cnt2[];          // [tile][bucket / 2 in the range]: two 16-bit counts
+    const int xcd = blockIdx.x % NXCD;
+    const long j = blockIdx.x / NXCD;
+    const long seg = (j / nsplit) * NXCD + xcd;
+    if (seg >= nseg) return;                    // padding of the last row of segments
+    const int bsz = nb / nsplit;                // even
+    const int b0 = (int)(j % nsplit) * bsz;
+    const int half = bsz >> 1;
     for (int i = threadIdx.x; i < ntiles * half; i += COUNT_THREADS) cnt2[i] = 0u;
     __syncthreads();
     const int32_t* bk = buckets + seg * (long)L;
     auto add = [&](int p, int b) __attribute__((always_inline)) {
-        if ((unsigned)b < (unsigned)nb)
-            atomicAdd(&cnt2[(p >> tile_shift) * half + (b >> 1)], 1u << ((b & 1) << 4));
+        const unsigned x = (unsigned)(b - b0);
+        if (x < (unsigned)bsz)
+            atomicAdd(&cnt2[(p >> tile_shift) * half + (x >> 1)], 1u << ((x & 1) << 4));
     };
     if ((L & 3) == 0) {                         // 16-byte aligned rows: 4 positions per load
         const int L4 = L >> 2;
@@ -326,17 +336,32 @@ void k_sort_count(const int32_t* __restrict__ buckets, int32_t* __restrict__ col
         }
     }
     __syncthreads();
-    for (int b = threadIdx.x; b < nb; b += COUNT_THREADS) {
-        int32_t* cp = colpre + seg * (long)ntiles * nb + b;
-        const int sh = (b & 1) << 4;
+    for (int x = threadIdx.x; x < bsz; x += COUNT_THREADS) {
+        int32_t* cp = colpre + seg * (long)ntiles * nb + b0 + x;
+        const int sh = (x & 1) << 4;
         uint32_t run = 0;
         for (int t = 0; t < ntiles; ++t) {
-            const uint32_t c = (cnt2[t * half + (b >> 1)] >> sh) & 0xFFFFu;
+            const uint32_t c = (cnt2[t * half + (x >> 1)] >> sh) & 0xFFFFu;
             cp[(long)t * nb] = (int32_t)run;
             run += c;
         }
-        totals[seg * (long)nb + b] = (int32_t)run;
+        totals[seg * (long)nb + b0 + x] = (int32_t)run;
     }
+}
+
+// Bucket ranges per segment for k_sort_count.  Long segments (at least 32768
+// positions) are split until the workgroups cover the CUs, up to 4 ranges of an
+// even number of buckets: at 64K positions, 64 segments and 1024 buckets, 4
+// ranges measured 11.2 us against 12.0 for one (more ranges were slower: each
+// workgroup still issues an LDS atomic instruction per 64 positions, with
+// fewer lanes active).  Shorter segments, and skewed bucket counts (most
+// positions in a few buckets, whose range then holds most of the atomics),
+// gained nothing from splitting.
+inline int count_splits(long nseg, int nb, int L)
+{
+    int s = 1;
+    while (L >= 32768 && s < 4 && nseg * s < 256 && (nb / (2 * s)) % 2 == 0) s *= 2;
+    return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1022,12 +1047,14 @@ hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int3
     const int rg = plan.rounds_per_group;
     // the placement kernels take column prefixes and totals: from k_sort_count
     // where the tile histograms fit in LDS (tile a power of two, or one tile)
-    const size_t count_lds = (size_t)plan.ntiles * n_buckets * sizeof(uint16_t);
+    const int nsplit = count_splits(plan.nseg, n_buckets, L);
+    const size_t count_lds = (size_t)plan.ntiles * (n_buckets / nsplit) * sizeof(uint16_t);
     const bool pow2_tile = (plan.tile & (plan.tile - 1)) == 0;
     if (rg > 0 && plan.tile <= 32768 && count_lds <= COUNT_LDS_LIMIT && (pow2_tile || plan.ntiles == 1)) {
         const int tile_shift = plan.ntiles == 1 ? 30 : __builtin_ctz((unsigned)plan.tile);
-        hipLaunchKernelGGL(k_sort_count, dim3((unsigned)plan.nseg), dim3(COUNT_THREADS), count_lds, s, buckets,
-                           counters, extra, L, n_buckets, tile_shift, plan.ntiles);
+        const long rows = (plan.nseg + NXCD - 1) / NXCD;
+        hipLaunchKernelGGL(k_sort_count, dim3((unsigned)(rows * NXCD * nsplit)), dim3(COUNT_THREADS), count_lds,
+                           s, buckets, counters, extra, plan.nseg, L, n_buckets, tile_shift, plan.ntiles, nsplit);
     } else {
         hipLaunchKernelGGL(k_sort_hist, dim3(blocks), dim3(SORT_THREADS), lds, s, buckets, counters, L,
                            n_buckets, plan.tile, plan.ntiles);
