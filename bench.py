@@ -367,6 +367,72 @@ def trace_summary(workload, stats_csv, bench_log, command, out_md, title="forwar
     print("\n".join(out))
 
 
+# Counters of the two --pmc passes that --counter-summary reads (each pass within
+# the per-pass limits of the SQ and GRBM blocks); MfmaUtil, VALUBusy, LdsUtil,
+# LDSBankConflict and OccupancyPercent are rocprofv3's derived metrics.
+COUNTER_PASSES = [
+    "MfmaUtil VALUBusy SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAVES",
+    "LdsUtil LDSBankConflict OccupancyPercent SQ_WAIT_INST_ANY SQ_WAVE_CYCLES",
+]
+
+
+def counter_summary(workload, dirs, out_md):
+    """Per-kernel means over every dispatch of rocprofv3 --pmc counter runs (one
+    folder per pass), as a short Markdown table."""
+    import csv
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if "lshk::" not in name:
+                    continue
+                name = name.replace("(anonymous namespace)::", "").replace("lshk::", "")
+                name = re.sub(r"\(.*", "", name).replace("void ", "").replace("attn::", "")
+                vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    cols = [("MfmaUtil", "MFMA busy %", 1), ("VALUBusy", "VALU busy %", 1), ("LdsUtil", "LDS busy %", 1),
+            ("LDSBankConflict", "LDS bank-conflict %", 1), ("OccupancyPercent", "occupancy %", 1),
+            ("SQ_WAIT_INST_ANY", "wait-any / wave-cycles %", None),
+            ("SQ_INSTS_VALU", "VALU instr per wave", "w"), ("SQ_INSTS_MFMA", "MFMA instr per wave", "w"),
+            ("SQ_INSTS_LDS", "LDS instr per wave", "w")]
+    from synthetic_inputs import WORKLOADS
+    w = WORKLOADS[workload]
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python bench.py --steps 2 "
+           "--warmup 1 --no-cpu-baseline --workload " + workload)
+    out = [f"# Hardware counters: forward pass, {workload} workload", "",
+           f"Workload {workload}: {w.description} (synthetic, seed {w.seed}).", "",
+           "Commands (repository root, MI355X), one counter pass each:", "",
+           "    cd /root/repo && export TMPDIR=/tmp"]
+    out += [f"    {cmd.format(c=c, d=d)}" for c, d in zip(COUNTER_PASSES, dirs)]
+    out += ["", "Means over every dispatch of each kernel (warm-up included).  MfmaUtil, VALUBusy, "
+                "LdsUtil, LDSBankConflict and OccupancyPercent are rocprofv3's derived metrics "
+                "(percent of the kernel's GPU-active cycles, per SIMD or CU); per-wave counts are the "
+                "instruction counters divided by SQ_WAVES; wait-any is SQ_WAIT_INST_ANY over "
+                "SQ_WAVE_CYCLES.", "",
+            "| kernel | " + " | ".join(c[1] for c in cols) + " |",
+            "|---|" + "---|" * len(cols)]
+    mean = lambda xs: sum(xs) / len(xs)
+    for name in sorted(vals, key=lambda n: -mean(vals[n].get("SQ_WAVE_CYCLES", [0]))):
+        v = vals[name]
+        cells = []
+        for key, _, kind in cols:
+            if key not in v:
+                cells.append("–")
+            elif kind == "w":
+                cells.append(f"{mean(v[key]) / max(1.0, mean(v.get('SQ_WAVES', [1]))):.0f}")
+            elif kind is None:
+                cyc = mean(v.get("SQ_WAVE_CYCLES", [0]))
+                cells.append(f"{100 * mean(v[key]) / cyc:.0f}" if cyc else "–")
+            else:
+                cells.append(f"{mean(v[key]):.1f}")
+        out.append(f"| `{name}` | " + " | ".join(cells) + " |")
+    out.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
 def copy_calibration():
     """A plain 1 GiB device-to-device copy: the reference for scaling the
     FETCH_SIZE / WRITE_SIZE counters, and the practical HBM copy bandwidth."""
@@ -414,6 +480,9 @@ def main():
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="write profiles/forward_<workload>_kernel_stats.md from a rocprofv3 "
                          "--kernel-trace --stats run of this benchmark (no GPU needed)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="write profiles/counters_<workload>.md from the two rocprofv3 --pmc passes "
+                         "of COUNTER_PASSES (no GPU needed)")
     ap.add_argument("--pmc-summary", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write profiles/pmc_traffic.json from rocprofv3 --pmc output folders")
@@ -435,6 +504,10 @@ def main():
                f"-o run -- python bench.py --no-cpu-baseline --workload {wl}{extra}")
         trace_summary(wl, stats, blog, cmd,
                       os.path.join(ROOT, "profiles", f"{mode}_{wl}{tag}_kernel_stats.md"), title)
+        return
+    if args.counter_summary:
+        counter_summary(args.workload, args.counter_summary,
+                        os.path.join(ROOT, "profiles", f"counters_{args.workload}.md"))
         return
     if args.pmc_summary:
         fd, wd, cfd, cwd = args.pmc_summary
@@ -643,6 +716,9 @@ def main():
         entry, ref_b, ref_m, Lp = base
         result["cpu_baseline"] = entry
         result["hash_check"] = hash_check(buckets.cpu().numpy(), ref_b, ref_m, Lp, L)
+    result["env"] = {"torch": torch.__version__, "hip": torch.version.hip,
+                     "device": torch.cuda.get_device_name(0),
+                     "host_cores": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
 
 
