@@ -278,6 +278,10 @@ SORT_SWEEP = [
     (4096, 128, 2, 64), (5000, 250, 5, 8), (2048, 2, 2, 64), (1344, 10, 3, 64),
     (8192, 1000, 8, 64), (4096, 1024, 2, 32), (12288, 2046, 2, 64), (6000, 4098, 3, 40),
     (32768, 16384, 2, 64),
+    # 32K positions and more: the counting kernel splits each segment's buckets
+    # over workgroups (4 ranges; 2 ranges with a ragged last tile; 4 ranges
+    # feeding the placement kernel for more than 1024 buckets)
+    (32768, 512, 2, 64), (36000, 36, 3, 40), (65536, 2048, 2, 64),
 ]
 
 
