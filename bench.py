@@ -376,7 +376,7 @@ COUNTER_PASSES = [
 ]
 
 
-def counter_summary(workload, dirs, out_md):
+def counter_summary(workload, dirs, out_md, title="forward pass", extra=""):
     """Per-kernel means over every dispatch of rocprofv3 --pmc counter runs (one
     folder per pass), as a short Markdown table."""
     import csv
@@ -399,8 +399,8 @@ def counter_summary(workload, dirs, out_md):
     from synthetic_inputs import WORKLOADS
     w = WORKLOADS[workload]
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python bench.py --steps 2 "
-           "--warmup 1 --no-cpu-baseline --workload " + workload)
-    out = [f"# Hardware counters: forward pass, {workload} workload", "",
+           "--warmup 1 --no-cpu-baseline --workload " + workload + extra)
+    out = [f"# Hardware counters: {title}, {workload} workload", "",
            f"Workload {workload}: {w.description} (synthetic, seed {w.seed}).", "",
            "Commands (repository root, MI355X), one counter pass each:", "",
            "    cd /root/repo && export TMPDIR=/tmp"]
@@ -506,8 +506,17 @@ def main():
                       os.path.join(ROOT, "profiles", f"{mode}_{wl}{tag}_kernel_stats.md"), title)
         return
     if args.counter_summary:
+        mode, extra, title, tag = "", "", "forward pass", ""
+        if args.backward:
+            mode, extra, title = "backward_", " --backward", "forward + backward (lsh_attn_backward)"
+        elif args.layer:
+            mode, extra, tag = "layer_", f" --layer {args.layer}", f"_d{args.layer}"
+            title = f"attention layer (projections around the four steps) at d_model {args.layer}"
+        elif args.block:
+            mode, extra, tag = "block_", f" --block {args.block}", f"_d{args.block}"
+            title = f"Reformer block forward and input recompute at d_model {args.block}"
         counter_summary(args.workload, args.counter_summary,
-                        os.path.join(ROOT, "profiles", f"counters_{args.workload}.md"))
+                        os.path.join(ROOT, "profiles", f"counters_{mode}{args.workload}{tag}.md"), title, extra)
         return
     if args.pmc_summary:
         fd, wd, cfd, cwd = args.pmc_summary
