@@ -285,6 +285,24 @@ const char* lsh_status_string(lsh_status status);
 /* Message describing the last non-OK status returned on the calling thread. */
 const char* lsh_last_error(void);
 
+/*
+ * Device-side bounds checks (debug build).  Not a step of the method.
+ * The kernels clamp or skip every index they take from caller data: positions
+ * read from perm (chunk attention and its backward), bucket ids (sort) and the
+ * sorted slots the sort computes from them.  So out-of-range values never
+ * reach memory outside the buffers; they only make the results meaningless.
+ * The debug library (liblsh_attention_debug.so, built with LSH_DEVICE_CHECKS)
+ * also counts every such value on the device.
+ *   count   host out: failed checks since the last reset, summed over the
+ *           library's kernels (one bad value may fail more than one check);
+ *           always 0 in the release library, which has no checks.
+ *   reset   nonzero: clear the counters after reading them.
+ * Reads the counters of the current device synchronously (hipMemcpyFromSymbol),
+ * so call it after the kernels of interest have finished.  Errors: count NULL
+ * (LSH_ERR_INVALID_ARG); a failed copy (LSH_ERR_HIP).
+ */
+lsh_status lsh_debug_check_failures(unsigned long long* count, int reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ liblsh_attention.so behind a C ABI (include/lsh_attention.h); this package is
 its Python binding.  Build the library with
 ``python -m lsh_attention_02_amd.build``.
 """
-from ._binding import (EXPORTED, LIB_PATH, LSH_BF16, LSH_ERR_HIP, LSH_ERR_INVALID_ARG,  # noqa: F401
+from ._binding import (DEBUG_LIB_PATH, EXPORTED, LIB_PATH, debug_check_failures, load_debug_library, LSH_BF16, LSH_ERR_HIP, LSH_ERR_INVALID_ARG,  # noqa: F401
                        LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_F32, LSH_FLAG_NO_DUP_CORRECTION,
                        LSH_FLAG_SAME_BUCKET, LSH_FLAG_WRAP_LOOKBACK, LSH_OK, CConfig,
                        LSHConfig, LSHError, backward_workspace, block_forward, block_inverse, forward,

@@ -20,6 +20,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblsh_attention.so")
+# the same library with the device-side bounds checks compiled in (build --debug)
+DEBUG_LIB_PATH = os.path.join(_PKG, "liblsh_attention_debug.so")
 
 LSH_OK, LSH_ERR_INVALID_ARG, LSH_ERR_UNSUPPORTED, LSH_ERR_WORKSPACE, LSH_ERR_HIP = range(5)
 LSH_F32, LSH_BF16 = 0, 1
@@ -29,7 +31,7 @@ LSH_FLAG_NO_DUP_CORRECTION, LSH_FLAG_WRAP_LOOKBACK, LSH_FLAG_SAME_BUCKET = 1, 2,
 EXPORTED = ("lsh_hash", "lsh_sort_workspace_bytes", "lsh_sort", "lsh_sort_noalloc", "lsh_chunk_attn",
             "lsh_combine_rounds", "lsh_backward_workspace_bytes", "lsh_attn_backward",
             "lsh_project_in", "lsh_project_out", "lsh_project_out_add", "lsh_ffn_workspace_bytes",
-            "lsh_ffn", "lsh_status_string", "lsh_last_error")
+            "lsh_ffn", "lsh_status_string", "lsh_last_error", "lsh_debug_check_failures")
 
 
 class LSHError(RuntimeError):
@@ -87,7 +89,32 @@ def load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m lsh_attention_02_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = _configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def load_debug_library() -> ctypes.CDLL:
+    """The debug build (device-side bounds checks counted, see
+    lsh_debug_check_failures), loaded beside the release one.  Assign it to
+    this module's ``_lib`` to route the wrappers through it."""
+    if not os.path.exists(DEBUG_LIB_PATH):
+        raise RuntimeError(f"{DEBUG_LIB_PATH} is missing: build it with "
+                           "`python -m lsh_attention_02_amd.build --debug` (hipcc, gfx950)")
+    return _configure(ctypes.CDLL(DEBUG_LIB_PATH))
+
+
+def debug_check_failures(lib: Optional[ctypes.CDLL] = None, reset: bool = False) -> int:
+    """Failed device-side bounds checks counted by `lib` (default: the loaded
+    library; always 0 for the release build) on the current device."""
+    lib = lib if lib is not None else load_library()
+    n = ctypes.c_ulonglong(0)
+    st = lib.lsh_debug_check_failures(ctypes.byref(n), int(reset))
+    if st != LSH_OK:
+        raise LSHError(st, "lsh_debug_check_failures", lib.lsh_last_error().decode())
+    return int(n.value)
+
+
+def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     P, CP, I32 = ctypes.c_void_p, ctypes.POINTER(CConfig), ctypes.c_int
     lib.lsh_hash.argtypes = [CP, P, P, P, P]
     lib.lsh_sort_workspace_bytes.argtypes = [CP]
@@ -113,7 +140,8 @@ def load_library() -> ctypes.CDLL:
     lib.lsh_status_string.restype = ctypes.c_char_p
     lib.lsh_last_error.argtypes = []
     lib.lsh_last_error.restype = ctypes.c_char_p
-    _lib = lib
+    lib.lsh_debug_check_failures.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), I32]
+    lib.lsh_debug_check_failures.restype = I32
     return lib
 
 

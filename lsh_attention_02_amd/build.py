@@ -1,6 +1,7 @@
 """Build the HIP library of the LSH-attention forward for gfx950 (MI355X).
 
-    python -m lsh_attention_02_amd.build        # or: from lsh_attention_02_amd.build import build
+    python -m lsh_attention_02_amd.build          # or: from lsh_attention_02_amd.build import build
+    python -m lsh_attention_02_amd.build --debug  # the same with device-side bounds checks
 
 Compiles every csrc/*.hip with hipcc (in parallel) and links
 lsh_attention_02_amd/liblsh_attention.so in-tree.  Always recompiles.
@@ -20,6 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "liblsh_attention.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+DEBUG_LIB_PATH = os.path.join(PKG, "liblsh_attention_debug.so")
+DEBUG_BUILD_DIR = os.path.join(PKG, "_build", "debug")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -51,14 +54,20 @@ def _run(cmd):
     return p.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link the library; returns its path.  Raises on failure."""
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile and link the library; returns its path.  Raises on failure.
+
+    debug: the same library with the device-side bounds checks compiled in
+    (LSH_DEVICE_CHECKS; lsh_debug_check_failures reads their counters), as
+    DEBUG_LIB_PATH.  The kernels are otherwise the same."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = DEBUG_BUILD_DIR if debug else BUILD_DIR
+    os.makedirs(bdir, exist_ok=True)
     sources = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD_DIR, s[:-4] + ".o") for s in sources]
-    jobs = [[cc, *CXXFLAGS, *([] if s in NO_VGPR_FORM else VGPR_FORM), "-c", os.path.join(CSRC, s),
-             "-o", o] for s, o in zip(sources, objs)]
+    objs = [os.path.join(bdir, s[:-4] + ".o") for s in sources]
+    extra = ["-DLSH_DEVICE_CHECKS"] if debug else []
+    jobs = [[cc, *CXXFLAGS, *extra, *([] if s in NO_VGPR_FORM else VGPR_FORM), "-c",
+             os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with cf.ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(_run, jobs))
@@ -67,14 +76,16 @@ def build(verbose: bool = False) -> str:
             print(f"[build] {src}\n{out}", file=sys.stderr)
         if rc:
             raise RuntimeError(f"hipcc failed on {src}")
-    tmp = LIB_PATH + ".tmp"
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    tmp = path + ".tmp"
     rc, out = _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     if rc:
         print(out, file=sys.stderr)
         raise RuntimeError("linking the LSH-attention library failed")
-    os.replace(tmp, LIB_PATH)
-    build_asan_check(objs, verbose)
-    return LIB_PATH
+    os.replace(tmp, path)
+    if not debug:
+        build_asan_check(objs, verbose)
+    return path
 
 
 ASAN_DIR = os.path.join(BUILD_DIR, "asan")
@@ -115,4 +126,4 @@ def build_asan_check(objs, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

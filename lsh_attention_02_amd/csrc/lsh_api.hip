@@ -163,6 +163,19 @@ const char* lsh_status_string(lsh_status s)
 
 const char* lsh_last_error(void) { return g_last_error.c_str(); }
 
+lsh_status lsh_debug_check_failures(unsigned long long* count, int reset)
+{
+    if (count == nullptr) return fail(LSH_ERR_INVALID_ARG, "count is null");
+    *count = 0;
+    const bool r = reset != 0;
+    LSH_TRY(hip_status(lshk::check_count_sort(count, r), "lsh_debug_check_failures"));
+    LSH_TRY(hip_status(lshk::check_count_attn_bwd(count, r), "lsh_debug_check_failures"));
+    LSH_TRY(hip_status(lshk::attn::check_count_bf16_d64(count, r), "lsh_debug_check_failures"));
+    LSH_TRY(hip_status(lshk::attn::check_count_bf16_d128(count, r), "lsh_debug_check_failures"));
+    LSH_TRY(hip_status(lshk::attn::check_count_f32_d64(count, r), "lsh_debug_check_failures"));
+    return hip_status(lshk::attn::check_count_f32_d128(count, r), "lsh_debug_check_failures");
+}
+
 lsh_status lsh_hash(const lsh_config* cfg, const void* qk, const void* R, int32_t* buckets,
                     hipStream_t stream)
 {

@@ -119,7 +119,10 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
 
     if (tid < 33) sm.neg_log2[tid] = (tid % 2 == 0 && tid / 2 < n_r) ? -__log2f((float)(n_r - tid / 2)) : 0.f;
 
-    auto clamp_pos = [&](int p) { return min(max(p, 0), L - 1); };
+    auto clamp_pos = [&](int p) {
+        LSH_CHECK((unsigned)p < (unsigned)L);
+        return min(max(p, 0), L - 1);
+    };
 
     // Gathers for the next chunk, kept raw in registers until stored (as in the
     // forward).  Job = 4 consecutive rows x one 16-byte piece of qk, v and d_o.
@@ -603,6 +606,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s)
 
 }  // namespace
 }  // namespace attn
+
+LSH_CHECK_ACCESSOR(check_count_attn_bwd)
 
 hipError_t launch_attn_backward(int d_head, const BwdArgs& a, hipStream_t stream)
 {

@@ -320,7 +320,10 @@ void k_chunk_attn(const T* __restrict__ qk, const T* __restrict__ v,
     // chunk and are never stored), so the compiler's wait counts are the same
     // in every iteration.
     // Positions come from the caller's perm: every gather stays inside the row.
-    auto clamp_pos = [&](int p) { return min(max(p, 0), L - 1); };
+    auto clamp_pos = [&](int p) {
+        LSH_CHECK((unsigned)p < (unsigned)L);
+        return min(max(p, 0), L - 1);
+    };
 
     // Per-row jobs: job m < C * NW loads word m % NW (rounds 2w and 2w+1) of
     // the packed chunk ids of row m / NW and, for m % NW == 0, the row's

@@ -4,6 +4,8 @@
 namespace lshk {
 namespace attn {
 
+LSH_CHECK_ACCESSOR(check_count_bf16_d128)
+
 hipError_t launch_bf16_d128(LSH_ATTN_LAUNCH_ARGS)
 {
     switch (chunk) {

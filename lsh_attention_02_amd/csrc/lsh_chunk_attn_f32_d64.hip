@@ -4,6 +4,8 @@
 namespace lshk {
 namespace attn {
 
+LSH_CHECK_ACCESSOR(check_count_f32_d64)
+
 hipError_t launch_f32_d64(LSH_ATTN_LAUNCH_ARGS)
 {
     switch (chunk) {

@@ -111,4 +111,35 @@ template <> __device__ __forceinline__ float from_f32<float>(float f) { return f
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Device-side bounds checks.  The kernels clamp or skip every index they take
+// from caller data (positions read from perm, bucket ids, sorted slots), so a
+// bad value never leaves a buffer.  A build with LSH_DEVICE_CHECKS defined also
+// counts each such value: LSH_CHECK(cond) adds one to this translation unit's
+// device counter when cond is false (a bad value may be counted by more than
+// one check), and LSH_CHECK_ACCESSOR(fn) defines the host function that adds
+// the counter to *acc and optionally clears it.  Without the macro both are
+// empty and the kernels are unchanged.
+#ifdef LSH_DEVICE_CHECKS
+static __device__ unsigned int g_check_failures;
+#define LSH_CHECK(cond)                                                                     \
+    do {                                                                                    \
+        if (!(cond)) atomicAdd(&::lshk::g_check_failures, 1u);                              \
+    } while (0)
+#define LSH_CHECK_ACCESSOR(fn)                                                              \
+    hipError_t fn(unsigned long long* acc, bool reset)                                      \
+    {                                                                                       \
+        unsigned int v = 0;                                                                 \
+        hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_failures), sizeof v);     \
+        if (e != hipSuccess) return e;                                                      \
+        *acc += v;                                                                          \
+        if (!reset) return hipSuccess;                                                      \
+        const unsigned int zero = 0;                                                        \
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_check_failures), &zero, sizeof zero);         \
+    }
+#else
+#define LSH_CHECK(cond) ((void)0)
+#define LSH_CHECK_ACCESSOR(fn)                                                              \
+    hipError_t fn(unsigned long long*, bool) { return hipSuccess; }
+#endif
+
 }  // namespace lshk

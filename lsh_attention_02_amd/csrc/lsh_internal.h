@@ -52,6 +52,18 @@ hipError_t launch_f32_d64(LSH_ATTN_LAUNCH_ARGS);
 hipError_t launch_f32_d128(LSH_ATTN_LAUNCH_ARGS);
 }  // namespace attn
 
+// Failed device-side bounds checks (LSH_CHECK) of each translation unit with
+// checks, added to *acc; reset clears them.  Builds without LSH_DEVICE_CHECKS
+// add nothing.
+hipError_t check_count_sort(unsigned long long* acc, bool reset);
+hipError_t check_count_attn_bwd(unsigned long long* acc, bool reset);
+namespace attn {
+hipError_t check_count_bf16_d64(unsigned long long* acc, bool reset);
+hipError_t check_count_bf16_d128(unsigned long long* acc, bool reset);
+hipError_t check_count_f32_d64(unsigned long long* acc, bool reset);
+hipError_t check_count_f32_d128(unsigned long long* acc, bool reset);
+}  // namespace attn
+
 hipError_t launch_combine(int dtype, int d_head, const void* o_rounds, const float* lse, void* o,
                           long bh, int L, int n_rounds, hipStream_t stream);
 

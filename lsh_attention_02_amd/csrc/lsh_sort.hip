@@ -68,8 +68,10 @@ void k_sort_hist(const int32_t* __restrict__ buckets, int32_t* __restrict__ coun
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = p + k * SORT_THREADS < p1 ? bk[min(p + k * SORT_THREADS, p1 - 1)] : -1;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+        for (int k = 0; k < 8; ++k) {
+            if (p + k * SORT_THREADS < p1) LSH_CHECK((unsigned)v[k] < (unsigned)nb);
             if ((unsigned)v[k] < (unsigned)nb) atomicAdd(&hist[v[k]], 1);
+        }
     }
     __syncthreads();
     int32_t* out = counters + (seg * ntiles + t) * (long)nb;
@@ -214,6 +216,7 @@ void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restri
         const int p = sub + threadIdx.x;
         const int b = p < p1 ? bk[p] : -1;
         const bool valid = (unsigned)b < (unsigned)nb;
+        if (p < p1) LSH_CHECK(valid);
         // peers = lanes of this wave holding the same bucket
         uint64_t peers = __ballot(valid);
         for (int bit = 0; bit < nbits; ++bit) {
@@ -235,6 +238,7 @@ void k_sort_scatter(const int32_t* __restrict__ buckets, const int32_t* __restri
         const int slot = base + rank;
         // slots stay in range unless the buckets or the workspace change under
         // the sort (e.g. two overlapping calls sharing one workspace)
+        if (valid) LSH_CHECK((unsigned)slot < (unsigned)L);
         if (valid && (unsigned)slot < (unsigned)L) {
             pm[slot] = p;
             // chunk id; with ranks, the window id chunk + 2 * rank(bucket)
@@ -306,6 +310,7 @@ void k_sort_count(const int32_t* __restrict__ buckets, int32_t* __restrict__ col
     __syncthreads();
     const int32_t* bk = buckets + seg * (long)L;
     auto add = [&](int p, int b) __attribute__((always_inline)) {
+        LSH_CHECK((unsigned)b < (unsigned)nb);
         const unsigned x = (unsigned)(b - b0);
         if (x < (unsigned)bsz)
             atomicAdd(&cnt2[(p >> tile_shift) * half + (x >> 1)], 1u << ((x & 1) << 4));
@@ -506,6 +511,7 @@ void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const bool ok = (unsigned)e[i] < (unsigned)nb;
+                        LSH_CHECK(ok);
                         const uint32_t u = ok ? (uint32_t)e[i] : 0xFFFFu;
                         if (i % 2 == 0) h[i / 2] = u; else h[i / 2] |= u << 16;
                         if (ok) atomicAdd(&cnt[e[i]], 1u);
@@ -523,6 +529,7 @@ void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict
             for (int k = 0; k < PLACE_LOADS; ++k) {
                 if (s + 64 * k < np) {
                     const bool ok = (unsigned)v[k] < (unsigned)nb;
+                    LSH_CHECK(ok);
                     bt[s + 64 * k] = ok ? (uint16_t)v[k] : (uint16_t)0xFFFF;
                     if (ok) atomicAdd(&cnt[v[k]], 1u);
                 }
@@ -663,6 +670,7 @@ void k_sort_place(const int32_t* __restrict__ buckets, const int32_t* __restrict
             id[k] = chunk_shift >= 0 ? slot >> chunk_shift : slot / (uint32_t)chunk;
             if constexpr (SAME) id[k] += rk[TAIL ? (b[k] < nb ? b[k] : 0) : b[k]];
             // in range unless the input changed under the sort
+            if (!TAIL || i0 + 64 * k < nvalid) LSH_CHECK(slot < (uint32_t)L);
             if ((!TAIL || i0 + 64 * k < nvalid) && slot < (uint32_t)L) pm[slot] = p0 + p[k];
         }
 #pragma unroll
@@ -766,6 +774,7 @@ void k_sort_place2(const int32_t* __restrict__ buckets, const int32_t* __restric
         const int p = 64 * k + lane;
         bv[k] = bk[min(p, np - 1)];
         if (p >= np) bv[k] = -1;
+        else LSH_CHECK((unsigned)bv[k] < (unsigned)nb);
     }
     for (int b = lane; b < nb; b += 64) tab[2 * b] = 0u;
 
@@ -900,6 +909,7 @@ void k_sort_place2(const int32_t* __restrict__ buckets, const int32_t* __restric
             const int i = i0 + 64 * k + lane;
             const uint32_t slot = (uint32_t)i + dl[k];
             // in range unless the input changed under the sort
+            if (i < nvalid) LSH_CHECK(slot < (uint32_t)L);
             if (i < nvalid && slot < (uint32_t)L) pm[slot] = p0 + (int)(e[k] & 0xFFFFu);
         }
     }
@@ -1012,6 +1022,8 @@ SortPlan sort_plan(long bh, int L, int n_rounds, int n_buckets, bool same_bucket
     p.extra = (size_t)p.nseg * n_buckets;
     return p;
 }
+
+LSH_CHECK_ACCESSOR(check_count_sort)
 
 hipError_t launch_sort(const int32_t* buckets, int32_t* perm, int16_t* cid, int32_t* counters,
                        int32_t* extra, bool same_bucket, const SortPlan& plan, long bh, int L,

@@ -349,3 +349,25 @@ def test_validation_under_host_asan():
                        text=True, env=env, timeout=120)
     assert p.returncode == 0, p.stdout[-4000:]
     assert "ok: 0 failure(s)" in p.stdout
+
+
+def test_debug_check_failures_release_build(lib):
+    """The release library has no device-side checks: the count is 0, read
+    without any HIP call; a null count is rejected."""
+    n = ctypes.c_ulonglong(7)
+    assert lib.lsh_debug_check_failures(ctypes.byref(n), 1) == B.LSH_OK
+    assert n.value == 0
+    assert lib.lsh_debug_check_failures(None, 0) == B.LSH_ERR_INVALID_ARG
+    assert b"count" in lib.lsh_last_error()
+
+
+def test_debug_library_exports(lib):
+    """The debug build (device-side bounds checks) exports the same C ABI."""
+    if not os.path.exists(B.DEBUG_LIB_PATH):
+        from lsh_attention_02_amd.build import build
+        build(debug=True)
+    dbg = ctypes.CDLL(B.DEBUG_LIB_PATH)
+    for name in B.EXPORTED:
+        assert hasattr(dbg, name), name
+    dbg.lsh_debug_check_failures.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert dbg.lsh_debug_check_failures(None, 0) == B.LSH_ERR_INVALID_ARG   # checked before any HIP call
