@@ -144,8 +144,8 @@ def bound_of(name, w):
 
 # Targets per call: at least this fraction of the MI355X peak, of the named
 # resource (chunk attention: bf16 MFMA; hash, sort and combine: HBM).
-NORTH_STAR_TARGET = {"lsh_chunk_attn": ("mfma", 0.5), "lsh_hash": ("hbm", 0.6),
-                     "lsh_sort": ("hbm", 0.6), "lsh_combine_rounds": ("hbm", 0.6)}
+TARGET_FRACTION = {"lsh_chunk_attn": ("mfma", 0.5), "lsh_hash": ("hbm", 0.6),
+                   "lsh_sort": ("hbm", 0.6), "lsh_combine_rounds": ("hbm", 0.6)}
 
 
 def both_fractions(name, w, ms, d_model=None, d_ff=None):
@@ -700,7 +700,7 @@ def main():
         e = roofline_entry(kind(n), w, per_call[n], dm, dff)
         e["ms"] = round(per_call[n], 4)
         e["mfma_frac"], e["hbm_frac"] = both_fractions(kind(n), w, per_call[n], dm, dff)
-        tgt = NORTH_STAR_TARGET.get(kind(n))
+        tgt = TARGET_FRACTION.get(kind(n))
         if tgt and not dm and not bwd and not blk:
             got = e[tgt[0] + "_frac"]
             e["target"] = {"of": tgt[0], "frac": tgt[1], "met": got >= tgt[1]}
