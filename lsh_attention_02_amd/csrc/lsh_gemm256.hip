@@ -10,7 +10,10 @@
 // 128 x 128 tiles (whose four 64 x 64 waves read 4 fragments for 4 MFMAs).  The
 // accumulators (256 per lane) live in the accumulation registers.  The MFMA
 // computes the transposed tile (w as the row operand), so each lane owns 4
-// consecutive output columns of a row: one 8-byte store each.
+// consecutive output columns of a row.  The output tile goes out through LDS
+// (below): stored straight from the accumulators, each store instruction would
+// write 16 bytes into each of 32 rows, and with one workgroup per CU nothing
+// hides those partial-line writes.
 //
 // K steps of 64: the operand tiles (2 x 32 KiB, swizzled as lin_swz) are double
 // buffered in LDS (128 KiB, one workgroup per CU) and copied straight from
@@ -170,23 +173,48 @@ void k_linear_big(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w0,
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the workgroup
 
-    // D element j of tile (a, b): column n = 32b + 8(j/4) + 4 kh + (j%4), row m = 32a + r32
+    // Epilogue through LDS, free now: 128 rows of the tile per pass as fp32
+    // (each of the four 32 KiB operand arrays holds 32 rows of 1 KiB, the
+    // 16-byte groups of a row XOR-swizzled by the row), written by the two
+    // waves of that half; then every thread stores 8 columns of a row, so each
+    // wave instruction writes whole rows instead of 16 bytes of 32 rows.
+    // D element j of tile (a, b): column n = 32b + 8(j/4) + 4 kh + (j%4), row m = 32a + r32.
+    __syncthreads();                                   // every wave past its operand reads
+    float* const st[4] = {reinterpret_cast<float*>(sa0), reinterpret_cast<float*>(sa1),
+                          reinterpret_cast<float*>(sw0), reinterpret_cast<float*>(sw1)};
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int r = 128 * wm + 32 * a + r32, m = m0 + r;
-        const RowPos p = row_pos(base, r, s.L);
+    for (int pass = 0; pass < 2; ++pass) {
+        if (wm == pass) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int jg = 0; jg < 4; ++jg) {
-                const int n = n0 + 128 * wn + 32 * b + 8 * jg + 4 * kh;
-                if (m < s.M && n < s.N) {
-                    const f32x16& c = acc[a][b];
-                    store4<OUT, D, EPI>(y, s, m, p, n, c[4 * jg], c[4 * jg + 1], c[4 * jg + 2],
-                                        c[4 * jg + 3], bias, resid, sign);
-                }
-            }
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int jg = 0; jg < 4; ++jg) {
+                        const int g = 32 * wn + 8 * b + 2 * jg + kh;      // 16-byte group of the row
+                        const f32x16& c = acc[a][b];
+                        *reinterpret_cast<f32x4*>(st[a] + r32 * 256 + 4 * (g ^ r32)) =
+                            f32x4{c[4 * jg], c[4 * jg + 1], c[4 * jg + 2], c[4 * jg + 3]};
+                    }
         }
+        __syncthreads();
+#pragma unroll
+        for (int arr = 0; arr < 4; ++arr)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                // 8 columns c8 of row r in column half hh: a wave covers 4 rows of one half
+                const int idx = it * BIG_THREADS + tid;
+                const int c8 = idx & 15, r = (idx >> 4) & 31, hh = idx >> 9;
+                const int g0 = 32 * hh + 2 * c8;
+                const float* row = st[arr] + r * 256;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(row + 4 * (g0 ^ r));
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 4 * ((g0 + 1) ^ r));
+                const int rt = 128 * pass + 32 * arr + r;
+                const int m = m0 + rt, n = n0 + 128 * hh + 8 * c8;
+                if (m < s.M && n < s.N)                    // N is a multiple of 64
+                    store8<OUT, D, EPI>(y, s, m, row_pos(base, rt, s.L), n, lo, hi, bias, resid, sign);
+            }
+        __syncthreads();                               // the arrays are rewritten by the next pass
     }
 }
 

@@ -97,6 +97,36 @@ __device__ __forceinline__ void store4(bf16_t* __restrict__ y, const LinShape& s
     *reinterpret_cast<u32x2*>(y + oi) = v;
 }
 
+// The same epilogue for 8 consecutive columns n .. n+7 of row m (n a multiple
+// of 8, so inside one head), element by element as store4, with one 16-byte
+// store.
+template <int OUT, int D, int EPI>
+__device__ __forceinline__ void store8(bf16_t* __restrict__ y, const LinShape& s, int m, RowPos p,
+                                       int n, f32x4 lo, f32x4 hi, const bf16_t* __restrict__ bias,
+                                       const bf16_t* __restrict__ resid, float sign)
+{
+    float e[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const long oi = out_index<OUT, D>(s, m, p, n);
+    if constexpr ((EPI & EPI_BIAS) != 0) {
+        const u32x4 bb = *reinterpret_cast<const u32x4*>(bias + n);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] += bf16_to_f32((uint16_t)(bb[i >> 1] >> (16 * (i & 1))));
+    }
+    if constexpr ((EPI & EPI_RELU) != 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = fmaxf(e[i], 0.f);
+    }
+    if constexpr ((EPI & EPI_RESID) != 0) {
+        const u32x4 rr = *reinterpret_cast<const u32x4*>(resid + oi);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            e[i] = fmaf(sign, e[i], bf16_to_f32((uint16_t)(rr[i >> 1] >> (16 * (i & 1)))));
+    }
+    const u32x4 v = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                     pack_bf16x2(e[6], e[7])};
+    *reinterpret_cast<u32x4*>(y + oi) = v;
+}
+
 // Tiles of a launch in (matrix, row tile, column tile) order; workgroups go to
 // the 8 XCDs round-robin by launch index and each XCD has its own L2, so each
 // XCD takes a contiguous run of tiles: the column tiles that share an input
