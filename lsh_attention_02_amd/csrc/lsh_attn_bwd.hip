@@ -252,14 +252,18 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
             const int krow = KSL * sw + 16 * kt + r16;
             const long pos = sm.pos[G][krow];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d0 = dt * 16 + 4 * g;
-                const u32x2 wk = {pack_bf16x2(acck[dt][kt][0] * scale, acck[dt][kt][1] * scale),
-                                  pack_bf16x2(acck[dt][kt][2] * scale, acck[dt][kt][3] * scale)};
-                const u32x2 wv = {pack_bf16x2(accv[dt][kt][0], accv[dt][kt][1]),
-                                  pack_bf16x2(accv[dt][kt][2], accv[dt][kt][3])};
-                *reinterpret_cast<u32x2*>(dk_r + rbase + pos * D + d0) = wk;
-                *reinterpret_cast<u32x2*>(dv_r + rbase + pos * D + d0) = wv;
+            for (int e = 0; e < DT / 2; ++e) {
+                const int a = 2 * e, b = 2 * e + 1;
+                store_tile_pair_bf16(dk_r + rbase + pos * D, g, a,
+                                     pack_bf16x2(acck[a][kt][0] * scale, acck[a][kt][1] * scale),
+                                     pack_bf16x2(acck[a][kt][2] * scale, acck[a][kt][3] * scale),
+                                     pack_bf16x2(acck[b][kt][0] * scale, acck[b][kt][1] * scale),
+                                     pack_bf16x2(acck[b][kt][2] * scale, acck[b][kt][3] * scale));
+                store_tile_pair_bf16(dv_r + rbase + pos * D, g, a,
+                                     pack_bf16x2(accv[a][kt][0], accv[a][kt][1]),
+                                     pack_bf16x2(accv[a][kt][2], accv[a][kt][3]),
+                                     pack_bf16x2(accv[b][kt][0], accv[b][kt][1]),
+                                     pack_bf16x2(accv[b][kt][2], accv[b][kt][3]));
             }
         }
     };
@@ -408,11 +412,13 @@ void k_attn_bwd(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v,
                 }
                 T* orow = dq_r + rbase + (long)qpos * D;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int d0 = dt * 16 + 4 * g;
-                    const u32x2 w = {pack_bf16x2(o[dt][0] * scale, o[dt][1] * scale),
-                                     pack_bf16x2(o[dt][2] * scale, o[dt][3] * scale)};
-                    *reinterpret_cast<u32x2*>(orow + d0) = w;
+                for (int e = 0; e < DT / 2; ++e) {
+                    const int a = 2 * e, b = 2 * e + 1;
+                    store_tile_pair_bf16(orow, g, a,
+                                         pack_bf16x2(o[a][0] * scale, o[a][1] * scale),
+                                         pack_bf16x2(o[a][2] * scale, o[a][3] * scale),
+                                         pack_bf16x2(o[b][0] * scale, o[b][1] * scale),
+                                         pack_bf16x2(o[b][2] * scale, o[b][3] * scale));
                 }
             }
         }
@@ -734,11 +740,13 @@ void k_bwd_q(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v, const 
             }
             T* orow = ob + (long)qpos * D;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d0 = dt * 16 + 4 * g;
-                const u32x2 w = {pack_bf16x2(o[dt][0] * scale, o[dt][1] * scale),
-                                 pack_bf16x2(o[dt][2] * scale, o[dt][3] * scale)};
-                *reinterpret_cast<u32x2*>(orow + d0) = w;
+            for (int e = 0; e < DT / 2; ++e) {
+                const int a = 2 * e, b = 2 * e + 1;
+                store_tile_pair_bf16(orow, g, a,
+                                     pack_bf16x2(o[a][0] * scale, o[a][1] * scale),
+                                     pack_bf16x2(o[a][2] * scale, o[a][3] * scale),
+                                     pack_bf16x2(o[b][0] * scale, o[b][1] * scale),
+                                     pack_bf16x2(o[b][2] * scale, o[b][3] * scale));
             }
         }
         __syncthreads();
@@ -976,13 +984,19 @@ void k_bwd_k(const bf16_t* __restrict__ qk, const bf16_t* __restrict__ v, const 
     auto write_keys = [&]() {
         // lane (r16, g): key 16 w + r16, d = 16 dt + 4 g + j
 #pragma unroll
+        for (int e = 0; e < DT / 2; ++e) {
+            const int a = 2 * e, b = 2 * e + 1;
+            store_tile_pair_bf16(dk_r + rbase + (long)kpos * D, g, a,
+                                 pack_bf16x2(acck[a][0] * scale, acck[a][1] * scale),
+                                 pack_bf16x2(acck[a][2] * scale, acck[a][3] * scale),
+                                 pack_bf16x2(acck[b][0] * scale, acck[b][1] * scale),
+                                 pack_bf16x2(acck[b][2] * scale, acck[b][3] * scale));
+            store_tile_pair_bf16(dv_r + rbase + (long)kpos * D, g, a,
+                                 pack_bf16x2(accv[a][0], accv[a][1]), pack_bf16x2(accv[a][2], accv[a][3]),
+                                 pack_bf16x2(accv[b][0], accv[b][1]), pack_bf16x2(accv[b][2], accv[b][3]));
+        }
+#pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const int d0 = dt * 16 + 4 * g;
-            const u32x2 wk = {pack_bf16x2(acck[dt][0] * scale, acck[dt][1] * scale),
-                              pack_bf16x2(acck[dt][2] * scale, acck[dt][3] * scale)};
-            const u32x2 wv = {pack_bf16x2(accv[dt][0], accv[dt][1]), pack_bf16x2(accv[dt][2], accv[dt][3])};
-            *reinterpret_cast<u32x2*>(dk_r + rbase + (long)kpos * D + d0) = wk;
-            *reinterpret_cast<u32x2*>(dv_r + rbase + (long)kpos * D + d0) = wv;
             acck[dt] = f32x4{};
             accv[dt] = f32x4{};
         }

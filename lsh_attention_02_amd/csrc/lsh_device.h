@@ -102,6 +102,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Rows held in the 16x16 MFMA output layout: lane (r16 = lane & 15, g = lane >> 4)
+// holds, for each 16-wide d tile dt, the 4 values d = 16 dt + 4 g .. + 3 of row
+// r16.  For a pair of tiles (dt0, dt0 + 1) given as packed bf16 words (a0, a1)
+// and (b0, b1), lanes g and g ^ 1 (lane ^ 16, the same row) trade one half, so
+// that each lane stores 16 contiguous bytes: the even lane d 16 dt0 + 4 g .. +7,
+// the odd lane d 16 (dt0 + 1) + 4 (g - 1) .. +7.  A store instruction then
+// writes 64 bytes of each of 16 rows instead of 32, and there are half as
+// many.  Every lane of the wave must call it (the trade reads lane ^ 16).
+__device__ __forceinline__ void store_tile_pair_bf16(bf16_t* row, int g, int dt0, uint32_t a0,
+                                                     uint32_t a1, uint32_t b0, uint32_t b1)
+{
+    const bool odd = (g & 1) != 0;
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16);
+    const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16);
+    const u32x4 w = odd ? u32x4{r0, r1, b0, b1} : u32x4{a0, a1, r0, r1};
+    const int d0 = odd ? 16 * (dt0 + 1) + 4 * (g - 1) : 16 * dt0 + 4 * g;
+    *reinterpret_cast<u32x4*>(row + d0) = w;
+}
+
 __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
