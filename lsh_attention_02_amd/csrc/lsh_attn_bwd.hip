@@ -1074,14 +1074,18 @@ void k_bwd_prep(const bf16_t* __restrict__ o, const bf16_t* __restrict__ d_o,
     }
 }
 
-// dqk = sum_r (dq_r + dk_r), dv = sum_r dv_r (fp32).  One thread per 8 elements.
+// dqk = sum_r (dq_r + dk_r), dv = sum_r dv_r (fp32).  One thread per 8 elements:
+// 4 in each half of the row (elements 4p .. 4p+3 and D/2 + 4p .. +3), so that
+// each load instruction reads, and each store instruction writes, contiguous
+// whole lines of a row (128 and 256 bytes at d 128) rather than 16 bytes at a
+// 32-byte stride.  The sums per element are the same.
 template <int D>
 __global__ __launch_bounds__(256)
 void k_bwd_reduce(const bf16_t* __restrict__ dq_r, const bf16_t* __restrict__ dk_r,
                   const bf16_t* __restrict__ dv_r, float* __restrict__ dqk, float* __restrict__ dv,
                   long rows, int L, int n_r)
 {
-    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    constexpr int TPR = D / 8, RPB = 256 / TPR, HALF = D / 2;
     const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
     const int part = threadIdx.x % TPR;
     if (row >= rows) return;
@@ -1091,24 +1095,27 @@ void k_bwd_reduce(const bf16_t* __restrict__ dq_r, const bf16_t* __restrict__ dk
 #pragma unroll
     for (int x = 0; x < 8; ++x) { aq[x] = 0.f; av[x] = 0.f; }
     for (int q = 0; q < n_r; ++q) {
-        const long off = ((bh * n_r + q) * (long)L + i) * D + part * 8;
-        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dq_r + off));
-        const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dk_r + off));
-        const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dv_r + off));
+        const long off = ((bh * n_r + q) * (long)L + i) * D + part * 4;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            aq[2 * x] += bf16_to_f32((uint16_t)(a[x] & 0xFFFFu)) + bf16_to_f32((uint16_t)(b[x] & 0xFFFFu));
-            aq[2 * x + 1] += bf16_to_f32((uint16_t)(a[x] >> 16)) + bf16_to_f32((uint16_t)(b[x] >> 16));
-            av[2 * x] += bf16_to_f32((uint16_t)(c[x] & 0xFFFFu));
-            av[2 * x + 1] += bf16_to_f32((uint16_t)(c[x] >> 16));
+        for (int h = 0; h < 2; ++h) {
+            const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(dq_r + off + h * HALF));
+            const u32x2 b = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(dk_r + off + h * HALF));
+            const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(dv_r + off + h * HALF));
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                aq[4 * h + 2 * x] += bf16_to_f32((uint16_t)(a[x] & 0xFFFFu)) + bf16_to_f32((uint16_t)(b[x] & 0xFFFFu));
+                aq[4 * h + 2 * x + 1] += bf16_to_f32((uint16_t)(a[x] >> 16)) + bf16_to_f32((uint16_t)(b[x] >> 16));
+                av[4 * h + 2 * x] += bf16_to_f32((uint16_t)(c[x] & 0xFFFFu));
+                av[4 * h + 2 * x + 1] += bf16_to_f32((uint16_t)(c[x] >> 16));
+            }
         }
     }
-    float* oq = dqk + row * D + part * 8;
-    float* ov = dv + row * D + part * 8;
+    float* oq = dqk + row * D + part * 4;
+    float* ov = dv + row * D + part * 4;
     __builtin_nontemporal_store(f32x4{aq[0], aq[1], aq[2], aq[3]}, reinterpret_cast<f32x4*>(oq));
-    __builtin_nontemporal_store(f32x4{aq[4], aq[5], aq[6], aq[7]}, reinterpret_cast<f32x4*>(oq + 4));
+    __builtin_nontemporal_store(f32x4{aq[4], aq[5], aq[6], aq[7]}, reinterpret_cast<f32x4*>(oq + HALF));
     __builtin_nontemporal_store(f32x4{av[0], av[1], av[2], av[3]}, reinterpret_cast<f32x4*>(ov));
-    __builtin_nontemporal_store(f32x4{av[4], av[5], av[6], av[7]}, reinterpret_cast<f32x4*>(ov + 4));
+    __builtin_nontemporal_store(f32x4{av[4], av[5], av[6], av[7]}, reinterpret_cast<f32x4*>(ov + HALF));
 }
 
 template <int D, int C, int NDW, bool WRAP, bool SAME>
